@@ -1,0 +1,282 @@
+/*
+ * lrm.h -- C ABI of the LRM-pruned MoE expert backward for one GPU's share of
+ * the experts (gfx950 / MI355X, HIP).
+ *
+ * The method (LRMoE, "load recalibration"): the forward stays complete; a
+ * controller fixes, per expert, how many token->expert pairs are kept in the
+ * backward for the whole layer call; when the gradient reaches the layer every
+ * pair is scored by the LRM metric, the squared Frobenius norm of its
+ * weight-gradient contribution, which factorises as
+ *     score = w^2 * |g|^2 * |x|^2
+ * (w routing weight, g incoming gradient at the projection output, x saved
+ * projection input); the top-quota pairs of each expert are kept, their rows
+ * are packed into dense per-expert blocks, the expert products run as
+ * variable-size grouped GEMMs without zero padding and the result is returned
+ * to the original layout.
+ *
+ * Sources: the page "LRMoE урезает обратный проход MoE и ускоряет обучение на
+ * 21–45%" (news.hamidun.com), section "Что делает LRMoE: полный прямой
+ * проход, обрезанный обратный", bullets "Квоты до вычислений" (quotas),
+ * "Отбор по метрике LRM" (scoring and selection) and "Физическое уплотнение"
+ * (compaction, grouped GEMM, return to layout), and the note after them on
+ * masking; its French twin "LRMoE élague la passe arrière des MoE ..." (same
+ * section); the German summary "LRMoE führt eine Nachkalibrierung der Last
+ * ... ein" (ai.mistergeeks.com), paragraph on the Lastnachkalibrierungs-
+ * Metrik.  Readings where the pages are silent:
+ *   - g is unscaled; the routing weight enters the contribution as w g x^T;
+ *   - ties in score are broken by lower pair index;
+ *   - a dropped pair contributes to neither dW nor dX;
+ *   - SwiGLU runs down -> gate/up; the gate/up candidates of an expert are the
+ *     pairs its down stage kept; each projection has its own score and quota.
+ *
+ * Conventions common to every call:
+ *   - Every pointer argument is caller-owned.  Pointers documented "device"
+ *     must be device memory of the current HIP device; "host" ones host memory.
+ *     The library never allocates or frees memory.
+ *   - Calls are asynchronous on the given stream (a hipStream_t passed as
+ *     void*, NULL = default stream) unless documented otherwise.  Host-side
+ *     argument validation happens before any launch: a call that returns an
+ *     error other than LRM_ERR_HIP has enqueued nothing and touched no memory.
+ *   - Pairs are indexed p = 0..N-1, token-major: token[] is non-decreasing.
+ *     N, T, E are pairs, tokens and experts resident on this GPU.
+ *   - Dense inputs are row-major with a leading dimension ld (elements) and
+ *     16-byte aligned rows; all dense inputs of one call share one dtype;
+ *     columns must be a multiple of 8 (bf16) or 4 (fp32).  Outputs are fp32.
+ *   - Outputs are overwritten, never accumulated.  Experts with nothing kept
+ *     get dW = 0; rows of dX that receive no kept pair are 0.
+ *   - Inputs must be finite; otherwise the results are undefined.
+ *   - Every call is deterministic: the same inputs give bit-identical outputs
+ *     (no floating-point atomics; all reductions in a fixed order).
+ *   - No exception crosses this interface.  Functions are re-entrant when
+ *     concurrent calls use distinct workspaces and outputs.
+ */
+#ifndef LRM_H_
+#define LRM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lrm_status {
+  LRM_OK = 0,
+  LRM_ERR_NULL = 1,        /* a required pointer is NULL */
+  LRM_ERR_SHAPE = 2,       /* sizes inconsistent or out of the supported range */
+  LRM_ERR_DTYPE = 3,       /* unknown dtype, or dense inputs of mixed dtype */
+  LRM_ERR_LAYOUT = 4,      /* unknown row layout, or a layout this call does not take */
+  LRM_ERR_ALIGN = 5,       /* a pointer or leading dimension breaks 16-byte row alignment */
+  LRM_ERR_QUOTA = 6,       /* a negative quota */
+  LRM_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than required */
+  LRM_ERR_INDEX = 8,       /* device-detected: expert or token index out of range / order */
+  LRM_ERR_HIP = 9,         /* a HIP runtime call or kernel launch failed */
+  LRM_ERR_UNSUPPORTED = 10 /* valid request outside what this library implements */
+} lrm_status;
+
+typedef enum lrm_dtype { LRM_F32 = 0, LRM_BF16 = 1 } lrm_dtype;
+
+/* Which row of a matrix a pair p reads: row token[p] (one row per token, shared
+ * by the token's pairs) or row p (one row per pair). */
+typedef enum lrm_rows { LRM_ROWS_TOKEN = 0, LRM_ROWS_PAIR = 1 } lrm_rows;
+
+typedef enum lrm_kind { LRM_LINEAR = 0, LRM_SWIGLU = 1 } lrm_kind;
+
+/* Flags of lrm_expert_backward. */
+#define LRM_KEEP_ALL 1u /* unpruned baseline: every pair kept, no score/select */
+
+/* The routed pairs of one layer call (the page's "pair": one token -> expert
+ * choice; page 1 introduction). */
+typedef struct lrm_pairs {
+  int32_t T;             /* tokens (rows of TOKEN-layout matrices), >= 0 */
+  int32_t N;             /* pairs resident on this GPU, >= 0 */
+  int32_t E;             /* experts resident on this GPU, 1..4096 */
+  int32_t _pad;
+  const int32_t* token;  /* device [N], non-decreasing, in [0, T) */
+  const int32_t* expert; /* device [N], in [0, E) */
+  const float* weight;   /* device [N], routing weight w_p */
+} lrm_pairs;
+
+/* A dense matrix whose rows are addressed through the pairs. */
+typedef struct lrm_mat {
+  const void* ptr; /* device, row-major */
+  int32_t dtype;   /* lrm_dtype */
+  int32_t rows;    /* lrm_rows: T rows (TOKEN) or N rows (PAIR) */
+  int32_t cols;
+  int32_t _pad;
+  int64_t ld;      /* elements between consecutive rows, >= cols */
+} lrm_mat;
+
+/* ------------------------------------------------------------------ steps */
+
+/* LRM score of every pair (page 1, bullet "Отбор по метрике LRM"):
+ *   score[p] = w_p^2 * |G row of p|^2 * |X row of p|^2
+ * Row sums of squares are accumulated in fp64 and the product is formed in
+ * fp64, then rounded to the nearest fp32 (scores are >= 0, so their fp32 bit
+ * patterns order like the values).  Each TOKEN-layout matrix is read once per
+ * token, each PAIR-layout matrix once per pair.
+ * score: device [N] fp32 output.  ws: device scratch of at least
+ * lrm_score_workspace_size(pairs) bytes (fp64 per-token norms). */
+lrm_status lrm_score(const lrm_pairs* pairs, const lrm_mat* X, const lrm_mat* G, float* score,
+                     void* ws, size_t ws_bytes, void* stream);
+size_t lrm_score_workspace_size(const lrm_pairs* pairs);
+
+/* LRM score of the down projection of a SwiGLU expert, whose saved input
+ * h_p = silu(a_p) * b_p is formed on the fly from the saved gate/up
+ * pre-activations A, B (PAIR layout, I columns) and whose incoming gradient is
+ * the G row of p (TOKEN or PAIR, H columns):
+ *   score[p] = w_p^2 * |g_p|^2 * |h_p|^2
+ * silu is evaluated in fp32 (expf), squares accumulated in fp64. */
+lrm_status lrm_score_glu(const lrm_pairs* pairs, const lrm_mat* A, const lrm_mat* B,
+                         const lrm_mat* G, float* score, void* ws, size_t ws_bytes, void* stream);
+
+/* Per-expert top-quota selection (page 1, bullets "Квоты до вычислений" and
+ * "Отбор по метрике LRM"): expert e keeps M_e = min(quota[e], n_e) of its n_e
+ * pairs, those with the largest score, ties broken by lower pair index.  The
+ * kept pairs are then given dense packed rows, expert blocks back to back
+ * with no padding and pairs ascending inside a block (bullet
+ * "Физическое уплотнение"):
+ *   offsets  device [E+1]: offsets[e] = M_0 + ... + M_{e-1}
+ *   kept     device [N]:   kept[offsets[e] + i] = i-th kept pair of e (only
+ *                          the first offsets[E] entries are written)
+ *   pos      device [N]:   packed row of p, or -1 if p is dropped
+ * quota: HOST [E] int32 (fixed by a controller for the call), copied
+ * stream-ordered into ws; negative quotas are rejected (LRM_ERR_QUOTA).
+ * flags: LRM_KEEP_ALL ignores score and quota and keeps every pair.
+ * ws: device scratch of lrm_select_workspace_size(pairs) bytes; its first word
+ * receives device-detected index errors (see lrm_check_device_errors). */
+lrm_status lrm_select(const lrm_pairs* pairs, const float* score, const int32_t* quota,
+                      uint32_t flags, int32_t* pos, int32_t* offsets, int32_t* kept, void* ws,
+                      size_t ws_bytes, void* stream);
+size_t lrm_select_workspace_size(const lrm_pairs* pairs);
+
+/* Physical compaction (page 1, bullet "Физическое уплотнение"): gathers the
+ * kept rows into dense per-expert blocks,
+ *   Xp[m] = w_p * (X row of p)   (rounded to X's dtype)
+ *   Gp[m] = G row of p
+ * for m < offsets[E], p = kept[m].  Either output may be NULL to skip it.
+ * Xp: device [max_rows][X.cols], Gp: device [max_rows][G.cols], both of the
+ * inputs' dtype and dense (ld = cols).  max_rows is the caller's capacity; it
+ * must be >= offsets[E] (guaranteed by max_rows >= min(N, sum of quotas)). */
+lrm_status lrm_compact(const lrm_pairs* pairs, const int32_t* kept, const int32_t* offsets,
+                       int32_t max_rows, const lrm_mat* X, const lrm_mat* G, void* Xp, void* Gp,
+                       void* stream);
+
+/* Variable-size grouped GEMMs on the packed blocks, no zero padding (page 1,
+ * bullet "Физическое уплотнение"): for every expert e with packed rows
+ * [offsets[e], offsets[e+1]) of Gp [rows][d_out] and Xp [rows][d_in]:
+ *   dW[e]  = Gp_e^T Xp_e        fp32 [d_out][d_in]   (0 when M_e = 0)
+ *   dXp_e  = Gp_e W_e           fp32 [M_e][d_in]     (row m of dXp)
+ * W: device, expert e at W + e*w_stride elements, [d_out][d_in] row-major.
+ * dtype applies to Gp, Xp, W; bf16 runs on MFMA with fp32 accumulation, fp32
+ * with fp32 FMA.  dW or dXp may be NULL to skip that product (W may then be
+ * NULL).  Rows of dXp at or beyond offsets[E] are not written.
+ * ws: device scratch of lrm_grouped_bwd_workspace_size(E) bytes. */
+lrm_status lrm_grouped_bwd(int32_t E, const int32_t* offsets, int32_t max_rows, int32_t dtype,
+                           const void* Gp, const void* Xp, const void* W, int64_t w_stride,
+                           int32_t d_in, int32_t d_out, float* dW, float* dXp, void* ws,
+                           size_t ws_bytes, void* stream);
+size_t lrm_grouped_bwd_workspace_size(int32_t E);
+
+/* Return to the original layout (page 1, bullet "Физическое уплотнение"):
+ *   TOKEN: dX[t] = sum over the pairs p of t with pos[p] >= 0, in pair order,
+ *          of w_p * dXp[pos[p]]; 0 for tokens with no kept pair
+ *   PAIR:  dX[p] = w_p * dXp[pos[p]], or 0 if pos[p] < 0
+ * dXp: device fp32 [*][d_in] dense; dX: device fp32 [T or N][d_in] dense.
+ * ws: device scratch of lrm_unpermute_workspace_size(pairs) bytes. */
+lrm_status lrm_unpermute(const lrm_pairs* pairs, const int32_t* pos, const float* dXp,
+                         int32_t d_in, int32_t out_rows, float* dX, void* ws, size_t ws_bytes,
+                         void* stream);
+size_t lrm_unpermute_workspace_size(const lrm_pairs* pairs);
+
+/* ------------------------------------------------------- the fused call */
+
+typedef struct lrm_problem {
+  int32_t kind;    /* lrm_kind */
+  uint32_t flags;  /* LRM_KEEP_ALL or 0 */
+  int32_t dtype;   /* lrm_dtype of every dense input */
+  int32_t _pad;
+  lrm_pairs pairs;
+  /* LINEAR: one projection y = W_e x per pair.  X: saved input (d_in cols,
+   * TOKEN or PAIR), G: incoming gradient at the output (d_out cols, TOKEN or
+   * PAIR), W: device [E][d_out][d_in] at stride w_stride, quota: HOST [E]. */
+  lrm_mat X;
+  lrm_mat G;
+  const void* W;
+  int64_t w_stride;
+  int32_t d_in, d_out;
+  const int32_t* quota;
+  /* SWIGLU: expert MLP W_down (silu(W_gate x) * (W_up x)).  X: saved input
+   * (H cols, TOKEN), G: incoming gradient at the layer output (H cols, TOKEN
+   * or PAIR), A, B: saved gate/up pre-activations (I cols, PAIR), weights
+   * W_gate, W_up device [E][I][H], W_down device [E][H][I] (dense, stride
+   * I*H), quotas HOST [E] per projection. */
+  lrm_mat A;
+  lrm_mat B;
+  const void* W_gate;
+  const void* W_up;
+  const void* W_down;
+  int32_t H, I;
+  const int32_t* quota_down;
+  const int32_t* quota_gate;
+  const int32_t* quota_up;
+} lrm_problem;
+
+typedef struct lrm_outputs {
+  float* dW;      /* LINEAR: device [E][d_out][d_in] */
+  float* dW_gate; /* SWIGLU: device [E][I][H] */
+  float* dW_up;   /* SWIGLU: device [E][I][H] */
+  float* dW_down; /* SWIGLU: device [E][H][I] */
+  float* dX;      /* device fp32, rows of X's layout (T or N) x d_in (or H) */
+  /* Optional (NULL = not returned).  LINEAR / SwiGLU down stage: */
+  float* score;     /* device [N] */
+  int32_t* pos;     /* device [N] */
+  int32_t* offsets; /* device [E+1] */
+  /* SwiGLU gate/up stages, indexed by the down stage's packed row m: */
+  float* score_gate;       /* device [max down rows] */
+  float* score_up;         /* device [max down rows] */
+  int32_t* pos_gate;       /* device [max down rows]: gate packed row or -1 */
+  int32_t* pos_up;         /* device [max down rows] */
+  int32_t* offsets_gate;   /* device [E+1] */
+  int32_t* offsets_up;     /* device [E+1] */
+} lrm_outputs;
+
+/* The whole pruned expert backward of one layer call, all steps enqueued on
+ * one stream with no device->host synchronisation:
+ *   LINEAR: score -> select -> compact -> grouped GEMM (dW, dXp) -> unpermute.
+ *   SWIGLU: down score -> select -> compact (g, w*h) -> grouped GEMM
+ *           (dW_down, u = W_down^T g) -> SwiGLU backward ga = u*b*silu'(a),
+ *           gb = u*silu(a) with gate/up scores -> gate and up select among
+ *           the down-kept pairs -> compact -> grouped GEMMs (dW_gate, dW_up,
+ *           dX rows) -> unpermute.
+ * With LRM_KEEP_ALL every pair is kept and no score or select runs (the
+ * unpruned baseline on the same kernels).
+ * ws: device scratch of lrm_workspace_size(prob) bytes, 256-byte aligned. */
+lrm_status lrm_expert_backward(const lrm_problem* prob, const lrm_outputs* out, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* Workspace bytes lrm_expert_backward needs for prob (0 if prob is invalid).
+ * Packed buffers are sized from the host quotas: min(N, sum of quotas) rows. */
+size_t lrm_workspace_size(const lrm_problem* prob);
+
+/* Upper bound on the kept rows of a selection with these host quotas:
+ * min(N, sum of quota[e]); -1 if a quota is negative or an argument is NULL. */
+int64_t lrm_max_kept(int32_t N, int32_t E, const int32_t* quota);
+
+/* Synchronises the stream, then reads the device error word at the start of
+ * a workspace used by lrm_select or lrm_expert_backward: LRM_OK, or
+ * LRM_ERR_INDEX if an expert index was out of range or token[] was out of
+ * range or decreasing (such pairs are treated as absent), and clears it. */
+lrm_status lrm_check_device_errors(void* ws, void* stream);
+
+/* Static description of a status code. */
+const char* lrm_status_string(lrm_status s);
+
+/* Library version (major*10000 + minor*100 + patch). */
+int32_t lrm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LRM_H_ */

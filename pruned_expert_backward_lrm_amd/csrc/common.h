@@ -1,0 +1,77 @@
+// Device-side helpers shared by the LRM kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <stdint.h>
+
+#include "platform.h"
+
+namespace lrm {
+
+constexpr int kWave = 64;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------- bf16 bits
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// fp32 -> bf16, round to nearest even (inputs are finite by precondition)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ------------------------------------------------------- wave reductions
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Inclusive scan across a wave (Hillis-Steele over 64 lanes).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int t = __shfl_up(v, o, kWave);
+    if (l >= o) v += t;
+  }
+  return v;
+}
+
+// Row addressing of a pair: the row a matrix holds for pair p.
+__device__ __forceinline__ int64_t pair_row(int rows_is_pair, const int32_t* token, int64_t p) {
+  return rows_is_pair ? p : (int64_t)token[p];
+}
+
+// SiLU pieces in fp32 (accurate expf).
+__device__ __forceinline__ float sigmoidf_acc(float a) { return 1.0f / (1.0f + expf(-a)); }
+
+// Device error bits (written into the first word of a workspace).
+enum : uint32_t {
+  kErrExpertRange = 1u,
+  kErrTokenRange = 2u,
+  kErrTokenOrder = 4u,
+};
+
+}  // namespace lrm

@@ -1,0 +1,98 @@
+// Physical compaction: kept gradient and activation rows are gathered into
+// dense per-expert blocks, expert after expert, with no padding (LRMoE page 1,
+// section on what LRMoE does, bullet "Физическое уплотнение").  The routing
+// weight is folded into the activation side here (Xp = w x), so the grouped
+// GEMM computes dW_e = Gp_e^T Xp_e directly.
+//
+// HBM-bound row copy: one wave per packed row, 16-byte loads and stores.
+#include "common.h"
+#include "launch.h"
+
+namespace lrm {
+
+__device__ __forceinline__ u32x4 scale_chunk_bf16(u32x4 v, float w) {
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(bf16_lo(v[i]) * w, bf16_hi(v[i]) * w);
+  return o;
+}
+__device__ __forceinline__ u32x4 scale_chunk_f32(u32x4 v, float w) {
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(__uint_as_float(v[i]) * w);
+  return o;
+}
+
+// w * silu(a) * b for one 16-byte chunk of a and b
+__device__ __forceinline__ u32x4 glu_chunk_bf16(u32x4 va, u32x4 vb, float w) {
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a0 = bf16_lo(va[i]), a1 = bf16_hi(va[i]);
+    const float h0 = a0 / (1.0f + expf(-a0)) * bf16_lo(vb[i]);
+    const float h1 = a1 / (1.0f + expf(-a1)) * bf16_hi(vb[i]);
+    o[i] = pack_bf16x2(w * h0, w * h1);
+  }
+  return o;
+}
+__device__ __forceinline__ u32x4 glu_chunk_f32(u32x4 va, u32x4 vb, float w) {
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float av = __uint_as_float(va[i]);
+    const float h = av / (1.0f + expf(-av)) * __uint_as_float(vb[i]);
+    o[i] = __float_as_uint(w * h);
+  }
+  return o;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
+  constexpr int kEsz = BF16 ? 2 : 4;
+  constexpr int kEpc = 16 / kEsz;
+  const int M = min(a.offsets[a.E], a.max_rows);
+  const int nw = gridDim.x * 4;
+  for (int j = blockIdx.x * 4 + (threadIdx.x >> 6); j < M; j += nw) {
+    const int id = a.kept[j];
+    const int p = a.pairmap ? a.pairmap[id] : id;
+    const int t = a.token[p];
+    if (a.Xp) {
+      const float w = a.weight[p];
+      const int64_t xr = (a.x_pair || a.glu) ? (int64_t)p : (int64_t)t;
+      const u32x4* src = reinterpret_cast<const u32x4*>((const char*)a.X + xr * a.ldx * kEsz);
+      u32x4* dst = reinterpret_cast<u32x4*>((char*)a.Xp + (int64_t)j * a.xcols * kEsz);
+      if (a.glu) {
+        const u32x4* src2 =
+            reinterpret_cast<const u32x4*>((const char*)a.X2 + xr * a.ldx2 * kEsz);
+        for (int c = lane_id(); c < a.xcols / kEpc; c += kWave)
+          dst[c] = BF16 ? glu_chunk_bf16(src[c], src2[c], w) : glu_chunk_f32(src[c], src2[c], w);
+      } else {
+        for (int c = lane_id(); c < a.xcols / kEpc; c += kWave) {
+          const u32x4 v = src[c];
+          dst[c] = BF16 ? scale_chunk_bf16(v, w) : scale_chunk_f32(v, w);
+        }
+      }
+    }
+    if (a.Gp) {
+      const int64_t gr = a.g_by_id ? (int64_t)id : (a.g_pair ? (int64_t)p : (int64_t)t);
+      const u32x4* src = reinterpret_cast<const u32x4*>((const char*)a.G + gr * a.ldg * kEsz);
+      u32x4* dst = reinterpret_cast<u32x4*>((char*)a.Gp + (int64_t)j * a.gcols * kEsz);
+      for (int c = lane_id(); c < a.gcols / kEpc; c += kWave) dst[c] = src[c];
+    }
+  }
+}
+
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
+  if (a.max_rows <= 0 || (!a.Xp && !a.Gp)) return hipSuccess;
+  if (!a.offsets || !a.kept || !a.token || !a.weight) return hipErrorInvalidValue;
+  if ((a.Xp && !a.X) || (a.Gp && !a.G) || (a.glu && !a.X2)) return hipErrorInvalidValue;
+  const int64_t want = ((int64_t)a.max_rows + 3) / 4;
+  const int blocks = (int)(want < (1 << 16) ? want : (1 << 16));
+  if (a.bf16)
+    LRM_LAUNCH(blocks, 256, 0, s, k_compact<true>)(a);
+  else
+    LRM_LAUNCH(blocks, 256, 0, s, k_compact<false>)(a);
+  return hipGetLastError();
+}
+
+}  // namespace lrm

@@ -1,0 +1,365 @@
+// Per-expert top-quota selection and packed-row assignment.
+//
+// A controller fixes one quota per expert for the layer call; when the
+// gradient arrives, each expert keeps its highest-scoring pairs within the
+// quota (LRMoE page 1, bullets "Квоты до вычислений" and "Отбор по метрике
+// LRM").  Kept rows are then packed expert by expert with no padding (bullet
+// "Физическое уплотнение").  Ties in score go to the lower pair index.
+//
+// Steps (all deterministic, no floating-point atomics, no host sync):
+//   1. bucket_count   per-chunk expert histograms (validates indices)
+//   2. bucket_scan    candidate offsets per expert and kept offsets
+//                     M_e = min(q_e, n_e), both exclusive prefix sums
+//   3. bucket_scatter stable counting-sort scatter of pair ids (ascending
+//                     inside an expert) and their fp32 score bits
+//   4. select         one workgroup per expert: 4-pass 8-bit radix search for
+//                     the M_e-th largest key, then a block prefix scan in
+//                     candidate order that keeps keys above the threshold and
+//                     the first (lowest-index) ties, and writes packed rows.
+// Scores are >= 0, so their fp32 bit patterns order like the values.
+#include "common.h"
+#include "launch.h"
+
+namespace lrm {
+
+constexpr int kSelThreads = 1024;
+
+__device__ __forceinline__ bool pair_valid(int64_t p, int T, int E, const int32_t* token,
+                                           const int32_t* expert) {
+  const int e = expert[p];
+  const int t = token[p];
+  return e >= 0 && e < E && t >= 0 && t < T;
+}
+
+// Exclusive scan of one int per thread over an NT-thread block.  lds must hold
+// NT/64 + 1 ints.  Returns the exclusive prefix; *total gets the block sum.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* lds, int* total) {
+  constexpr int NW = NT / kWave;
+  const int incl = wave_incl_scan(v);
+  const int w = threadIdx.x >> 6, l = lane_id();
+  if (l == kWave - 1) lds[w] = incl;
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    const int t = (l < NW) ? lds[l] : 0;
+    const int ti = wave_incl_scan(t);
+    if (l < NW) lds[l] = ti - t;
+    if (l == NW - 1) lds[NW] = ti;
+  }
+  __syncthreads();
+  const int res = lds[w] + incl - v;
+  *total = lds[NW];
+  __syncthreads();
+  return res;
+}
+
+// Exclusive scan of n values (n <= 4 * NT) given by get(i) into out[0..n],
+// out[n] = total.  Values are handled in contiguous runs of 4 per thread.
+template <int NT, typename F>
+__device__ void block_scan_array(int n, F get, int32_t* out, int* lds) {
+  const int per = 4;
+  const int i0 = threadIdx.x * per;
+  int v[per];
+  int local = 0;
+#pragma unroll
+  for (int j = 0; j < per; ++j) {
+    v[j] = (i0 + j < n) ? get(i0 + j) : 0;
+    local += v[j];
+  }
+  int total;
+  int run = block_excl_scan<NT>(local, lds, &total);
+#pragma unroll
+  for (int j = 0; j < per; ++j) {
+    if (i0 + j < n) out[i0 + j] = run;
+    run += v[j];
+  }
+  if (threadIdx.x == 0) out[n] = total;
+}
+
+__global__ __launch_bounds__(256) void k_bucket_count(int N, int T, int E, int chunk,
+                                                      const int32_t* __restrict__ token,
+                                                      const int32_t* __restrict__ expert,
+                                                      int32_t* __restrict__ blkcnt,
+                                                      uint32_t* __restrict__ err) {
+  LRM_DYN_SHARED(int, hist);
+  for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+  __syncthreads();
+  const int64_t p0 = (int64_t)blockIdx.x * chunk;
+  const int64_t p1 = min<int64_t>(p0 + chunk, N);
+  uint32_t bad = 0;
+  for (int64_t p = p0 + threadIdx.x; p < p1; p += 256) {
+    const int e = expert[p];
+    const int t = token[p];
+    if (e < 0 || e >= E) bad |= kErrExpertRange;
+    if (t < 0 || t >= T) bad |= kErrTokenRange;
+    if (p > 0 && token[p - 1] > t) bad |= kErrTokenOrder;
+    if (e >= 0 && e < E && t >= 0 && t < T) atomicAdd(&hist[e], 1);
+  }
+  if (bad) atomicOr(err, bad);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) blkcnt[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
+// blkcnt[b][e] -> exclusive within-expert offset of block b; cand_off = prefix
+// of the per-expert counts; offsets = prefix of M_e = min(quota_e, n_e)
+// (quota == nullptr: keep all).
+__global__ __launch_bounds__(kSelThreads) void k_bucket_scan(int nblk, int E,
+                                                             int32_t* __restrict__ blkcnt,
+                                                             const int32_t* __restrict__ quota,
+                                                             int32_t* __restrict__ cand_off,
+                                                             int32_t* __restrict__ offsets) {
+  LRM_DYN_SHARED(int, counts);  // [E]
+  __shared__ int lds[kSelThreads / kWave + 1];
+  for (int e = threadIdx.x; e < E; e += kSelThreads) {
+    int run = 0;
+    for (int b = 0; b < nblk; ++b) {
+      const int v = blkcnt[(int64_t)b * E + e];
+      blkcnt[(int64_t)b * E + e] = run;
+      run += v;
+    }
+    counts[e] = run;
+  }
+  __syncthreads();
+  block_scan_array<kSelThreads>(E, [&](int e) { return counts[e]; }, cand_off, lds);
+  block_scan_array<kSelThreads>(
+      E,
+      [&](int e) {
+        const int n = counts[e];
+        return quota ? min(max(quota[e], 0), n) : n;
+      },
+      offsets, lds);
+}
+
+// Stage-two offsets: candidates of e are cand_off[e]..cand_off[e+1].
+__global__ __launch_bounds__(kSelThreads) void k_kept_offsets(int E,
+                                                              const int32_t* __restrict__ cand_off,
+                                                              const int32_t* __restrict__ quota,
+                                                              int32_t* __restrict__ offsets) {
+  __shared__ int lds[kSelThreads / kWave + 1];
+  block_scan_array<kSelThreads>(
+      E,
+      [&](int e) {
+        const int n = cand_off[e + 1] - cand_off[e];
+        return quota ? min(max(quota[e], 0), n) : n;
+      },
+      offsets, lds);
+}
+
+// One wave per chunk; stable scatter in pair order.  Lanes with the same
+// expert are matched with ballots over the expert-id bits.
+__global__ __launch_bounds__(64) void k_bucket_scatter(int N, int T, int E, int chunk,
+                                                       const int32_t* __restrict__ token,
+                                                       const int32_t* __restrict__ expert,
+                                                       const int32_t* __restrict__ blkcnt,
+                                                       const int32_t* __restrict__ cand_off,
+                                                       const float* __restrict__ score,
+                                                       int32_t* __restrict__ cand,
+                                                       uint32_t* __restrict__ keys,
+                                                       int32_t* __restrict__ pos, int keep_all) {
+  LRM_DYN_SHARED(int, run);  // [E]
+  const int l = lane_id();
+  for (int e = l; e < E; e += kWave) run[e] = cand_off[e] + blkcnt[(int64_t)blockIdx.x * E + e];
+  __syncthreads();
+  const int nbits = (E > 1) ? 32 - __clz(E - 1) : 0;
+  const int64_t p0 = (int64_t)blockIdx.x * chunk;
+  const int64_t p1 = min<int64_t>(p0 + chunk, N);
+  const uint64_t lt_mask = (l == 0) ? 0ull : (~0ull >> (64 - l));
+  for (int64_t base = p0; base < p1; base += kWave) {
+    const int64_t p = base + l;
+    const bool in = p < p1;
+    const bool valid = in && pair_valid(p, T, E, token, expert);
+    const int e = valid ? expert[p] : 0;
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bb = __ballot(bit);
+      m &= bit ? bb : ~bb;
+    }
+    const int rank = __popcll(m & lt_mask);
+    const int dst = valid ? run[e] + rank : 0;
+    // every lane has read its expert's running offset before the group
+    // leader advances it (lockstep within the wave)
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      cand[dst] = (int32_t)p;
+      if (keys) keys[dst] = __float_as_uint(score[p]);
+      if (keep_all) pos[p] = dst;
+      if (rank == 0) run[e] += __popcll(m);
+    } else if (in) {
+      pos[p] = -1;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// One workgroup per expert.  keys[c] and ids cand[c] (or c itself when cand is
+// null) for candidates c in [cand_off[e], cand_off[e+1]), ascending id.
+__global__ __launch_bounds__(kSelThreads) void k_select(const int32_t* __restrict__ cand_off,
+                                                        const int32_t* __restrict__ offsets,
+                                                        const uint32_t* __restrict__ keys,
+                                                        const int32_t* __restrict__ cand,
+                                                        int32_t* __restrict__ pos,
+                                                        int32_t* __restrict__ kept) {
+  const int e = blockIdx.x;
+  const int c0 = cand_off[e];
+  const int n = cand_off[e + 1] - c0;
+  const int o = offsets[e];
+  const int m = offsets[e + 1] - o;
+  const int tid = threadIdx.x;
+  __shared__ int hist[256];
+  __shared__ int lds[kSelThreads / kWave + 1];
+  __shared__ uint32_t sh_prefix;
+  __shared__ int sh_rank;
+  auto id_of = [&](int c) -> int { return cand ? cand[c] : c; };
+
+  if (m >= n) {
+    for (int i = tid; i < n; i += kSelThreads) {
+      const int id = id_of(c0 + i);
+      kept[o + i] = id;
+      pos[id] = o + i;
+    }
+    return;
+  }
+  if (m <= 0) {
+    for (int i = tid; i < n; i += kSelThreads) pos[id_of(c0 + i)] = -1;
+    return;
+  }
+  // radix search for the m-th largest key (rank r counted from the top)
+  uint32_t prefix = 0, pmask = 0;
+  int r = m;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += kSelThreads) {
+      const uint32_t k = keys[c0 + i];
+      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      // lane l owns bins 255-4l .. 252-4l (descending)
+      int c[4];
+      int local = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = hist[255 - 4 * tid - j];
+        local += c[j];
+      }
+      int before = wave_incl_scan(local) - local;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (before < r && before + c[j] >= r) {
+          sh_prefix = prefix | ((uint32_t)(255 - 4 * tid - j) << shift);
+          sh_rank = r - before;
+        }
+        before += c[j];
+      }
+    }
+    __syncthreads();
+    prefix = sh_prefix;
+    r = sh_rank;
+    pmask |= 0xffu << shift;
+    __syncthreads();
+  }
+  // keep keys above the threshold, and the first r keys equal to it
+  const uint32_t K = prefix;
+  int eq_carry = 0, keep_carry = 0;
+  for (int base = 0; base < n; base += kSelThreads) {
+    const int i = base + tid;
+    const bool valid = i < n;
+    const uint32_t k = valid ? keys[c0 + i] : 0u;
+    const int eq = (valid && k == K) ? 1 : 0;
+    const int gt = (valid && k > K) ? 1 : 0;
+    int tot;
+    const int eq_before = block_excl_scan<kSelThreads>(eq, lds, &tot) + eq_carry;
+    eq_carry += tot;
+    const int keep = (gt || (eq && eq_before < r)) ? 1 : 0;
+    const int kp_before = block_excl_scan<kSelThreads>(keep, lds, &tot) + keep_carry;
+    keep_carry += tot;
+    if (valid) {
+      const int id = id_of(c0 + i);
+      if (keep) {
+        kept[o + kp_before] = id;
+        pos[id] = o + kp_before;
+      } else {
+        pos[id] = -1;
+      }
+    }
+  }
+}
+
+// tok_off[t] = first pair index whose token is >= t, for t in [0, T].
+__global__ __launch_bounds__(256) void k_token_offsets(int N, int T,
+                                                       const int32_t* __restrict__ token,
+                                                       int32_t* __restrict__ tok_off) {
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (p > N) return;
+  const int lo = (p == 0) ? 0 : min(max(token[p - 1], -1), T - 1) + 1;
+  const int hi = (p == N) ? T : min(max(token[p], 0), T);
+  for (int t = lo; t <= hi; ++t) tok_off[t] = (int32_t)p;
+}
+
+// mt_off[e] = sum over e' < e of ceil(M_e' / bm)  (row tiles of the dX GEMM)
+__global__ __launch_bounds__(kSelThreads) void k_tile_plan(int E, int bm,
+                                                           const int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ mt_off) {
+  __shared__ int lds[kSelThreads / kWave + 1];
+  block_scan_array<kSelThreads>(
+      E, [&](int e) { return (offsets[e + 1] - offsets[e] + bm - 1) / bm; }, mt_off, lds);
+}
+
+__global__ __launch_bounds__(256) void k_fill_u32(uint32_t* __restrict__ p, uint32_t v,
+                                                  int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// ------------------------------------------------------------- launchers
+
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  LRM_LAUNCH((unsigned)((n + 255) / 256), 256, 0, s, k_fill_u32)(p, v, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_bucket(const BucketArgs& a, hipStream_t s) {
+  const int nblk = bucket_blocks(a.N);
+  if (a.N > 0) {
+    LRM_LAUNCH(nblk, 256, a.E * sizeof(int), s, k_bucket_count)(a.N, a.T, a.E, kBucketChunk, a.token,
+                                                        a.expert, a.blkcnt, a.err);
+  }
+  LRM_LAUNCH(1, kSelThreads, a.E * sizeof(int), s, k_bucket_scan)(nblk, a.E, a.blkcnt, a.quota,
+                                                          a.cand_off, a.offsets);
+  if (a.N > 0) {
+    LRM_LAUNCH(nblk, 64, a.E * sizeof(int), s, k_bucket_scatter)(a.N, a.T, a.E, kBucketChunk, a.token,
+                                                         a.expert, a.blkcnt, a.cand_off, a.score,
+                                                         a.cand, a.keys, a.pos, a.keep_all);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_select(int E, const int32_t* cand_off, const int32_t* offsets,
+                         const uint32_t* keys, const int32_t* cand, int32_t* pos, int32_t* kept,
+                         hipStream_t s) {
+  LRM_LAUNCH(E, kSelThreads, 0, s, k_select)(cand_off, offsets, keys, cand, pos, kept);
+  return hipGetLastError();
+}
+
+hipError_t launch_kept_offsets(int E, const int32_t* cand_off, const int32_t* quota,
+                               int32_t* offsets, hipStream_t s) {
+  LRM_LAUNCH(1, kSelThreads, 0, s, k_kept_offsets)(E, cand_off, quota, offsets);
+  return hipGetLastError();
+}
+
+hipError_t launch_token_offsets(int N, int T, const int32_t* token, int32_t* tok_off,
+                                hipStream_t s) {
+  LRM_LAUNCH((N + 1 + 255) / 256, 256, 0, s, k_token_offsets)(N, T, token, tok_off);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_plan(int E, int bm, const int32_t* offsets, int32_t* mt_off,
+                            hipStream_t s) {
+  LRM_LAUNCH(1, kSelThreads, 0, s, k_tile_plan)(E, bm, offsets, mt_off);
+  return hipGetLastError();
+}
+
+}  // namespace lrm

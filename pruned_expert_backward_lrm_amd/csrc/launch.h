@@ -1,0 +1,131 @@
+// Internal launchers of the LRM kernels (host side).  Not part of the ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include "platform.h"
+
+namespace lrm {
+
+constexpr int kBucketChunk = 2048;  // pairs per bucketing block
+inline int bucket_blocks(int N) { return (N + kBucketChunk - 1) / kBucketChunk; }
+
+// --------------------------------------------------------------- score
+hipError_t launch_row_sumsq(const void* M, int bf16, int64_t ld, int cols, int rows,
+                            double* out, hipStream_t s);
+
+struct ScoreOperands {
+  int N, T, bf16;
+  const int32_t* token;
+  const float* weight;
+  // g factor: PAIR rows reduced inline (gtab == nullptr) or a table indexed by
+  // token (g_pair = 0) or by pair (g_pair = 1)
+  const void* G; int64_t ldg; int gcols; const double* gtab; int g_pair;
+  // x factor: same conventions; glu = 1 forms silu(A) * B rows inline instead
+  const void* X; int64_t ldx; int xcols; const double* xtab; int x_pair;
+  int glu; const void* A; const void* B; int64_t lda, ldb; int icols;
+  float* score;
+};
+hipError_t launch_pair_score(const ScoreOperands& op, hipStream_t s);
+
+// -------------------------------------------------------------- select
+struct BucketArgs {
+  int N, T, E;
+  const int32_t* token;
+  const int32_t* expert;
+  const int32_t* quota;  // device [E] or nullptr (keep all)
+  const float* score;    // nullptr: no keys gathered
+  int32_t* blkcnt;       // [bucket_blocks(N) * E]
+  int32_t* cand_off;     // [E+1]
+  int32_t* offsets;      // [E+1] kept offsets
+  int32_t* cand;         // [N]
+  uint32_t* keys;        // [N] or nullptr
+  int32_t* pos;          // [N]
+  int keep_all;          // pos written here (every valid pair kept, cand = kept)
+  uint32_t* err;
+};
+hipError_t launch_bucket(const BucketArgs& a, hipStream_t s);
+hipError_t launch_select(int E, const int32_t* cand_off, const int32_t* offsets,
+                         const uint32_t* keys, const int32_t* cand, int32_t* pos, int32_t* kept,
+                         hipStream_t s);
+hipError_t launch_kept_offsets(int E, const int32_t* cand_off, const int32_t* quota,
+                               int32_t* offsets, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
+hipError_t launch_token_offsets(int N, int T, const int32_t* token, int32_t* tok_off,
+                                hipStream_t s);
+hipError_t launch_tile_plan(int E, int bm, const int32_t* offsets, int32_t* mt_off,
+                            hipStream_t s);
+
+// ------------------------------------------------------------- compact
+// Row j < min(offsets[E], max_rows) of the packed block:
+//   a = kept[j]; p = pairmap ? pairmap[a] : a
+//   Xp[j] = w_p * X[x_pair ? p : token[p]]            (glu = 0)
+//   Xp[j] = w_p * silu(X[p]) * X2[p]                  (glu = 1, PAIR rows)
+//   Gp[j] = G[g_by_id ? a : (g_pair ? p : token[p])]
+struct CompactArgs {
+  int T, bf16, max_rows, E;
+  const int32_t* offsets;
+  const int32_t* kept;
+  const int32_t* pairmap;
+  const int32_t* token;
+  const float* weight;
+  const void* X; int64_t ldx; int xcols; int x_pair; void* Xp;
+  int glu; const void* X2; int64_t ldx2;
+  const void* G; int64_t ldg; int gcols; int g_pair; int g_by_id; void* Gp;
+};
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+
+// --------------------------------------------------------- grouped GEMM
+// For each expert e with packed rows [offsets[e], offsets[e+1]):
+//   dW[e]  = Gp_e^T Xp_e                 [d_out][d_in]
+//   dXp_e  = Gp_e W_e (+ Gp2_e W2_e)     [M_e][d_in]   (second term optional)
+struct GemmArgs {
+  int E, bf16, max_rows, d_in, d_out;
+  const int32_t* offsets;
+  const void* Gp;  // [rows][d_out]
+  const void* Xp;  // [rows][d_in]
+  const void* W; int64_t w_stride;  // [E][d_out][d_in]
+  const void* Gp2; const void* W2; int64_t w2_stride; int d_out2;  // optional
+  float* dW;   // [E][d_out][d_in] or nullptr
+  float* dXp;  // [max_rows][d_in] or nullptr
+  int32_t* mt_off;  // workspace [E+1]
+};
+int gemm_row_tile(int bf16);
+hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------ unpermute
+// Up to two sources; the row of pair p in source k is
+//   r = pos_k[p]; if (r >= 0 && pos2_k) r = pos2_k[r];
+struct ScatterArgs {
+  int N, T, d, out_pair;
+  const int32_t* token;
+  const float* weight;
+  const int32_t* tok_off;  // [T+1] (TOKEN output)
+  const int32_t* pos[2];
+  const int32_t* pos2[2];
+  const float* src[2];
+  float* dX;
+};
+hipError_t launch_unpermute(const ScatterArgs& a, hipStream_t s);
+
+// --------------------------------------------------------- SwiGLU backward
+// For down-kept row m < min(offsets_down[E], max_rows), p = kept_down[m]:
+//   u = U[m]; a = A[p]; b = B[p]
+//   ga = u * b * silu'(a) -> GA[m];  gb = u * silu(a) -> GB[m]
+//   s_gate[m] = w^2 |ga|^2 x2[row of p];  s_up[m] = w^2 |gb|^2 x2[row of p]
+struct GluBwdArgs {
+  int T, bf16, max_rows, E, I;
+  const int32_t* offsets_down;
+  const int32_t* kept_down;
+  const int32_t* token;
+  const float* weight;
+  const float* U;  // [rows][I] fp32
+  const void* A; int64_t lda;
+  const void* B; int64_t ldb;
+  const double* x2; int x_pair;
+  void* GA; void* GB;  // [rows][I]
+  float* s_gate; float* s_up;
+};
+hipError_t launch_glu_bwd(const GluBwdArgs& a, hipStream_t s);
+
+}  // namespace lrm

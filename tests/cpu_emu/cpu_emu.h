@@ -1,0 +1,222 @@
+// CPU emulation of the HIP subset used by the LRM kernels -- TEST
+// INFRASTRUCTURE ONLY.  It lets the unchanged kernel sources be compiled as
+// host C++ (with AddressSanitizer) so that every global-memory access of a
+// kernel can be bounds-checked on the CPU.  The product binding never loads a
+// library built with it.
+//
+// Model: each thread of a block is a std::thread; blocks run one after the
+// other, so static __shared__ arrays are shared by the threads of the running
+// block.  __syncthreads is a block barrier, wave collectives (ballot,
+// shuffles, MFMA) exchange values through a 64-slot buffer between two wave
+// barriers.  Lanes that have returned leave both barriers and drop out of
+// ballots.  The MFMA model follows the documented 16x16 layouts: A row =
+// lane%16, B column = lane%16, 8 consecutive k per lane group lane/16, and
+// D[4*(lane/16)+i][lane%16] in accumulator element i.
+#pragma once
+
+#include <algorithm>
+#include <barrier>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <memory>
+#include <thread>
+#include <tuple>
+#include <vector>
+
+#define __global__
+#define __device__
+#define __host__
+#define __forceinline__ inline
+#define __launch_bounds__(...)
+#define __shared__ static
+
+struct dim3 {
+  unsigned x, y, z;
+  dim3(unsigned a = 1, unsigned b = 1, unsigned c = 1) : x(a), y(b), z(c) {}
+};
+typedef int hipError_t;
+enum { hipSuccess = 0, hipErrorInvalidValue = 1 };
+typedef void* hipStream_t;
+enum hipMemcpyKind {
+  hipMemcpyHostToHost, hipMemcpyHostToDevice, hipMemcpyDeviceToHost, hipMemcpyDeviceToDevice,
+  hipMemcpyDefault
+};
+inline hipError_t hipMemcpyAsync(void* d, const void* s, size_t n, hipMemcpyKind, hipStream_t) {
+  std::memcpy(d, s, n);
+  return hipSuccess;
+}
+inline hipError_t hipMemcpy(void* d, const void* s, size_t n, hipMemcpyKind) {
+  std::memcpy(d, s, n);
+  return hipSuccess;
+}
+inline hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
+inline hipError_t hipGetLastError() { return hipSuccess; }
+
+namespace emu {
+
+struct Wave {
+  std::unique_ptr<std::barrier<>> bar;
+  uint64_t slot[64];
+  unsigned char wide[64][32];
+  bool active[64];
+};
+
+struct Ctx {
+  dim3 tid, bid;
+  int lane = 0, wave = 0;
+};
+inline thread_local Ctx ctx;
+inline dim3 g_blockDim, g_gridDim;
+inline unsigned char* g_dyn = nullptr;
+inline std::barrier<>* g_block = nullptr;
+inline std::vector<Wave>* g_waves = nullptr;
+
+inline void syncthreads() { g_block->arrive_and_wait(); }
+inline Wave& wave() { return (*g_waves)[ctx.wave]; }
+
+template <typename T>
+inline T exchange(T v, int src) {
+  Wave& w = wave();
+  uint64_t bits = 0;
+  std::memcpy(&bits, &v, sizeof(T));
+  w.slot[ctx.lane] = bits;
+  w.bar->arrive_and_wait();
+  uint64_t got = w.slot[src];
+  w.bar->arrive_and_wait();
+  T out;
+  std::memcpy(&out, &got, sizeof(T));
+  return out;
+}
+
+inline void wave_barrier() { wave().bar->arrive_and_wait(); }
+
+inline uint64_t ballot(bool p) {
+  Wave& w = wave();
+  w.slot[ctx.lane] = p ? 1 : 0;
+  w.bar->arrive_and_wait();
+  uint64_t m = 0;
+  for (int i = 0; i < 64; ++i)
+    if (w.active[i] && w.slot[i]) m |= 1ull << i;
+  w.bar->arrive_and_wait();
+  return m;
+}
+
+inline float bf16f(__bf16 h) {
+  uint16_t u;
+  std::memcpy(&u, &h, 2);
+  uint32_t x = uint32_t(u) << 16;
+  float f;
+  std::memcpy(&f, &x, 4);
+  return f;
+}
+
+template <typename V8, typename F4>
+inline F4 mfma16x16x32(V8 a, V8 b, F4 c) {
+  Wave& w = wave();
+  std::memcpy(w.wide[ctx.lane], &a, 16);
+  std::memcpy(w.wide[ctx.lane] + 16, &b, 16);
+  w.bar->arrive_and_wait();
+  const int l = ctx.lane;
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * (l / 16) + i, col = l % 16;
+    double s = 0.0;
+    for (int k = 0; k < 32; ++k) {
+      __bf16 av, bv;
+      std::memcpy(&av, w.wide[r + 16 * (k / 8)] + 2 * (k % 8), 2);
+      std::memcpy(&bv, w.wide[col + 16 * (k / 8)] + 16 + 2 * (k % 8), 2);
+      s += (double)bf16f(av) * (double)bf16f(bv);
+    }
+    c[i] += (float)s;
+  }
+  w.bar->arrive_and_wait();
+  return c;
+}
+
+template <typename... KArgs>
+struct Launch {
+  dim3 g, b;
+  size_t sh;
+  void (*k)(KArgs...);
+  template <typename... Args>
+  void operator()(Args&&... args) {
+    std::tuple<KArgs...> targs(std::forward<Args>(args)...);
+    const unsigned nt = b.x * b.y * b.z;
+    const unsigned nw = (nt + 63) / 64;
+    for (unsigned bz = 0; bz < g.z; ++bz)
+      for (unsigned by = 0; by < g.y; ++by)
+        for (unsigned bx = 0; bx < g.x; ++bx) {
+          std::vector<unsigned char> dyn(sh + 16, 0xCD);
+          std::barrier<> block(nt);
+          std::vector<Wave> waves(nw);
+          for (unsigned w = 0; w < nw; ++w) {
+            const unsigned n = std::min(64u, nt - 64 * w);
+            waves[w].bar = std::make_unique<std::barrier<>>(n);
+            for (int i = 0; i < 64; ++i) waves[w].active[i] = i < (int)n;
+          }
+          g_blockDim = b;
+          g_gridDim = g;
+          g_dyn = dyn.data();
+          g_block = &block;
+          g_waves = &waves;
+          std::vector<std::thread> th;
+          th.reserve(nt);
+          for (unsigned t = 0; t < nt; ++t) {
+            th.emplace_back([&, t] {
+              ctx.tid = dim3(t % b.x, (t / b.x) % b.y, t / (b.x * b.y));
+              ctx.bid = dim3(bx, by, bz);
+              ctx.lane = t % 64;
+              ctx.wave = t / 64;
+              std::apply(k, targs);
+              Wave& wv = waves[t / 64];
+              wv.active[t % 64] = false;
+              wv.bar->arrive_and_drop();
+              block.arrive_and_drop();
+            });
+          }
+          for (auto& x : th) x.join();
+        }
+  }
+};
+
+template <typename... KArgs>
+Launch<KArgs...> launch(dim3 g, dim3 b, size_t sh, hipStream_t, void (*k)(KArgs...)) {
+  return Launch<KArgs...>{g, b, sh, k};
+}
+
+}  // namespace emu
+
+#define threadIdx (::emu::ctx.tid)
+#define blockIdx (::emu::ctx.bid)
+#define blockDim (::emu::g_blockDim)
+#define gridDim (::emu::g_gridDim)
+#define __syncthreads() ::emu::syncthreads()
+#define LRM_LAUNCH(g, b, sh, s, ...) ::emu::launch(dim3(g), dim3(b), (sh), (s), &__VA_ARGS__)
+#define LRM_DYN_SHARED(T, name) T* name = reinterpret_cast<T*>(::emu::g_dyn)
+#define __builtin_amdgcn_wave_barrier() ::emu::wave_barrier()
+#define __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, x, y, z) ::emu::mfma16x16x32((a), (b), (c))
+
+template <typename T, typename U>
+inline T min(T a, U b) { return a < (T)b ? a : (T)b; }
+template <typename T, typename U>
+inline T max(T a, U b) { return a > (T)b ? a : (T)b; }
+inline unsigned __float_as_uint(float f) { unsigned u; std::memcpy(&u, &f, 4); return u; }
+inline float __uint_as_float(unsigned u) { float f; std::memcpy(&f, &u, 4); return f; }
+inline int __clz(int x) { return x == 0 ? 32 : __builtin_clz((unsigned)x); }
+inline int __popcll(unsigned long long x) { return __builtin_popcountll(x); }
+inline unsigned long long __ballot(int p) { return ::emu::ballot(p != 0); }
+template <typename T>
+inline T __shfl_xor(T v, int o, int = 64) { return ::emu::exchange(v, ::emu::ctx.lane ^ o); }
+template <typename T>
+inline T __shfl_up(T v, unsigned o, int = 64) {
+  const int src = ::emu::ctx.lane - (int)o;
+  T got = ::emu::exchange(v, src >= 0 ? src : ::emu::ctx.lane);
+  return src >= 0 ? got : v;
+}
+inline int atomicAdd(int* p, int v) { return __atomic_fetch_add(p, v, __ATOMIC_RELAXED); }
+inline unsigned atomicOr(unsigned* p, unsigned v) { return __atomic_fetch_or(p, v, __ATOMIC_RELAXED); }
+#include <math.h>
+
+

@@ -1,0 +1,311 @@
+"""GPU parity of the single-projection (LINEAR) pruned backward, through the C
+ABI, against the fp64 oracle: each step on its own, then the fused call."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import lrm_oracle as O
+from pruned_expert_backward_lrm_amd import synth
+
+from parity import (TOL, check_packing, check_selection, judge_linear, kept_from_pos, rel_fro,
+                    run_linear)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from pruned_expert_backward_lrm_amd import lrm
+    return lrm
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# ----------------------------------------------------------------- score
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("x_rows,g_rows", [("token", "pair"), ("pair", "token"),
+                                           ("token", "token"), ("pair", "pair")])
+def test_score_layouts(L, dtype, x_rows, g_rows):
+    say("score", dtype, x_rows, g_rows)
+    p = synth.make_linear(300, 6, 3, 72 if dtype == "f32" else 80, 48, dtype=dtype,
+                          x_rows=x_rows, g_rows=g_rows, seed=1)
+    r = p["routing"]
+    pairs = L.Pairs.from_routing(r, DEV)
+    X, G = p["X"].to(DEV), p["G"].to(DEV)
+    score = torch.empty(r.N, device=DEV)
+    L.lrm_score(pairs, L.mat(X, x_rows), L.mat(G, g_rows), score)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(score.cpu().numpy().astype(np.float64), O.linear_scores(p),
+                               rtol=2 ** -23, atol=0)
+
+
+def test_score_glu(L):
+    say("score_glu")
+    p = synth.make_swiglu(200, 5, 2, 64, 96, dtype="bf16", seed=2)
+    r = p["routing"]
+    pairs = L.Pairs.from_routing(r, DEV)
+    score = torch.empty(r.N, device=DEV)
+    L.lrm_score_glu(pairs, L.mat(p["A"].to(DEV), "pair"), L.mat(p["B"].to(DEV), "pair"),
+                    L.mat(p["G"].to(DEV), "token"), score)
+    torch.cuda.synchronize()
+    # silu in fp32 on the GPU: a few ulp per element, inside the select window
+    got = score.cpu().numpy().astype(np.float64)
+    ref = O.swiglu_down_scores(p)
+    rel = np.abs(got - ref) / ref
+    say("  glu score max rel err", rel.max(), "mean", rel.mean())
+    assert rel.max() < 1e-6, rel.max()
+
+
+# ---------------------------------------------------------------- select
+
+def _select(L, r, score_np, quota, flags=0):
+    pairs = L.Pairs.from_routing(r, DEV)
+    N = max(r.N, 1)
+    score = torch.as_tensor(np.asarray(score_np, np.float32), device=DEV)
+    pos = torch.full((N,), -7, dtype=torch.int32, device=DEV)
+    kept = torch.full((N,), -7, dtype=torch.int32, device=DEV)
+    offsets = torch.full((r.E + 1,), -7, dtype=torch.int32, device=DEV)
+    ws = L.lrm_select(pairs, score, quota, pos, offsets, kept, flags=flags, device=DEV)
+    torch.cuda.synchronize()
+    return pos.cpu().numpy()[: r.N], offsets.cpu().numpy(), kept.cpu().numpy(), ws
+
+
+@pytest.mark.parametrize("case", ["half", "zero", "all", "over", "ones", "ties", "empty_experts",
+                                  "single"])
+def test_select_cases(L, case):
+    say("select", case)
+    T, E, k = 700, 9, 2
+    p = synth.make_linear(T, E, k, 16, 16, dtype="f32", seed=3, zipf=1.3)
+    r = p["routing"]
+    rng = np.random.default_rng(4)
+    s = rng.random(r.N).astype(np.float32)
+    c = r.counts
+    q = {"half": c // 2, "zero": 0 * c, "all": c, "over": c + 5, "ones": np.ones_like(c),
+         "ties": c // 3, "empty_experts": c // 2, "single": np.minimum(c, 1)}[case]
+    if case == "ties":
+        s = rng.integers(0, 4, r.N).astype(np.float32)  # massive exact ties
+    if case == "empty_experts":
+        # experts 0, 3 and 8 receive no pairs at all
+        keep = ~np.isin(r.expert, [0, 3, 8])
+        r = synth.Routing(r.T, E, k, r.expert[keep], r.token[keep], r.weight[keep],
+                          np.bincount(r.expert[keep], minlength=E), {})
+        s = s[keep]
+        q = r.counts // 2 + (np.arange(E) % 2)
+    if case == "single":
+        keep = np.zeros(r.N, bool)
+        for e in range(E):
+            keep[np.nonzero(r.expert == e)[0][:1]] = True
+        r = synth.Routing(r.T, E, k, r.expert[keep], r.token[keep], r.weight[keep],
+                          np.bincount(r.expert[keep], minlength=E), {})
+        s = s[keep]
+    pos, offsets, kept, _ = _select(L, r, s, q)
+    s64 = s.astype(np.float64)
+    ora = O.select_top_quota(r.expert, s64, q, E)
+    gk = kept_from_pos(pos, r.expert, E)
+    # fp32 keys are the oracle's own inputs here: sets must be identical
+    for e in range(E):
+        assert np.array_equal(gk[e], ora[e]), f"expert {e}"
+    check_packing(pos, offsets, r.expert, E)
+    M = offsets[-1]
+    assert np.array_equal(kept[:M], np.concatenate(ora) if ora else kept[:0])
+
+
+def test_select_large_expert(L):
+    """One expert with 70k candidates (multi-pass radix, many waves)."""
+    say("select large")
+    T, E, k = 40000, 4, 2
+    rng = np.random.default_rng(5)
+    token = np.repeat(np.arange(T, dtype=np.int32), k)
+    expert = np.where(rng.random(T * k) < 0.88, 0, rng.integers(1, E, T * k)).astype(np.int32)
+    r = synth.Routing(T, E, k, expert, token, rng.random(T * k).astype(np.float32),
+                      np.bincount(expert, minlength=E), {})
+    s = (rng.standard_normal(r.N) ** 2 * 1e-3).astype(np.float32)
+    s[::97] = s[5]  # ties straddling the threshold region
+    q = (r.counts * 3) // 7
+    pos, offsets, kept, _ = _select(L, r, s, q)
+    ora = O.select_top_quota(r.expert, s.astype(np.float64), q, E)
+    gk = kept_from_pos(pos, r.expert, E)
+    for e in range(E):
+        assert np.array_equal(gk[e], ora[e]), f"expert {e}"
+    check_packing(pos, offsets, r.expert, E)
+
+
+def test_select_keep_all_and_index_errors(L):
+    say("select keep_all / index errors")
+    p = synth.make_linear(128, 5, 2, 16, 16, dtype="f32", seed=6)
+    r = p["routing"]
+    pos, offsets, kept, ws = _select(L, r, np.zeros(r.N), None, flags=L.LRM_KEEP_ALL)
+    assert np.all(pos >= 0)
+    check_packing(pos, offsets, r.expert, r.E)
+    assert L.lrm_check_device_errors(ws) == L.LRM_OK
+    # out-of-range experts are reported and treated as absent
+    bad = r.expert.copy()
+    bad[[3, 50]] = [r.E + 2, -1]
+    r2 = synth.Routing(r.T, r.E, r.k, bad, r.token, r.weight, r.counts, {})
+    q = np.full(r.E, 1000, np.int32)
+    pos, offsets, kept, ws = _select(L, r2, np.ones(r.N), q)
+    assert pos[3] == -1 and pos[50] == -1
+    assert offsets[-1] == r.N - 2
+    assert L.lrm_check_device_errors(ws) == 8  # LRM_ERR_INDEX
+    assert L.lrm_check_device_errors(ws) == L.LRM_OK  # cleared
+
+
+# ------------------------------------------- compact, GEMM, unpermute alone
+
+def _oracle_packing(p, kept_sets):
+    r = p["routing"]
+    offsets, kept_list, pos = O.pack(kept_sets, r.N)
+    return offsets.astype(np.int32), kept_list.astype(np.int32), pos.astype(np.int32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_compact_gemm_unpermute_steps(L, dtype):
+    say("steps", dtype)
+    d_in, d_out = (72, 40) if dtype == "f32" else (264, 136)  # several tiles + ragged tails
+    p = synth.make_linear(900, 7, 3, d_in, d_out, dtype=dtype, seed=7, zipf=1.0,
+                          quota=lambda c: (2 * c) // 3)
+    r = p["routing"]
+    kept_sets = O.select_top_quota(r.expert, O.linear_scores(p), p["quota"], r.E)
+    offsets, kept_list, pos = _oracle_packing(p, kept_sets)
+    M = int(offsets[-1])
+    max_rows = M + 5
+    pairs = L.Pairs.from_routing(r, DEV)
+    X, G, W = (p[k].to(DEV) for k in ("X", "G", "W"))
+    dt = X.dtype
+    t_off = torch.as_tensor(offsets, device=DEV)
+    t_kept = torch.as_tensor(kept_list, device=DEV)
+    Xp = torch.zeros(max_rows, d_in, dtype=dt, device=DEV)
+    Gp = torch.zeros(max_rows, d_out, dtype=dt, device=DEV)
+    L.lrm_compact(pairs, t_kept, t_off, max_rows, L.mat(X, "token"), L.mat(G, "pair"), Xp, Gp)
+    torch.cuda.synchronize()
+    # Gp is an exact row copy; Xp = w * x rounded once to the input dtype
+    g_ref = O.pair_rows(p["G"], "pair", r.token, kept_list)
+    assert np.array_equal(Gp[:M].float().cpu().numpy().astype(np.float64), g_ref)
+    x_ref = r.weight[kept_list].astype(np.float64)[:, None] * O.pair_rows(p["X"], "token",
+                                                                          r.token, kept_list)
+    ulp = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -23
+    np.testing.assert_allclose(Xp[:M].float().cpu().numpy(), x_ref, rtol=ulp, atol=1e-30)
+    dW = torch.full((r.E, d_out, d_in), float("nan"), device=DEV)
+    dXp = torch.full((max_rows, d_in), float("nan"), device=DEV)
+    L.lrm_grouped_bwd(r.E, t_off, max_rows, Gp, Xp, W, d_in, d_out, dW, dXp)
+    torch.cuda.synchronize()
+    # reference products on the GPU's own packed operands (exact fp64 sums)
+    Gp64 = Gp[:M].double().cpu().numpy()
+    Xp64 = Xp[:M].double().cpu().numpy()
+    tol = TOL[dtype] / 20
+    for e in range(r.E):
+        a, b = offsets[e], offsets[e + 1]
+        ref = Gp64[a:b].T @ Xp64[a:b]
+        got = dW[e].cpu().numpy()
+        if a == b:
+            assert not got.any()
+        else:
+            assert rel_fro(got, ref) < tol, e
+        refx = Gp64[a:b] @ O.f64(p["W"][e])
+        assert rel_fro(dXp[a:b].cpu().numpy(), refx) < tol, e
+    assert torch.isnan(dXp[M:]).all(), "rows past the kept count must stay untouched"
+    dX = torch.full((r.T, d_in), float("nan"), device=DEV)
+    L.lrm_unpermute(pairs, torch.as_tensor(pos, device=DEV), dXp, d_in, "token", dX)
+    torch.cuda.synchronize()
+    dxp = dXp[:M].double().cpu().numpy()
+    ref = np.zeros((r.T, d_in))
+    np.add.at(ref, r.token[kept_list], r.weight[kept_list].astype(np.float64)[:, None] * dxp)
+    assert rel_fro(dX.cpu().numpy(), ref) < 1e-6
+    assert not dX.cpu().numpy()[~np.isin(np.arange(r.T), r.token[kept_list])].any()
+    dXpair = torch.full((r.N, d_in), float("nan"), device=DEV)
+    L.lrm_unpermute(pairs, torch.as_tensor(pos, device=DEV), dXp, d_in, "pair", dXpair)
+    torch.cuda.synchronize()
+    refp = np.zeros((r.N, d_in))
+    refp[kept_list] = r.weight[kept_list].astype(np.float64)[:, None] * dxp
+    assert rel_fro(dXpair.cpu().numpy(), refp) < 1e-6
+
+
+def test_gemm_zero_rows_and_heavy_expert(L):
+    """M = 0 everywhere (all dW zero), then one expert holding 3000 rows."""
+    say("gemm zero/heavy")
+    E, d_in, d_out = 6, 128, 256
+    W = synth.normal((E, d_out, d_in), 0.02, torch.bfloat16, DEV, "t", 1)
+    for sizes in ([0] * E, [0, 3000, 0, 1, 129, 0]):
+        offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+        M = int(offsets[-1])
+        rows = max(M, 1)
+        Gp = synth.normal((rows, d_out), 1.0, torch.bfloat16, DEV, "t", 2)
+        Xp = synth.normal((rows, d_in), 1.0, torch.bfloat16, DEV, "t", 3)
+        dW = torch.full((E, d_out, d_in), float("nan"), device=DEV)
+        dXp = torch.full((rows, d_in), float("nan"), device=DEV)
+        L.lrm_grouped_bwd(E, torch.as_tensor(offsets, device=DEV), M, Gp, Xp, W, d_in, d_out,
+                          dW, dXp)
+        torch.cuda.synchronize()
+        G64, X64 = Gp.double().cpu().numpy(), Xp.double().cpu().numpy()
+        for e in range(E):
+            a, b = offsets[e], offsets[e + 1]
+            got = dW[e].cpu().numpy()
+            if a == b:
+                assert not got.any()
+            else:
+                assert rel_fro(got, G64[a:b].T @ X64[a:b]) < 1e-3
+                assert rel_fro(dXp[a:b].cpu().numpy(),
+                               G64[a:b] @ O.f64(W[e].cpu())) < 1e-3
+
+
+# ------------------------------------------------------------ fused call
+
+@pytest.mark.parametrize("x_rows,g_rows", [("token", "pair"), ("pair", "token")])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fused_linear_small(L, dtype, x_rows, g_rows):
+    say("fused linear", dtype, x_rows, g_rows)
+    p = synth.make_linear(600, 10, 4, 136, 200, dtype=dtype, x_rows=x_rows, g_rows=g_rows,
+                          seed=8, zipf=1.4, quota=lambda c: (c * 5) // 8 + (c % 3 == 0))
+    res = run_linear(L, p, DEV)
+    s = judge_linear(p, res)
+    say("  ", s)
+
+
+def test_fused_linear_config1(L):
+    p = synth.make_config(1)
+    res = run_linear(L, p, DEV)
+    s = judge_linear(p, res)
+    say("config1", s)
+    assert s["kept"] == 253
+
+
+def test_fused_linear_keep_all_is_unpruned(L):
+    p = synth.make_linear(500, 8, 2, 64, 128, dtype="bf16", seed=9, zipf=1.0)
+    res = run_linear(L, p, DEV, flags=L.LRM_KEEP_ALL)
+    s = judge_linear(p, res, keep_all=True)
+    assert s["kept"] == p["routing"].N
+
+
+def test_fused_linear_quota_zero(L):
+    p = synth.make_linear(300, 6, 2, 64, 64, dtype="bf16", seed=10, quota=lambda c: 0 * c)
+    res = run_linear(L, p, DEV)
+    assert not res["dW"].any() and not res["dX"].any()
+    assert (res["pos"].numpy()[: p["routing"].N] == -1).all()
+
+
+def test_fused_linear_deterministic(L):
+    p = synth.make_linear(800, 12, 4, 256, 128, dtype="bf16", seed=11, zipf=1.2)
+    a = run_linear(L, p, DEV)
+    b = run_linear(L, p, DEV)
+    for k in ("dW", "dX", "score", "pos", "offsets"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_fused_linear_config2(L):
+    """Qwen3-30B-A3B-shaped projection at full size (the benchmark workload)."""
+    say("config2: generating")
+    p = synth.make_config(2, device=DEV)
+    say("config2: running")
+    res = run_linear(L, p, DEV)
+    say("config2: oracle")
+    host = dict(p, X=p["X"].cpu(), G=p["G"].cpu(), W=p["W"].cpu())
+    s = judge_linear(host, res)
+    say("config2", s)
+    assert s["kept"] == int(np.minimum(p["quota"], p["routing"].counts).sum())
