@@ -207,8 +207,8 @@ typedef struct lrm_problem {
   int32_t d_in, d_out;
   const int32_t* quota;
   /* SWIGLU: expert MLP W_down (silu(W_gate x) * (W_up x)).  X: saved input
-   * (H cols, TOKEN), G: incoming gradient at the layer output (H cols, TOKEN
-   * or PAIR), A, B: saved gate/up pre-activations (I cols, PAIR), weights
+   * (H cols, TOKEN), G: incoming gradient at the layer output (H cols,
+   * TOKEN), A, B: saved gate/up pre-activations (I cols, PAIR), weights
    * W_gate, W_up device [E][I][H], W_down device [E][H][I] (dense, stride
    * I*H), quotas HOST [E] per projection. */
   lrm_mat A;
@@ -239,6 +239,9 @@ typedef struct lrm_outputs {
   int32_t* pos_up;         /* device [max down rows] */
   int32_t* offsets_gate;   /* device [E+1] */
   int32_t* offsets_up;     /* device [E+1] */
+  /* SwiGLU: the unscaled hidden gradient u = W_down^T g of every down-kept
+   * row, fp32 [max down rows][I] (the input of the gate/up scores). */
+  float* dH;
 } lrm_outputs;
 
 /* The whole pruned expert backward of one layer call, all steps enqueued on
@@ -254,6 +257,22 @@ typedef struct lrm_outputs {
  * ws: device scratch of lrm_workspace_size(prob) bytes, 256-byte aligned. */
 lrm_status lrm_expert_backward(const lrm_problem* prob, const lrm_outputs* out, void* ws,
                                size_t ws_bytes, void* stream);
+
+/* lrm_expert_backward, additionally recording events[i] (a hipEvent_t created
+ * by the caller, passed as void*) on the stream at stage boundary i, for each
+ * i < n_events with events[i] != NULL.  Boundaries:
+ *   LINEAR: 0 start, 1 after score, 2 after select, 3 after compaction,
+ *           4 after the grouped GEMM, 5 after unpermute (end);
+ *   SWIGLU: 0 start, 1 after the down score, 2 after the down select, 3 after
+ *           the down compaction, 4 after the down grouped GEMM, 5 after the
+ *           SwiGLU backward with the gate/up scores, 6 after the gate/up
+ *           selects, 7 after the gate/up compaction, 8 after the gate/up
+ *           grouped GEMMs, 9 after unpermute (end).
+ * The time between consecutive events is that stage's device time on the
+ * stream (for profiling; the results are those of lrm_expert_backward). */
+lrm_status lrm_expert_backward_events(const lrm_problem* prob, const lrm_outputs* out, void* ws,
+                                      size_t ws_bytes, void* stream, void* const* events,
+                                      int32_t n_events);
 
 /* Workspace bytes lrm_expert_backward needs for prob (0 if prob is invalid).
  * Packed buffers are sized from the host quotas: min(N, sum of quotas) rows. */

@@ -83,12 +83,28 @@ def pair_rows(mat, rows: str, token: np.ndarray, pairs: np.ndarray) -> np.ndarra
     return np.asarray(mat[idx], dtype=np.float64)
 
 
+def _chunks(n: int, chunk: int, fn) -> None:
+    """Apply fn(r0, r1) to row ranges; ranges are independent, so they may run
+    on several host threads without changing any result."""
+    import concurrent.futures as cf
+    import os
+    ranges = [(r0, min(r0 + chunk, n)) for r0 in range(0, n, chunk)]
+    if len(ranges) <= 1:
+        for a, b in ranges:
+            fn(a, b)
+        return
+    with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(lambda ab: fn(*ab), ranges))
+
+
 def row_sumsq(mat, chunk: int = 8192) -> np.ndarray:
     """Sum of squares of every row, in fp64 (rows visited in chunks)."""
     out = np.empty(mat.shape[0], dtype=np.float64)
-    for r0 in range(0, mat.shape[0], chunk):
-        m = f64(mat[r0:r0 + chunk])
-        out[r0:r0 + chunk] = (m * m).sum(axis=1)
+
+    def work(r0, r1):
+        m = f64(mat[r0:r1])
+        out[r0:r1] = (m * m).sum(axis=1)
+    _chunks(mat.shape[0], chunk, work)
     return out
 
 
@@ -266,11 +282,11 @@ def swiglu_down_scores(p: dict) -> np.ndarray:
     r = p["routing"]
     gs = row_sumsq(p["G"])[r.token]
     hs = np.empty(r.N)
-    for r0 in range(0, r.N, 8192):
-        a = f64(p["A"][r0:r0 + 8192])
-        b = f64(p["B"][r0:r0 + 8192])
-        h = silu(a) * b
-        hs[r0:r0 + 8192] = (h * h).sum(axis=1)
+
+    def work(r0, r1):
+        h = silu(f64(p["A"][r0:r1])) * f64(p["B"][r0:r1])
+        hs[r0:r1] = (h * h).sum(axis=1)
+    _chunks(r.N, 8192, work)
     return lrm_score(r.weight, gs, hs)
 
 
@@ -300,23 +316,32 @@ def swiglu_gate_up_grads(p: dict, kd: np.ndarray, u: np.ndarray):
 
 
 def swiglu_reference(p: dict, experts=None, keep_all: bool = False,
-                     u_override: dict | None = None) -> dict:
+                     u_override: dict | None = None, kept: dict | None = None) -> dict:
     """The SwiGLU expert backward (reading R-glu), expert by expert.
 
     ``experts`` limits which experts' weight gradients and pair gradients are
     formed (all by default); kept sets of the down stage are always complete.
     ``u_override[e]`` replaces the hidden gradient of expert e's down-kept
     pairs (used to judge the second selection on another implementation's
-    own intermediate values).  Returns kept sets, scores, dW per expert and,
-    when every expert is formed, dX [T, H]."""
+    own intermediate values).  ``kept`` may hold any of "down" (a list per
+    expert), "gate" and "up" (dicts by expert): given kept sets replace the
+    corresponding selections (the same arithmetic re-run on another
+    implementation's choices; when "down" is given no down scores are formed).
+    Returns kept sets, scores, dW per expert and, when every expert is
+    formed, dX [T, H]."""
     r = p["routing"]
     E = r.E
     big = np.full(E, r.N, dtype=np.int64)
     qd = big if keep_all else p["quota_down"]
     qg = big if keep_all else p["quota_gate"]
     qu = big if keep_all else p["quota_up"]
-    s_down = swiglu_down_scores(p)
-    K_down = select_top_quota(r.expert, s_down, qd, E)
+    kept = kept or {}
+    if "down" not in kept:
+        s_down = swiglu_down_scores(p)
+        K_down = select_top_quota(r.expert, s_down, qd, E)
+    else:
+        s_down = None
+        K_down = [np.sort(np.asarray(k, dtype=np.int64)) for k in kept["down"]]
     x2 = row_sumsq(p["X"])
     experts = list(range(E)) if experts is None else list(experts)
     out = dict(s_down=s_down, K_down=K_down, K_gate={}, K_up={}, s_gate={}, s_up={},
@@ -336,8 +361,14 @@ def swiglu_reference(p: dict, experts=None, keep_all: bool = False,
         s_full_g[kd] = sg
         s_full_u = np.zeros(r.N)
         s_full_u[kd] = su
-        Kg = select_top_quota(r.expert, s_full_g, qg, E, candidates=kd)[e]
-        Ku = select_top_quota(r.expert, s_full_u, qu, E, candidates=kd)[e]
+        if "gate" in kept:
+            Kg = np.sort(np.asarray(kept["gate"][e], dtype=np.int64))
+        else:
+            Kg = select_top_quota(r.expert, s_full_g, qg, E, candidates=kd)[e]
+        if "up" in kept:
+            Ku = np.sort(np.asarray(kept["up"][e], dtype=np.int64))
+        else:
+            Ku = select_top_quota(r.expert, s_full_u, qu, E, candidates=kd)[e]
         row = {pp: i for i, pp in enumerate(kd.tolist())}
         ig = np.array([row[pp] for pp in Kg.tolist()], dtype=np.int64)
         iu = np.array([row[pp] for pp in Ku.tolist()], dtype=np.int64)
@@ -363,6 +394,28 @@ def swiglu_reference(p: dict, experts=None, keep_all: bool = False,
             if kd.size:
                 np.add.at(dX, r.token[kd], dx)
         out["dX"] = dX
+    return out
+
+
+def swiglu_pair_dx(p: dict, pairs, in_gate, in_up) -> np.ndarray:
+    """Input-gradient row of each listed down-kept pair q (token t, expert e):
+    w_q (1[q kept by gate] ga_q W_gate_e + 1[q kept by up] gb_q W_up_e), with
+    u = W_down_e^T g_t, ga = u * b * silu'(a), gb = u * silu(a)."""
+    r = p["routing"]
+    out = np.zeros((len(pairs), p["H"]))
+    for i, q in enumerate(pairs):
+        q = int(q)
+        e, t = int(r.expert[q]), int(r.token[q])
+        g = f64(p["G"][t])
+        a = f64(p["A"][q])
+        b = f64(p["B"][q])
+        u = g @ f64(p["W_down"][e])
+        dx = np.zeros(p["H"])
+        if in_gate[i]:
+            dx += (u * b * dsilu(a)) @ f64(p["W_gate"][e])
+        if in_up[i]:
+            dx += (u * silu(a)) @ f64(p["W_up"][e])
+        out[i] = float(r.weight[q]) * dx
     return out
 
 

@@ -11,11 +11,11 @@
 //
 // bf16: v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  128x128 tile, BK 64,
 // 4 waves as 2x2, each wave 64x64 = 4x4 MFMA blocks.  Operands are staged in
-// LDS as [row][k] (k contiguous, rows padded to 144 B) so that each lane's
-// fragment (8 consecutive k) is one 16-byte LDS read.  Sources whose k runs
-// along rows (Gp and Xp in dW, W in dX) are loaded as 4x8 blocks with 16-byte
-// global loads and transposed in registers before the LDS store.  The next
-// k-tile's global loads are issued before the current tile's MFMAs.
+// LDS as [row][k] (k contiguous, XOR-swizzled 128-byte rows) so that each
+// lane's fragment (8 consecutive k) is one 16-byte LDS read.  Sources whose k
+// runs along rows (Gp and Xp in dW, W in dX) are loaded as 4x8 blocks with
+// 16-byte global loads and transposed in registers before the LDS store.  Two
+// LDS stages; global loads run two k-tiles ahead of the MFMAs.
 // The MFMA is issued with the N-side fragment first, so each lane's four
 // accumulators are four consecutive output columns (one 16-byte store).
 //
@@ -26,7 +26,6 @@
 namespace lrm {
 
 constexpr int BM = 128, BN = 128, BK = 64, NT = 256;
-constexpr int LDK = BK + 8;  // LDS row pitch in bf16 elements (144 bytes)
 
 __device__ __forceinline__ int xcd_remap(int b, int G) {
   // hardware places block b on XCD b % 8; give each XCD a contiguous range
@@ -43,7 +42,32 @@ __device__ __forceinline__ int find_expert(const int32_t* mt_off, int E, int mt)
   return lo;
 }
 
+// The two tile kinds are interleaved along the logical order so that every
+// XCD receives its proportional share of both: position L holds dX tile c(L)
+// when c(L+1) > c(L), with c(L) = floor(L * nX / (nW + nX)), and dW tile
+// L - c(L) otherwise (a bijection onto both tile lists).
+__device__ __forceinline__ bool is_dx_tile(int L, int nW, int nX, int* idx) {
+  const int64_t T = (int64_t)nW + nX;
+  const int c0 = (int)(((int64_t)L * nX) / T);
+  const int c1 = (int)(((int64_t)(L + 1) * nX) / T);
+  if (c1 > c0) {
+    *idx = c0;
+    return true;
+  }
+  *idx = L - c0;
+  return false;
+}
+
 // ------------------------------------------------------------------ bf16
+
+// LDS operand tile: 128 rows x 64 k (bf16), 128-byte rows, no padding.  The
+// 8-byte half-granules of row r are XOR-swizzled by 2*((r & 7) ^ ((r>>3) & 7))
+// (an even value, so 16-byte granules stay contiguous): the 16-byte fragment
+// reads (16 consecutive rows) and the transposed 8-byte stores (rows 8 apart)
+// both spread over all banks.
+__device__ __forceinline__ int lds_off(int r, int h) {
+  return r * BK + ((h ^ (((r & 7) ^ ((r >> 3) & 7)) << 1)) << 2);
+}
 
 struct Regs { u32x4 v[4]; };
 
@@ -64,7 +88,7 @@ __device__ __forceinline__ void store_direct(const Regs& R, uint16_t* lds) {
   for (int q = 0; q < 4; ++q) {
     const int idx = threadIdx.x + q * NT;
     const int r = idx >> 3, kc = idx & 7;
-    *reinterpret_cast<u32x4*>(lds + r * LDK + kc * 8) = R.v[q];
+    *reinterpret_cast<u32x4*>(lds + lds_off(r, 2 * kc)) = R.v[q];
   }
 }
 
@@ -93,7 +117,7 @@ __device__ __forceinline__ void store_trans(const Regs& R, uint16_t* lds) {
     u32x2 o;
     o[0] = pick_half(R.v[0][w], R.v[1][w], h);
     o[1] = pick_half(R.v[2][w], R.v[3][w], h);
-    *reinterpret_cast<u32x2*>(lds + (ng * 8 + c) * LDK + kg * 4) = o;
+    *reinterpret_cast<u32x2*>(lds + lds_off(ng * 8 + c, kg)) = o;
   }
 }
 
@@ -137,6 +161,9 @@ __device__ __forceinline__ TileSrc pick_seg(const TileSrc& x, const TileSrc& y, 
 }
 
 // One output tile: the K segments s0 and (if nseg == 2) s1 are summed.
+// Two LDS stages: while the MFMAs consume stage kt & 1, the registers holding
+// k-tile kt+1 are stored into the other stage and the global loads of k-tile
+// kt+2 are issued; one barrier per k-tile.
 template <bool A_DIRECT>
 __device__ __forceinline__ void mma_tile(const TileSrc& s0, const TileSrc& s1, int nseg, float* C,
                                          int64_t ldc, int rows_valid, int cols_valid,
@@ -152,31 +179,31 @@ __device__ __forceinline__ void mma_tile(const TileSrc& s0, const TileSrc& s1, i
   const int nk0 = (s0.K + BK - 1) / BK;
   const int nk1 = nseg > 1 ? (s1.K + BK - 1) / BK : 0;
   const int total = nk0 + nk1;
+  auto k_of = [&](int t) { return (t < nk0 ? t : t - nk0) * BK; };
 
   Regs RA, RB;
   if (total > 0) {
-    load_tile<A_DIRECT>(RA, RB, pick_seg(s0, s1, nk0 > 0), 0);
+    load_tile<A_DIRECT>(RA, RB, pick_seg(s0, s1, 0 < nk0), 0);
     store_tile<A_DIRECT>(RA, RB, As, Bs);
+    if (total > 1) load_tile<A_DIRECT>(RA, RB, pick_seg(s0, s1, 1 < nk0), k_of(1));
     __syncthreads();
   }
   for (int kt = 0; kt < total; ++kt) {
-    const int nt = kt + 1;
-    if (nt < total) {
-      const bool first = nt < nk0;
-      load_tile<A_DIRECT>(RA, RB, pick_seg(s0, s1, first), (first ? nt : nt - nk0) * BK);
-    }
+    const int cur = (kt & 1) * (BM * BK);
+    const uint16_t* Ac = As + cur;
+    const uint16_t* Bc = Bs + cur;
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
+    for (int kk = 0; kk < BK / 8; kk += 4) {
       bf16x8 af[4], bf[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = wm * 64 + i * 16 + (l & 15);
-        af[i] = *reinterpret_cast<const bf16x8*>(As + row * LDK + kk + (l >> 4) * 8);
+        af[i] = *reinterpret_cast<const bf16x8*>(Ac + lds_off(row, 2 * (kk + (l >> 4))));
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int col = wn * 64 + j * 16 + (l & 15);
-        bf[j] = *reinterpret_cast<const bf16x8*>(Bs + col * LDK + kk + (l >> 4) * 8);
+        bf[j] = *reinterpret_cast<const bf16x8*>(Bc + lds_off(col, 2 * (kk + (l >> 4))));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -184,11 +211,13 @@ __device__ __forceinline__ void mma_tile(const TileSrc& s0, const TileSrc& s1, i
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
     }
-    __syncthreads();
-    if (nt < total) {
-      store_tile<A_DIRECT>(RA, RB, As, Bs);
-      __syncthreads();
+    if (kt + 1 < total) {
+      const int nxt = ((kt + 1) & 1) * (BM * BK);
+      store_tile<A_DIRECT>(RA, RB, As + nxt, Bs + nxt);
+      if (kt + 2 < total)
+        load_tile<A_DIRECT>(RA, RB, pick_seg(s0, s1, kt + 2 < nk0), k_of(kt + 2));
     }
+    __syncthreads();
   }
   // lane holds C[row = .. + (l & 15)][col = .. + (l >> 4) * 4 + 0..3]
 #pragma unroll
@@ -209,13 +238,16 @@ struct GemmPlan {
 };
 
 __global__ __launch_bounds__(NT) void k_grouped_gemm_bf16(GemmPlan P) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t As[2 * BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2 * BN * BK];
   const GemmArgs& a = P.a;
   const int L = xcd_remap(blockIdx.x, P.G);
-  if (L < P.nW) {
+  if (L >= P.nW + P.nX) return;
+  int idx;
+  const bool dx = is_dx_tile(L, P.nW, P.nX, &idx);
+  if (!dx) {
     const int per = P.ntm_w * P.ntn;
-    const int e = L / per, rem = L % per;
+    const int e = idx / per, rem = idx % per;
     const int i0 = (rem / P.ntn) * BM, j0 = (rem % P.ntn) * BN;
     const int kb = a.offsets[e];
     const int Me = max(0, min(a.offsets[e + 1], a.max_rows) - kb);
@@ -229,9 +261,7 @@ __global__ __launch_bounds__(NT) void k_grouped_gemm_bf16(GemmPlan P) {
     mma_tile<false>(s, s, 1, C, a.d_in, min(BM, a.d_out - i0), min(BN, a.d_in - j0), As, Bs);
     return;
   }
-  const int Lx = L - P.nW;
-  if (Lx >= P.nX) return;
-  const int mt = Lx / P.ntn, tn = Lx % P.ntn;
+  const int mt = idx / P.ntn, tn = idx % P.ntn;
   if (mt >= a.mt_off[a.E]) return;
   const int e = find_expert(a.mt_off, a.E, mt);
   const int m0 = a.offsets[e] + (mt - a.mt_off[e]) * BM;
@@ -324,9 +354,12 @@ __device__ void f32_tile(const F32Seg& s0, const F32Seg& s1, int nseg, float* C,
 __global__ __launch_bounds__(NT) void k_grouped_gemm_f32(GemmPlan P) {
   const GemmArgs& a = P.a;
   const int L = xcd_remap(blockIdx.x, P.G);
-  if (L < P.nW) {
+  if (L >= P.nW + P.nX) return;
+  int idx;
+  const bool dx = is_dx_tile(L, P.nW, P.nX, &idx);
+  if (!dx) {
     const int per = P.ntm_w * P.ntn;
-    const int e = L / per, rem = L % per;
+    const int e = idx / per, rem = idx % per;
     const int i0 = (rem / P.ntn) * FBM, j0 = (rem % P.ntn) * FBN;
     const int kb = a.offsets[e];
     const int Me = max(0, min(a.offsets[e + 1], a.max_rows) - kb);
@@ -338,9 +371,7 @@ __global__ __launch_bounds__(NT) void k_grouped_gemm_f32(GemmPlan P) {
     f32_tile(s, s, 1, C, a.d_in, min(FBM, a.d_out - i0), min(FBN, a.d_in - j0), i0, j0);
     return;
   }
-  const int Lx = L - P.nW;
-  if (Lx >= P.nX) return;
-  const int mt = Lx / P.ntn, tn = Lx % P.ntn;
+  const int mt = idx / P.ntn, tn = idx % P.ntn;
   if (mt >= a.mt_off[a.E]) return;
   const int e = find_expert(a.mt_off, a.E, mt);
   const int m0 = a.offsets[e] + (mt - a.mt_off[e]) * FBM;

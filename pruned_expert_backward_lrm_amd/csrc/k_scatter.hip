@@ -22,23 +22,56 @@ __device__ __forceinline__ f32x4 ld4(const float* p) {
   return *reinterpret_cast<const f32x4*>(p);
 }
 
+// Columns held in registers per pass: kUnpChunks x 64 lanes x 4 floats.
+constexpr int kUnpChunks = 8;
+
+// One wave per token.  The token's pair descriptors (source rows, weight) are
+// loaded once, one pair per lane, and broadcast with shuffles; each pair then
+// issues kUnpChunks independent 16-byte loads per lane.
 __global__ __launch_bounds__(256) void k_unpermute_token(ScatterArgs a) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;
+  const int l = lane_id();
   const int p0 = min(max(a.tok_off[t], 0), a.N);
   const int p1 = min(max(a.tok_off[t + 1], p0), a.N);
   float* out = a.dX + (int64_t)t * a.d;
-  for (int c = lane_id() * 4; c < a.d; c += kWave * 4) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int p = p0; p < p1; ++p) {
-      const float w = a.weight[p];
+  for (int cb = 0; cb < a.d; cb += kUnpChunks * kWave * 4) {
+    f32x4 acc[kUnpChunks];
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int r = src_row(a, k, p);
-        if (r >= 0) acc += w * ld4(a.src[k] + (int64_t)r * a.d + c);
+    for (int u = 0; u < kUnpChunks; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int pb = p0; pb < p1; pb += kWave) {
+      const int pi = pb + l;
+      int r0 = -1, r1 = -1;
+      float w = 0.f;
+      if (pi < p1) {
+        w = a.weight[pi];
+        r0 = src_row(a, 0, pi);
+        r1 = src_row(a, 1, pi);
+      }
+      const int np = min(kWave, p1 - pb);
+      for (int j = 0; j < np; ++j) {
+        const float wj = __shfl(w, j, kWave);
+        const int rj0 = __shfl(r0, j, kWave);
+        const int rj1 = __shfl(r1, j, kWave);
+        if (rj0 >= 0) {
+          const float* src = a.src[0] + (int64_t)rj0 * a.d + cb + l * 4;
+#pragma unroll
+          for (int u = 0; u < kUnpChunks; ++u)
+            if (cb + (u * kWave + l) * 4 < a.d) acc[u] += wj * ld4(src + u * kWave * 4);
+        }
+        if (rj1 >= 0) {
+          const float* src = a.src[1] + (int64_t)rj1 * a.d + cb + l * 4;
+#pragma unroll
+          for (int u = 0; u < kUnpChunks; ++u)
+            if (cb + (u * kWave + l) * 4 < a.d) acc[u] += wj * ld4(src + u * kWave * 4);
+        }
       }
     }
-    *reinterpret_cast<f32x4*>(out + c) = acc;
+#pragma unroll
+    for (int u = 0; u < kUnpChunks; ++u) {
+      const int c = cb + (u * kWave + l) * 4;
+      if (c < a.d) *reinterpret_cast<f32x4*>(out + c) = acc[u];
+    }
   }
 }
 

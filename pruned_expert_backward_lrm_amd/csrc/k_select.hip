@@ -97,11 +97,12 @@ __global__ __launch_bounds__(256) void k_bucket_count(int N, int T, int E, int c
   }
   if (bad) atomicOr(err, bad);
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) blkcnt[(int64_t)blockIdx.x * E + e] = hist[e];
+  for (int e = threadIdx.x; e < E; e += 256) blkcnt[(int64_t)e * gridDim.x + blockIdx.x] = hist[e];
 }
 
-// blkcnt[b][e] -> exclusive within-expert offset of block b; cand_off = prefix
-// of the per-expert counts; offsets = prefix of M_e = min(quota_e, n_e)
+// blkcnt[e][b] -> exclusive within-expert offset of block b (one wave scans
+// one expert's block counts, 64 at a time); cand_off = prefix of the
+// per-expert counts; offsets = prefix of M_e = min(quota_e, n_e)
 // (quota == nullptr: keep all).
 __global__ __launch_bounds__(kSelThreads) void k_bucket_scan(int nblk, int E,
                                                              int32_t* __restrict__ blkcnt,
@@ -110,14 +111,17 @@ __global__ __launch_bounds__(kSelThreads) void k_bucket_scan(int nblk, int E,
                                                              int32_t* __restrict__ offsets) {
   LRM_DYN_SHARED(int, counts);  // [E]
   __shared__ int lds[kSelThreads / kWave + 1];
-  for (int e = threadIdx.x; e < E; e += kSelThreads) {
+  const int w = threadIdx.x >> 6, l = lane_id();
+  for (int e = w; e < E; e += kSelThreads / kWave) {
+    int32_t* row = blkcnt + (int64_t)e * nblk;
     int run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      const int v = blkcnt[(int64_t)b * E + e];
-      blkcnt[(int64_t)b * E + e] = run;
-      run += v;
+    for (int b0 = 0; b0 < nblk; b0 += kWave) {
+      const int v = (b0 + l < nblk) ? row[b0 + l] : 0;
+      const int incl = wave_incl_scan(v);
+      if (b0 + l < nblk) row[b0 + l] = run + incl - v;
+      run += __shfl(incl, kWave - 1, kWave);
     }
-    counts[e] = run;
+    if (l == 0) counts[e] = run;
   }
   __syncthreads();
   block_scan_array<kSelThreads>(E, [&](int e) { return counts[e]; }, cand_off, lds);
@@ -158,7 +162,7 @@ __global__ __launch_bounds__(64) void k_bucket_scatter(int N, int T, int E, int 
                                                        int32_t* __restrict__ pos, int keep_all) {
   LRM_DYN_SHARED(int, run);  // [E]
   const int l = lane_id();
-  for (int e = l; e < E; e += kWave) run[e] = cand_off[e] + blkcnt[(int64_t)blockIdx.x * E + e];
+  for (int e = l; e < E; e += kWave) run[e] = cand_off[e] + blkcnt[(int64_t)e * gridDim.x + blockIdx.x];
   __syncthreads();
   const int nbits = (E > 1) ? 32 - __clz(E - 1) : 0;
   const int64_t p0 = (int64_t)blockIdx.x * chunk;
@@ -323,14 +327,15 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s) {
 
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s) {
   const int nblk = bucket_blocks(a.N);
+  const int chunk = bucket_chunk(a.N);
   if (a.N > 0) {
-    LRM_LAUNCH(nblk, 256, a.E * sizeof(int), s, k_bucket_count)(a.N, a.T, a.E, kBucketChunk, a.token,
+    LRM_LAUNCH(nblk, 256, a.E * sizeof(int), s, k_bucket_count)(a.N, a.T, a.E, chunk, a.token,
                                                         a.expert, a.blkcnt, a.err);
   }
   LRM_LAUNCH(1, kSelThreads, a.E * sizeof(int), s, k_bucket_scan)(nblk, a.E, a.blkcnt, a.quota,
                                                           a.cand_off, a.offsets);
   if (a.N > 0) {
-    LRM_LAUNCH(nblk, 64, a.E * sizeof(int), s, k_bucket_scatter)(a.N, a.T, a.E, kBucketChunk, a.token,
+    LRM_LAUNCH(nblk, 64, a.E * sizeof(int), s, k_bucket_scatter)(a.N, a.T, a.E, chunk, a.token,
                                                          a.expert, a.blkcnt, a.cand_off, a.score,
                                                          a.cand, a.keys, a.pos, a.keep_all);
   }

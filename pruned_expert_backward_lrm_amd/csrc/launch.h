@@ -7,8 +7,12 @@
 
 namespace lrm {
 
-constexpr int kBucketChunk = 2048;  // pairs per bucketing block
-inline int bucket_blocks(int N) { return (N + kBucketChunk - 1) / kBucketChunk; }
+// Pairs per bucketing block: at least 256, and at most 1024 blocks.
+inline int bucket_chunk(int N) {
+  const int c = (N + 1023) / 1024;
+  return c <= 256 ? 256 : (c + 63) / 64 * 64;
+}
+inline int bucket_blocks(int N) { return (N + bucket_chunk(N) - 1) / bucket_chunk(N); }
 
 // --------------------------------------------------------------- score
 hipError_t launch_row_sumsq(const void* M, int bf16, int64_t ld, int cols, int rows,
@@ -35,7 +39,7 @@ struct BucketArgs {
   const int32_t* expert;
   const int32_t* quota;  // device [E] or nullptr (keep all)
   const float* score;    // nullptr: no keys gathered
-  int32_t* blkcnt;       // [bucket_blocks(N) * E]
+  int32_t* blkcnt;       // [E][bucket_blocks(N)]
   int32_t* cand_off;     // [E+1]
   int32_t* offsets;      // [E+1] kept offsets
   int32_t* cand;         // [N]

@@ -510,6 +510,7 @@ GluPlan carve_glu(Carve& c, const lrm_problem* pb, const lrm_outputs* out, int64
     if (out->pos_up) L.pos_u = out->pos_up;
     if (out->offsets_gate) L.off_g = out->offsets_gate;
     if (out->offsets_up) L.off_u = out->offsets_up;
+    if (out->dH) L.U = out->dH;
   }
   return L;
 }
@@ -560,8 +561,8 @@ lrm_status check_problem(const lrm_problem* pb, const lrm_outputs* out) {
   } else if (pb->kind == LRM_SWIGLU) {
     if (pb->H <= 0 || pb->I <= 0) return LRM_ERR_SHAPE;
     if (pb->H % q || pb->I % q) return LRM_ERR_UNSUPPORTED;
-    LRM_TRY(check_mat(&pb->X, p, pb->dtype, pb->H, -1));
-    LRM_TRY(check_mat(&pb->G, p, pb->dtype, pb->H, -1));
+    LRM_TRY(check_mat(&pb->X, p, pb->dtype, pb->H, LRM_ROWS_TOKEN));
+    LRM_TRY(check_mat(&pb->G, p, pb->dtype, pb->H, LRM_ROWS_TOKEN));
     LRM_TRY(check_mat(&pb->A, p, pb->dtype, pb->I, LRM_ROWS_PAIR));
     LRM_TRY(check_mat(&pb->B, p, pb->dtype, pb->I, LRM_ROWS_PAIR));
     if (!pb->W_gate || !pb->W_up || !pb->W_down) return LRM_ERR_NULL;
@@ -605,19 +606,34 @@ size_t plan_size(const lrm_problem* pb, const lrm_outputs* out) {
   return c.size();
 }
 
-lrm_status run_linear(const lrm_problem* pb, const lrm_outputs* out, void* ws, hipStream_t s) {
+// Optional profiling events recorded at stage boundaries.
+struct Marks {
+  void* const* ev;
+  int n;
+  hipStream_t s;
+  hipError_t operator()(int i) const {
+    if (ev && i < n && ev[i]) return hipEventRecord(reinterpret_cast<hipEvent_t>(ev[i]), s);
+    return hipSuccess;
+  }
+};
+
+lrm_status run_linear(const lrm_problem* pb, const lrm_outputs* out, void* ws, hipStream_t s,
+                      const Marks& mark) {
   const lrm_pairs* p = &pb->pairs;
   const bool keep_all = (pb->flags & LRM_KEEP_ALL) != 0;
   const int64_t Mcap = keep_all ? p->N : lrm_max_kept(p->N, p->E, pb->quota);
   Carve c(ws);
   LinearPlan L = carve_linear(c, pb, out, Mcap);
   const int bf16 = pb->dtype == LRM_BF16;
+  LRM_TRY_HIP(mark(0));
   LRM_TRY_HIP(launch_fill_u32(L.sel.err, 0u, 1, s));
   // 1. LRM score of every pair
   if (!keep_all) LRM_TRY_HIP(run_score(p, &pb->X, &pb->G, L.score, L.sc, s));
+  LRM_TRY_HIP(mark(1));
   // 2. per-expert top-quota selection and packed rows
   LRM_TRY(run_select(p, L.score, keep_all ? nullptr : pb->quota, L.pos, L.offsets, L.kept,
                      L.sel, s));
+  LRM_TRY_HIP(mark(2));
   // 3. compaction: Xp = w x, Gp = g
   CompactArgs ca{};
   ca.T = p->T; ca.bf16 = bf16; ca.max_rows = (int)Mcap; ca.E = p->E;
@@ -627,12 +643,14 @@ lrm_status run_linear(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   ca.G = pb->G.ptr; ca.ldg = pb->G.ld; ca.gcols = pb->d_out;
   ca.g_pair = pb->G.rows == LRM_ROWS_PAIR; ca.Gp = L.Gp;
   LRM_TRY_HIP(launch_compact(ca, s));
+  LRM_TRY_HIP(mark(3));
   // 4. grouped GEMM: dW_e = Gp_e^T Xp_e, dXp_e = Gp_e W_e
   GemmArgs g{};
   g.E = p->E; g.bf16 = bf16; g.max_rows = (int)Mcap; g.d_in = pb->d_in; g.d_out = pb->d_out;
   g.offsets = L.offsets; g.Gp = L.Gp; g.Xp = L.Xp; g.W = pb->W; g.w_stride = pb->w_stride;
   g.dW = out->dW; g.dXp = L.dXp; g.mt_off = L.mt_off;
   LRM_TRY_HIP(launch_grouped_gemm(g, s));
+  LRM_TRY_HIP(mark(4));
   // 5. back to the layout of X, times the routing weight
   ScatterArgs sa{};
   sa.N = p->N; sa.T = p->T; sa.d = pb->d_in; sa.out_pair = pb->X.rows == LRM_ROWS_PAIR;
@@ -643,10 +661,12 @@ lrm_status run_linear(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   }
   sa.dX = out->dX;
   LRM_TRY_HIP(launch_unpermute(sa, s));
+  LRM_TRY_HIP(mark(5));
   return LRM_OK;
 }
 
-lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, hipStream_t s) {
+lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, hipStream_t s,
+                      const Marks& mark) {
   const lrm_pairs* p = &pb->pairs;
   const bool keep_all = (pb->flags & LRM_KEEP_ALL) != 0;
   const GluSizes z = glu_sizes(pb);
@@ -654,11 +674,14 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   GluPlan L = carve_glu(c, pb, out, z.Md, z.Mg, z.Mu, z.pass_through);
   const int bf16 = pb->dtype == LRM_BF16;
   const int H = pb->H, I = pb->I, E = p->E;
+  LRM_TRY_HIP(mark(0));
   LRM_TRY_HIP(launch_fill_u32(L.sel.err, 0u, 1, s));
   // ---- down projection: input h = silu(a) * b, gradient g = G row
   if (!keep_all) LRM_TRY_HIP(run_score_glu(p, &pb->A, &pb->B, &pb->G, L.score, L.sc, s));
+  LRM_TRY_HIP(mark(1));
   LRM_TRY(run_select(p, L.score, keep_all ? nullptr : pb->quota_down, L.pos, L.offsets, L.kept,
                      L.sel, s));
+  LRM_TRY_HIP(mark(2));
   CompactArgs cd{};
   cd.T = p->T; cd.bf16 = bf16; cd.max_rows = (int)z.Md; cd.E = E;
   cd.offsets = L.offsets; cd.kept = L.kept; cd.token = p->token; cd.weight = p->weight;
@@ -667,12 +690,14 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   cd.G = pb->G.ptr; cd.ldg = pb->G.ld; cd.gcols = H; cd.g_pair = pb->G.rows == LRM_ROWS_PAIR;
   cd.Gp = L.Gd;
   LRM_TRY_HIP(launch_compact(cd, s));
+  LRM_TRY_HIP(mark(3));
   GemmArgs gd{};
   gd.E = E; gd.bf16 = bf16; gd.max_rows = (int)z.Md; gd.d_in = I; gd.d_out = H;
   gd.offsets = L.offsets; gd.Gp = L.Gd; gd.Xp = L.Hd;
   gd.W = pb->W_down; gd.w_stride = (int64_t)H * I;
   gd.dW = out->dW_down; gd.dXp = L.U; gd.mt_off = L.mt_off;
   LRM_TRY_HIP(launch_grouped_gemm(gd, s));
+  LRM_TRY_HIP(mark(4));
   // ---- SwiGLU backward and the gate/up scores
   const bool x_pair = pb->X.rows == LRM_ROWS_PAIR;
   if (!keep_all)
@@ -685,6 +710,7 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   gb.s_gate = keep_all ? nullptr : L.s_gate;
   gb.s_up = keep_all ? nullptr : L.s_up;
   LRM_TRY_HIP(launch_glu_bwd(gb, s));
+  LRM_TRY_HIP(mark(5));
   // ---- gate/up selections among the down-kept rows (candidate ids = rows)
   if (!keep_all) {
     LRM_TRY_HIP(hipMemcpyAsync(L.qgate, pb->quota_gate, sizeof(int32_t) * E,
@@ -699,6 +725,7 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
     LRM_TRY_HIP(launch_select(E, L.offsets, L.off_u, reinterpret_cast<const uint32_t*>(L.s_up),
                               nullptr, L.pos_u, L.kept_u, s));
   }
+  LRM_TRY_HIP(mark(6));
   const bool x_tok = !x_pair;
   ScatterArgs sa{};
   sa.N = p->N; sa.T = p->T; sa.d = H; sa.out_pair = x_pair;
@@ -711,6 +738,7 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
     cx.offsets = L.offsets; cx.kept = L.kept; cx.token = p->token; cx.weight = p->weight;
     cx.X = pb->X.ptr; cx.ldx = pb->X.ld; cx.xcols = H; cx.x_pair = x_pair; cx.Xp = L.Xgu;
     LRM_TRY_HIP(launch_compact(cx, s));
+    LRM_TRY_HIP(mark(7));
     GemmArgs gg{};
     gg.E = E; gg.bf16 = bf16; gg.max_rows = (int)z.Md; gg.d_in = H; gg.d_out = I;
     gg.offsets = L.offsets; gg.Gp = L.GA; gg.Xp = L.Xgu;
@@ -743,6 +771,9 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
       cg.X = pb->X.ptr; cg.ldx = pb->X.ld; cg.xcols = H; cg.x_pair = x_pair; cg.Xp = Xpv[k];
       cg.G = GAsrc[k]; cg.ldg = I; cg.gcols = I; cg.g_by_id = 1; cg.Gp = Gpv[k];
       LRM_TRY_HIP(launch_compact(cg, s));
+    }
+    LRM_TRY_HIP(mark(7));
+    for (int k = 0; k < 2; ++k) {
       GemmArgs gk{};
       gk.E = E; gk.bf16 = bf16; gk.max_rows = (int)cap[k]; gk.d_in = H; gk.d_out = I;
       gk.offsets = offv[k]; gk.Gp = Gpv[k]; gk.Xp = Xpv[k];
@@ -752,12 +783,14 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
       sa.pos[k] = L.pos; sa.pos2[k] = posv[k]; sa.src[k] = dXv[k];
     }
   }
+  LRM_TRY_HIP(mark(8));
   if (x_tok) {
     LRM_TRY_HIP(launch_token_offsets(p->N, p->T, p->token, L.tok_off, s));
     sa.tok_off = L.tok_off;
   }
   sa.dX = out->dX;
   LRM_TRY_HIP(launch_unpermute(sa, s));
+  LRM_TRY_HIP(mark(9));
   return LRM_OK;
 }
 
@@ -770,15 +803,22 @@ size_t lrm_workspace_size(const lrm_problem* prob) {
   return plan_size(prob, nullptr);
 }
 
-lrm_status lrm_expert_backward(const lrm_problem* prob, const lrm_outputs* out, void* ws,
-                               size_t ws_bytes, void* stream) {
+lrm_status lrm_expert_backward_events(const lrm_problem* prob, const lrm_outputs* out, void* ws,
+                                      size_t ws_bytes, void* stream, void* const* events,
+                                      int32_t n_events) {
   if (!out) return LRM_ERR_NULL;
   LRM_TRY(check_problem(prob, out));
   if (!ws || ws_bytes < plan_size(prob, out)) return LRM_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return LRM_ERR_ALIGN;
   hipStream_t s = as_stream(stream);
-  if (prob->kind == LRM_LINEAR) return run_linear(prob, out, ws, s);
-  return run_swiglu(prob, out, ws, s);
+  const Marks mark{events, n_events, s};
+  if (prob->kind == LRM_LINEAR) return run_linear(prob, out, ws, s, mark);
+  return run_swiglu(prob, out, ws, s, mark);
+}
+
+lrm_status lrm_expert_backward(const lrm_problem* prob, const lrm_outputs* out, void* ws,
+                               size_t ws_bytes, void* stream) {
+  return lrm_expert_backward_events(prob, out, ws, ws_bytes, stream, nullptr, 0);
 }
 
 }  // extern "C"

@@ -64,7 +64,7 @@ class lrm_problem(C.Structure):
 class lrm_outputs(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in (
         "dW", "dW_gate", "dW_up", "dW_down", "dX", "score", "pos", "offsets", "score_gate",
-        "score_up", "pos_gate", "pos_up", "offsets_gate", "offsets_up")]
+        "score_up", "pos_gate", "pos_up", "offsets_gate", "offsets_up", "dH")]
 
 
 _P = C.c_void_p
@@ -90,6 +90,8 @@ _sigs = {
     "lrm_unpermute_workspace_size": (_SZ, [C.POINTER(lrm_pairs)]),
     "lrm_expert_backward": (C.c_int, [C.POINTER(lrm_problem), C.POINTER(lrm_outputs), _P, _SZ,
                                       _P]),
+    "lrm_expert_backward_events": (C.c_int, [C.POINTER(lrm_problem), C.POINTER(lrm_outputs), _P,
+                                             _SZ, _P, C.POINTER(C.c_void_p), _I32]),
     "lrm_workspace_size": (_SZ, [C.POINTER(lrm_problem)]),
     "lrm_check_device_errors": (C.c_int, [_P, _P]),
 }
@@ -277,15 +279,37 @@ def lrm_workspace_size(pb: Problem) -> int:
     return int(_lib.lrm_workspace_size(C.byref(pb.c)))
 
 
-def lrm_expert_backward(pb: Problem, outputs: dict, ws=None, stream=None):
+def _outputs(outputs: dict) -> lrm_outputs:
     o = lrm_outputs()
     for k, v in outputs.items():
         setattr(o, k, _ptr(v))
-    if ws is None:
-        n = lrm_workspace_size(pb)
-        if n == 0:
-            raise LrmError(2, "lrm_workspace_size")
-        ws = torch.empty(n, dtype=torch.uint8, device=pb.pairs.token.device)
+    return o
+
+
+def _fused_ws(pb: Problem, ws):
+    if ws is not None:
+        return ws
+    n = lrm_workspace_size(pb)
+    if n == 0:
+        raise LrmError(2, "lrm_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=pb.pairs.token.device)
+
+
+def lrm_expert_backward(pb: Problem, outputs: dict, ws=None, stream=None):
+    o = _outputs(outputs)
+    ws = _fused_ws(pb, ws)
     _check(_lib.lrm_expert_backward(C.byref(pb.c), C.byref(o), _ptr(ws), ws.numel(),
                                     _stream(stream)), "lrm_expert_backward")
+    return ws
+
+
+def lrm_expert_backward_events(pb: Problem, outputs: dict, events, ws=None, stream=None):
+    """The fused call recording torch.cuda.Event objects at stage boundaries
+    (each event must have been recorded once so that its handle exists)."""
+    o = _outputs(outputs)
+    ws = _fused_ws(pb, ws)
+    arr = (C.c_void_p * len(events))(*[ev.cuda_event for ev in events])
+    _check(_lib.lrm_expert_backward_events(C.byref(pb.c), C.byref(o), _ptr(ws), ws.numel(),
+                                           _stream(stream), arr, len(events)),
+           "lrm_expert_backward_events")
     return ws

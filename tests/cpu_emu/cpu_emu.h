@@ -54,6 +54,8 @@ inline hipError_t hipMemcpy(void* d, const void* s, size_t n, hipMemcpyKind) {
 }
 inline hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
 inline hipError_t hipGetLastError() { return hipSuccess; }
+typedef void* hipEvent_t;
+inline hipError_t hipEventRecord(hipEvent_t, hipStream_t) { return hipSuccess; }
 
 namespace emu {
 
@@ -209,6 +211,8 @@ inline int __popcll(unsigned long long x) { return __builtin_popcountll(x); }
 inline unsigned long long __ballot(int p) { return ::emu::ballot(p != 0); }
 template <typename T>
 inline T __shfl_xor(T v, int o, int = 64) { return ::emu::exchange(v, ::emu::ctx.lane ^ o); }
+template <typename T>
+inline T __shfl(T v, int src, int = 64) { return ::emu::exchange(v, src & 63); }
 template <typename T>
 inline T __shfl_up(T v, unsigned o, int = 64) {
   const int src = ::emu::ctx.lane - (int)o;

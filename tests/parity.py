@@ -94,6 +94,156 @@ def run_linear(L, p: dict, device: str, flags: int = 0, ws=None):
     return res
 
 
+def run_swiglu(L, p: dict, device: str, flags: int = 0, ws=None):
+    """The fused SwiGLU backward through the C ABI, with every optional output
+    requested.  Returns host tensors."""
+    r = p["routing"]
+    keep_all = bool(flags & L.LRM_KEEP_ALL)
+    pairs = L.Pairs.from_routing(r, device)
+    t = {k: p[k].to(device) for k in ("X", "G", "A", "B", "W_gate", "W_up", "W_down")}
+    q = (None, None, None) if keep_all else (p["quota_down"], p["quota_gate"], p["quota_up"])
+    pb = L.swiglu_problem(pairs, t["X"], "token", t["G"], "token", t["A"], t["B"], t["W_gate"],
+                          t["W_up"], t["W_down"], *q, flags)
+    H, I, E, N = p["H"], p["I"], r.E, r.N
+    Md = N if keep_all else max(L.lrm_max_kept(N, p["quota_down"]), 1)
+    f32, i32 = dict(dtype=torch.float32, device=device), dict(dtype=torch.int32, device=device)
+    nan = float("nan")
+    out = dict(dW_gate=torch.full((E, I, H), nan, **f32), dW_up=torch.full((E, I, H), nan, **f32),
+               dW_down=torch.full((E, H, I), nan, **f32), dX=torch.full((r.T, H), nan, **f32),
+               score=torch.full((max(N, 1),), nan, **f32),
+               pos=torch.full((max(N, 1),), -7, **i32),
+               offsets=torch.full((E + 1,), -7, **i32),
+               score_gate=torch.full((Md,), nan, **f32), score_up=torch.full((Md,), nan, **f32),
+               pos_gate=torch.full((Md,), -7, **i32), pos_up=torch.full((Md,), -7, **i32),
+               offsets_gate=torch.full((E + 1,), -7, **i32),
+               offsets_up=torch.full((E + 1,), -7, **i32),
+               dH=torch.full((Md, I), nan, **f32))
+    ws = L.lrm_expert_backward(pb, out, ws=ws)
+    torch.cuda.synchronize()
+    res = {k: v.cpu() for k, v in out.items()}
+    res["ws"] = ws
+    return res
+
+
+def pick_experts(counts_kept: np.ndarray, k_heavy=2, k_mid=2, k_light=1, seed=0):
+    """A sample of experts: the heaviest, some median and light ones."""
+    order = np.argsort(-counts_kept, kind="stable")
+    nz = order[counts_kept[order] > 0]
+    pick = list(nz[:k_heavy])
+    if nz.size:
+        mid = nz.size // 2
+        pick += list(nz[mid:mid + k_mid])
+        pick += list(nz[-k_light:])
+    return sorted(set(int(e) for e in pick))
+
+
+def judge_swiglu(p: dict, res: dict, keep_all: bool = False, experts=None, tokens=None):
+    """Compare one fused SwiGLU result with the oracle (reading R-glu).
+
+    Down stage: scores and kept sets against the pure oracle.  Gate/up stages:
+    scores and kept sets against the oracle run on the GPU's own hidden
+    gradient u (the chained selection depends on it).  Gradients: the oracle
+    re-run on the GPU's kept sets.  ``experts`` samples the experts whose
+    weight gradients are formed; ``tokens`` samples dX rows (all if None)."""
+    r = p["routing"]
+    E, N, H, I = r.E, r.N, p["H"], p["I"]
+    tol = TOL[p["dtype"]]
+    pos = res["pos"][:N].numpy()
+    offs = res["offsets"].numpy().astype(np.int64)
+    check_packing(pos, offs, r.expert, E)
+    Kd = kept_from_pos(pos, r.expert, E)
+    summary = {"kept_down": int(offs[-1])}
+    if keep_all:
+        assert all(k.size == c for k, c in zip(Kd, r.counts))
+    else:
+        s64 = O.swiglu_down_scores(p)
+        gs = res["score"][:N].numpy().astype(np.float64)
+        rel = np.abs(gs - s64) / np.maximum(s64, 1e-300)
+        summary["score_down_max_rel"] = float(rel.max()) if N else 0.0
+        assert rel.max() < 1e-6 if N else True, rel.max()
+        ora_kd = O.select_top_quota(r.expert, s64, p["quota_down"], E)
+        summary["ndiff_down"] = check_selection(Kd, ora_kd, s64, r.counts, "down")
+    Md = int(offs[-1])
+    ex = list(range(E)) if experts is None else list(experts)
+    U = res["dH"].numpy()
+    kept_g, kept_u = {}, {}
+    for e in ex:
+        a, b = offs[e], offs[e + 1]
+        if keep_all:
+            kept_g[e], kept_u[e] = Kd[e], Kd[e]
+            continue
+        pg = res["pos_gate"].numpy()[a:b]
+        pu = res["pos_up"].numpy()[a:b]
+        kept_g[e], kept_u[e] = Kd[e][pg >= 0], Kd[e][pu >= 0]
+    if not keep_all:
+        # gate/up selections judged on the GPU's own u (upcast to fp64)
+        uo = {e: U[offs[e]:offs[e + 1]] for e in ex}
+        chk = O.swiglu_reference(p, experts=ex, u_override=uo, kept={"down": Kd})
+        for name, kg, key in (("gate", kept_g, "K_gate"), ("up", kept_u, "K_up")):
+            sk = "s_" + name
+            nd = 0
+            for e in ex:
+                kd = Kd[e]
+                gpu_s = res["score_" + name].numpy()[offs[e]:offs[e + 1]].astype(np.float64)
+                ref_s = chk[sk][e]
+                if kd.size:
+                    rel = np.abs(gpu_s - ref_s) / np.maximum(ref_s, 1e-300)
+                    assert rel.max() < 2e-6, (name, e, rel.max())
+                full = np.zeros(N)
+                full[kd] = ref_s
+                cnt = np.bincount(r.expert[kd], minlength=E)
+                nd += check_selection([kg[e]], [chk[key][e]], full, [cnt[e]], f"{name} e{e}")
+            summary["ndiff_" + name] = nd
+            o2 = res["offsets_" + name].numpy().astype(np.int64)
+            for e in ex:
+                assert o2[e + 1] - o2[e] == kg[e].size
+    # gradients on the GPU's kept sets
+    ref = O.swiglu_reference(p, experts=ex, kept={"down": Kd, "gate": kept_g, "up": kept_u})
+    errs = {}
+    for name in ("dW_down", "dW_gate", "dW_up"):
+        got = res[name].numpy()[ex]
+        want = np.stack([ref[name][e] for e in ex])
+        errs[name] = rel_fro(got, want)
+        assert errs[name] <= tol, (name, errs[name])
+    for e in range(E):
+        if offs[e + 1] == offs[e]:
+            assert not res["dW_down"][e].any() and not res["dW_gate"][e].any() \
+                and not res["dW_up"][e].any(), f"expert {e} kept nothing but dW != 0"
+    dX = res["dX"].numpy()
+    if experts is None and tokens is None:
+        errs["dX"] = rel_fro(dX, ref["dX"])
+        assert errs["dX"] <= tol, errs["dX"]
+        assert not dX[~np.any(ref["dX"] != 0, axis=1)].any()
+    else:
+        toks = np.asarray(tokens if tokens is not None else np.arange(min(r.T, 16)))
+        want = np.zeros((toks.size, H))
+        setg = {e: set(v.tolist()) for e, v in kept_g.items()}
+        setu = {e: set(v.tolist()) for e, v in kept_u.items()}
+        for i, t in enumerate(toks):
+            qs = [q for q in np.nonzero(r.token == t)[0] if pos[q] >= 0]
+            if not qs:
+                continue
+            ing, inu = [], []
+            for q in qs:
+                e = int(r.expert[q])
+                if keep_all:
+                    ing.append(True); inu.append(True)
+                    continue
+                if e not in setg:
+                    a, b = offs[e], offs[e + 1]
+                    kd = Kd[e]
+                    setg[e] = set(kd[res["pos_gate"].numpy()[a:b] >= 0].tolist())
+                    setu[e] = set(kd[res["pos_up"].numpy()[a:b] >= 0].tolist())
+                ing.append(q in setg[e])
+                inu.append(q in setu[e])
+            want[i] = O.swiglu_pair_dx(p, qs, ing, inu).sum(axis=0)
+        errs["dX_sampled"] = rel_fro(dX[toks], want)
+        assert errs["dX_sampled"] <= tol, errs["dX_sampled"]
+        assert not dX[toks][~np.any(want != 0, axis=1)].any()
+    summary.update(errs)
+    return summary
+
+
 def judge_linear(p: dict, res: dict, keep_all: bool = False, experts=None):
     """Compare one fused LINEAR result with the oracle.  Returns a summary."""
     r = p["routing"]

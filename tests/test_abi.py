@@ -32,7 +32,7 @@ def test_struct_layouts_match_header():
     # explicit padding in the header makes these sizes ABI-stable
     assert C.sizeof(L.lrm_pairs) == 40
     assert C.sizeof(L.lrm_mat) == 32
-    assert C.sizeof(L.lrm_outputs) == 14 * 8
+    assert C.sizeof(L.lrm_outputs) == 15 * 8
     assert L.lrm_problem.X.offset == 56 and L.lrm_problem.quota.offset == 144
     assert C.sizeof(L.lrm_problem) == 272
 

@@ -1,0 +1,89 @@
+"""GPU parity of the SwiGLU expert backward (down -> gate/up, each projection
+with its own LRM scores and quotas) through the fused C-ABI call, against the
+fp64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+from pruned_expert_backward_lrm_amd import synth
+
+from parity import judge_swiglu, pick_experts, run_swiglu
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from pruned_expert_backward_lrm_amd import lrm
+    return lrm
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+QUOTAS = {
+    # gate/up quotas at least the down quotas: the second selection keeps all
+    "same": (lambda c: c // 2, lambda c: c // 2, lambda c: c // 2),
+    # a real second selection with different gate and up quotas
+    "second": (lambda c: (3 * c) // 4, lambda c: (3 * c) // 8 + 1, lambda c: c // 3),
+}
+
+
+@pytest.mark.parametrize("variant", ["same", "second"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fused_swiglu_small(L, dtype, variant):
+    say("swiglu small", dtype, variant)
+    p = synth.make_swiglu(400, 6, 2, 136, 72, dtype=dtype, seed=5, zipf=1.2,
+                          quotas=QUOTAS[variant], g_std=1e-2)
+    s = judge_swiglu(p, run_swiglu(L, p, DEV))
+    say("  ", s)
+
+
+def test_fused_swiglu_keep_all(L):
+    p = synth.make_swiglu(300, 5, 2, 128, 64, dtype="bf16", seed=6, zipf=1.0)
+    s = judge_swiglu(p, run_swiglu(L, p, DEV, flags=L.LRM_KEEP_ALL), keep_all=True)
+    assert s["kept_down"] == p["routing"].N
+
+
+def test_fused_swiglu_quota_zero(L):
+    p = synth.make_swiglu(200, 4, 2, 64, 64, dtype="bf16", seed=7,
+                          quotas=(lambda c: 0 * c, lambda c: c, lambda c: c))
+    res = run_swiglu(L, p, DEV)
+    for k in ("dW_gate", "dW_up", "dW_down", "dX"):
+        assert not res[k].any(), k
+
+
+def test_fused_swiglu_deterministic(L):
+    p = synth.make_swiglu(500, 8, 2, 256, 128, dtype="bf16", seed=8, zipf=1.1,
+                          quotas=QUOTAS["second"])
+    a = run_swiglu(L, p, DEV)
+    b = run_swiglu(L, p, DEV)
+    for k in ("dW_gate", "dW_up", "dW_down", "dX", "score", "pos", "score_gate", "pos_gate",
+              "pos_up"):
+        assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("cfg", ["3", "3b", "4", "5"])
+def test_swiglu_configs(L, cfg):
+    """Full-size SwiGLU workloads: every kept set of the down stage, and the
+    gate/up kept sets and weight gradients of a sample of experts (heaviest,
+    median, light, plus every expert that kept nothing), dX on sampled tokens."""
+    cid = int(cfg[0])
+    say(f"config {cfg}: generating")
+    p = synth.make_config(cid, device=DEV, variant="3b" if cfg == "3b" else None)
+    say(f"config {cfg}: running")
+    res = run_swiglu(L, p, DEV)
+    host = dict(p, **{k: p[k].cpu() for k in ("X", "G", "A", "B", "W_gate", "W_up", "W_down")})
+    r = p["routing"]
+    kept = np.diff(res["offsets"].numpy())
+    ex = pick_experts(kept)
+    rng = np.random.default_rng(cid)
+    toks = np.sort(rng.choice(r.T, size=24, replace=False))
+    say(f"config {cfg}: oracle on experts {ex}")
+    s = judge_swiglu(host, res, experts=ex, tokens=toks)
+    say(f"config {cfg}", s)
