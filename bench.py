@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--variant", default=None, help="3b: a real gate/up second selection")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-full", action="store_true",
+                    help="skip the unpruned (keep-all) comparison run")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 512 MiB device copy (a known-size kernel that "
                          "calibrates the HBM byte counters of a profiler pass)")
@@ -236,8 +238,10 @@ def main():
     log("bench: timing the pruned backward")
     wall, per = time_fused(W, a.steps, a.warmup)
     M, Me = W.kept()
-    log("bench: timing the unpruned backward (every pair kept)")
-    ms_full = time_loop(W.step_full, a.steps, a.warmup) * 1e3
+    ms_full = None
+    if not a.no_full:
+        log("bench: timing the unpruned backward (every pair kept)")
+        ms_full = time_loop(W.step_full, a.steps, a.warmup) * 1e3
     work = W.work(M, Me)
     flops = sum(work[s]["flops"] for s in W.gemm_stages)
     gbytes = sum(work[s]["bytes"] for s in W.gemm_stages)
@@ -285,9 +289,9 @@ def main():
         "stages_gbs": {s: round(work[s]["bytes"] / (per[s] * 1e-3) / 1e9, 1) for s in mem_stages},
         "score_compact_gbs": round(sum(work[s]["bytes"] for s in sc)
                                    / (sum(per[s] for s in sc) * 1e-3) / 1e9, 1),
-        "unpruned_ms_per_step": round(ms_full, 4),
+        "unpruned_ms_per_step": round(ms_full, 4) if ms_full else None,
         "kept_fraction": round(M / r.N, 4),
-        "pruned_over_unpruned_time": round(wall * 1e3 / ms_full, 4),
+        "pruned_over_unpruned_time": round(wall * 1e3 / ms_full, 4) if ms_full else None,
     }
     if not a.no_cpu:
         log("bench: timing the CPU oracle")
