@@ -9,23 +9,28 @@
 // remapped so that consecutive tiles (the same expert) land on the same XCD
 // and share its L2.
 //
-// bf16: v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  128x128 tile, BK 64,
-// 4 waves as 2x2, each wave 64x64 = 4x4 MFMA blocks.  Operands are staged in
-// LDS as [row][k] (k contiguous, XOR-swizzled 128-byte rows) so that each
-// lane's fragment (8 consecutive k) is one 16-byte LDS read.  Sources whose k
-// runs along rows (Gp and Xp in dW, W in dX) are loaded as 4x8 blocks with
-// 16-byte global loads and transposed in registers before the LDS store.  Two
-// LDS stages; global loads run two k-tiles ahead of the MFMAs.
+// bf16: v_mfma_f32_16x16x32_bf16 with fp32 accumulation, BK 64, tile shapes
+// 128x128 (4 waves of 64x64), 256x128 (8 waves of 64x64) and 256x256 (8 waves
+// of 128x64).  Operands are staged in LDS as [row][k] (k contiguous, 128-byte
+// rows with a bank-aware granule swizzle) so that each lane's fragment (8
+// consecutive k) is one 16-byte LDS read.  Sources whose k runs along rows (Gp
+// and Xp in dW, W in dX) are loaded as 4x8 blocks with 16-byte buffer loads
+// and transposed in registers (v_perm) before the LDS store.  Two LDS stages;
+// global loads run two k-tiles ahead of the MFMAs.
 // The MFMA is issued with the N-side fragment first, so each lane's four
 // accumulators are four consecutive output columns (one 16-byte store).
 //
 // fp32: plain LDS-tiled fp32 FMA (64x64 tile) for fp32 inputs.
+#include <stdlib.h>
+
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
 namespace lrm {
 
-constexpr int BM = 128, BN = 128, BK = 64, NT = 256;
+constexpr int NT = 256;  // threads of an fp32 block
 
 __device__ __forceinline__ int xcd_remap(int b, int G) {
   // hardware places block b on XCD b % 8; give each XCD a contiguous range
@@ -58,176 +63,285 @@ __device__ __forceinline__ bool is_dx_tile(int L, int nW, int nX, int* idx) {
   return false;
 }
 
+// Grouped raster over an nr x nc tile grid: tiles are taken kRasterH rows at a
+// time, column by column, so the tiles resident on one XCD at any moment (a
+// window of consecutive positions) share a few row panels and a few column
+// panels in its L2 instead of one row panel and every column panel.
+constexpr int kRasterH = 4;
+__device__ __forceinline__ void raster(int t, int nr, int nc, int* r, int* c) {
+  const int r0 = t / (kRasterH * nc) * kRasterH;
+  const int gh = min(kRasterH, nr - r0);
+  const int rem = t - r0 * nc;
+  *r = r0 + rem % gh;
+  *c = rem / gh;
+}
+
 // ------------------------------------------------------------------ bf16
 
-// LDS operand tile: 128 rows x 64 k (bf16), 128-byte rows, no padding.  The
-// 8-byte half-granules of row r are XOR-swizzled by 2*((r & 7) ^ ((r>>3) & 7))
-// (an even value, so 16-byte granules stay contiguous): the 16-byte fragment
-// reads (16 consecutive rows) and the transposed 8-byte stores (rows 8 apart)
-// both spread over all banks.
-__device__ __forceinline__ int lds_off(int r, int h) {
-  return r * BK + ((h ^ (((r & 7) ^ ((r >> 3) & 7)) << 1)) << 2);
-}
-
-struct Regs { u32x4 v[4]; };
-
-// k-contiguous source: tile rows r in [0,128) at src + r*ld, k in [k0,k0+64)
-__device__ __forceinline__ void load_direct(Regs& R, const uint16_t* src, int64_t ld,
-                                            int rows_valid, int k0, int K) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int idx = threadIdx.x + q * NT;
-    const int r = idx >> 3, k = k0 + (idx & 7) * 8;
-    R.v[q] = (r < rows_valid && k < K)
-                 ? *reinterpret_cast<const u32x4*>(src + (int64_t)r * ld + k)
-                 : u32x4{0u, 0u, 0u, 0u};
-  }
-}
-__device__ __forceinline__ void store_direct(const Regs& R, uint16_t* lds) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int idx = threadIdx.x + q * NT;
-    const int r = idx >> 3, kc = idx & 7;
-    *reinterpret_cast<u32x4*>(lds + lds_off(r, 2 * kc)) = R.v[q];
-  }
-}
-
-// k-strided source: element (k, n) at src + k*ld + n.  Thread owns k rows
-// kg*4..kg*4+3 and columns ng*8..ng*8+7 of the 64x128 tile.
-__device__ __forceinline__ void load_trans(Regs& R, const uint16_t* src, int64_t ld, int k0,
-                                           int kend, int n0, int ncols) {
-  const int kg = threadIdx.x >> 4, ng = threadIdx.x & 15;
-  const int n = n0 + ng * 8;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int k = k0 + kg * 4 + r;
-    R.v[r] = (k < kend && n < ncols)
-                 ? *reinterpret_cast<const u32x4*>(src + (int64_t)k * ld + n)
-                 : u32x4{0u, 0u, 0u, 0u};
-  }
-}
-__device__ __forceinline__ uint32_t pick_half(uint32_t x, uint32_t y, int hi) {
-  return hi ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-}
-__device__ __forceinline__ void store_trans(const Regs& R, uint16_t* lds) {
-  const int kg = threadIdx.x >> 4, ng = threadIdx.x & 15;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int w = c >> 1, h = c & 1;
-    u32x2 o;
-    o[0] = pick_half(R.v[0][w], R.v[1][w], h);
-    o[1] = pick_half(R.v[2][w], R.v[3][w], h);
-    *reinterpret_cast<u32x2*>(lds + lds_off(ng * 8 + c, kg)) = o;
-  }
-}
-
-struct TileSrc {
-  // A side (output rows): direct (dX: Gp rows) or transposed (dW: Gp columns)
-  const uint16_t* a; int64_t lda; int a_rows_valid; int a_n0; int a_ncols;
-  // B side (output columns): always transposed
-  const uint16_t* b; int64_t ldb; int b_n0; int b_ncols;
-  int K;  // k extent of this segment (rows valid for the transposed sources)
+// A block tile configuration: BM x BN outputs, k-tiles of 64, WGM x WGN waves,
+// each wave owning a TM x TN sub-tile of FM x FN 16x16 MFMA blocks.
+template <int BM_, int BN_, int WGM_, int WGN_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = 64;
+  static constexpr int WGM = WGM_, WGN = WGN_, NW = WGM_ * WGN_, NT = 64 * NW;
+  static constexpr int TM = BM / WGM, TN = BN / WGN;
+  static constexpr int FM = TM / 16, FN = TN / 16;
+  static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile");
 };
 
-template <bool A_DIRECT>
-__device__ __forceinline__ void load_tile(Regs& RA, Regs& RB, const TileSrc& s, int k0) {
-  if constexpr (A_DIRECT)
-    load_direct(RA, s.a, s.lda, s.a_rows_valid, k0, s.K);
-  else
-    load_trans(RA, s.a, s.lda, k0, s.K, s.a_n0, s.a_ncols);
-  load_trans(RB, s.b, s.ldb, k0, s.K, s.b_n0, s.b_ncols);
+// LDS operand tile: R rows x 64 k (bf16), 128-byte rows, no padding.  The
+// 16-byte granule G of row r sits at granule G ^ f(r), with f built from row
+// bits as (r4, r3, r1 ^ r5).  On gfx950 a ds_read_b128 is served in four
+// passes of 16 lanes ({0-3, 12-15, 20-23, 24-27}, {4-7, 8-11, 16-19, 28-31}
+// and the same +32) over 64 four-byte banks, and a ds_write_b64 in passes of
+// 16 consecutive lanes over 32 banks (both measured with bank-conflict
+// counters).  With this f the fragment reads (16 consecutive rows, granules
+// g and g+1 in a pass) and the transposed 8-byte stores (16 lanes: 8 rows 8
+// apart x both halves of a granule) hit 16 distinct bank slots per pass.
+constexpr int BK = 64;
+__device__ __forceinline__ int lds_swz(int r) {
+  return ((r >> 4) & 1) | (r & 8) >> 2 | (((r >> 1) ^ (r >> 5)) & 1) << 2;
 }
-template <bool A_DIRECT>
-__device__ __forceinline__ void store_tile(const Regs& RA, const Regs& RB, uint16_t* As,
-                                           uint16_t* Bs) {
-  if constexpr (A_DIRECT) store_direct(RA, As); else store_trans(RA, As);
-  store_trans(RB, Bs);
+// element offset of 8-byte half-granule h (0..15) of row r
+__device__ __forceinline__ int lds_off(int r, int h) {
+  return r * BK + ((h ^ (lds_swz(r) << 1)) << 2);
 }
 
-// Field-wise select (keeps both descriptors in registers).
+// Operand panels are read with buffer loads: a buffer resource per k-tile
+// (scalar base and byte bound) plus per-lane byte offsets fixed for the whole
+// output tile.  Loads past the bound return zero in hardware, which pads the
+// k tail of a segment and the rows past an expert's block without any
+// per-lane masking or address arithmetic inside the k loop.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const char* base, int64_t nbytes) {
+  const int n = nbytes <= 0 ? 0 : (nbytes > 0x7ffffff0ll ? 0x7ffffff0 : (int)nbytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, n, kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 bload(rsrc_t r, int off) {
+  return (u32x4)__builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// Row panel, k contiguous (dX: Gp rows of one expert): row r at
+// base + r*ld, k-tile [k0, k0+64).  Bytes valid: rows_valid rows.
+template <int R, int NT>
+struct DirectTile {
+  static constexpr int Q = (R * 8 + NT - 1) / NT;
+  u32x4 v[Q];
+  int off[Q];
+  __device__ __forceinline__ void init(int64_t ld) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int idx = threadIdx.x + q * NT;
+      off[q] = idx < R * 8 ? (int)(((idx >> 3) * ld + (idx & 7) * 8) * 2) : 0x7ffffff0;
+    }
+  }
+  // k0: first k of the tile; K: k extent of the panel (zero past it: a lane
+  // whose 8 columns start at or past K takes an offset outside the bound)
+  __device__ __forceinline__ void load(const char* base, int64_t ld, int rows_valid, int k0,
+                                       int K) {
+    const rsrc_t rs = make_rsrc(base + (int64_t)k0 * 2, (int64_t)rows_valid * ld * 2 - k0 * 2);
+    const bool tail = k0 + (int)(threadIdx.x & 7) * 8 >= K;  // NT % 8 == 0
+#pragma unroll
+    for (int q = 0; q < Q; ++q) v[q] = bload(rs, tail ? 0x7ffffff0 : off[q]);
+  }
+  __device__ __forceinline__ void store(uint16_t* lds) const {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int idx = threadIdx.x + q * NT;
+      if ((R * 8) % NT == 0 || idx < R * 8)  // (threadIdx.x < NT)
+        *reinterpret_cast<u32x4*>(lds + lds_off(idx >> 3, 2 * (idx & 7))) = v[q];
+    }
+  }
+};
+
+// Two bf16 from the same half of x and y: (x.lo, y.lo) or (x.hi, y.hi), x in
+// the low half of the result.  One v_perm_b32 (bytes of y are 4..7).
+__device__ __forceinline__ uint32_t pick_half(uint32_t x, uint32_t y, int hi) {
+  return __builtin_amdgcn_perm(y, x, hi ? 0x07060302u : 0x05040100u);
+}
+
+// k-strided panel, R columns (dW: Gp and Xp columns; dX: W columns): element
+// (k, n) at base + k*ld + n, columns [n0, n0+R), rows k < kend valid.  The
+// tile is cut into 4(k) x 8(n) blocks, each read with four 16-byte loads and
+// transposed in registers into eight 8-byte LDS stores (rows n, 4 k each).
+template <int R, int NT>
+struct TransTile {
+  static constexpr int NB = 16 * (R / 8);  // blocks per tile
+  static constexpr int Q = (NB + NT - 1) / NT;
+  static constexpr int NHI = R / 64;         // groups of 8 column blocks
+  static_assert(R % 64 == 0, "transposed tile width");
+  u32x4 v[Q][4];
+  int off[Q];
+  // Block b -> (k group kg of 4 rows, column group ng of 8).  Lanes 0-7 take 8
+  // column groups, lane bit 3 the k-group parity, so each 16-lane store pass
+  // covers both halves of a granule (see lds_swz).
+  __device__ __forceinline__ static void block_of(int b, int* kg, int* ng) {
+    *ng = (b & 7) + 8 * ((b >> 4) % NHI);
+    *kg = ((b >> 3) & 1) + 2 * ((b >> 4) / NHI);
+  }
+  __device__ __forceinline__ void init(int64_t ld) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int b = threadIdx.x + q * NT;
+      int kg, ng;
+      block_of(b, &kg, &ng);
+      off[q] = b < NB ? (int)((kg * 4 * ld + ng * 8) * 2) : 0x7ffffff0;
+    }
+  }
+  __device__ __forceinline__ void load(const char* base, int64_t ld, int k0, int kend, int n0) {
+    const rsrc_t rs = make_rsrc(base + ((int64_t)k0 * ld + n0) * 2,
+                                (int64_t)(kend - k0) * ld * 2 - (int64_t)n0 * 2);
+    const int row = (int)(ld * 2);
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[q][r] = bload(rs, off[q] + r * row);
+  }
+  __device__ __forceinline__ void store(uint16_t* lds) const {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int b = threadIdx.x + q * NT;
+      if (NB % NT != 0 && b >= NB) continue;  // (threadIdx.x < NT)
+      int kg, ng;
+      block_of(b, &kg, &ng);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int w = c >> 1, h = c & 1;
+        u32x2 o;
+        o[0] = pick_half(v[q][0][w], v[q][1][w], h);
+        o[1] = pick_half(v[q][2][w], v[q][3][w], h);
+        *reinterpret_cast<u32x2*>(lds + lds_off(ng * 8 + c, kg)) = o;
+      }
+    }
+  }
+};
+
+// One K segment of an output tile.  A panel: direct (dX: Gp rows, k
+// contiguous) or transposed (dW: Gp columns); B panel: always transposed.
+// Both segments of a dual-K tile share the leading dimensions.
+struct TileSrc {
+  const char* a; const char* b;
+  int a_rows_valid;  // direct A: rows of the tile inside the expert's block
+  int a_n0, b_n0;    // transposed panels: first column of the tile
+  int K;             // k extent (direct: columns of A; transposed: valid rows)
+};
+
 __device__ __forceinline__ TileSrc pick_seg(const TileSrc& x, const TileSrc& y, bool first) {
   TileSrc r;
   r.a = first ? x.a : y.a;
-  r.lda = first ? x.lda : y.lda;
+  r.b = first ? x.b : y.b;
   r.a_rows_valid = first ? x.a_rows_valid : y.a_rows_valid;
   r.a_n0 = first ? x.a_n0 : y.a_n0;
-  r.a_ncols = first ? x.a_ncols : y.a_ncols;
-  r.b = first ? x.b : y.b;
-  r.ldb = first ? x.ldb : y.ldb;
   r.b_n0 = first ? x.b_n0 : y.b_n0;
-  r.b_ncols = first ? x.b_ncols : y.b_ncols;
   r.K = first ? x.K : y.K;
   return r;
 }
+
+template <class C, bool A_DIRECT>
+struct Stage {
+  using ATile = typename std::conditional<A_DIRECT, DirectTile<C::BM, C::NT>,
+                                          TransTile<C::BM, C::NT>>::type;
+  ATile A;
+  TransTile<C::BN, C::NT> B;
+  int64_t lda, ldb;
+  __device__ __forceinline__ void init(int64_t la, int64_t lb) {
+    lda = la;
+    ldb = lb;
+    A.init(la);
+    B.init(lb);
+  }
+  __device__ __forceinline__ void load(const TileSrc& s, int k0) {
+    if constexpr (A_DIRECT)
+      A.load(s.a, lda, s.a_rows_valid, k0, s.K);
+    else
+      A.load(s.a, lda, k0, s.K, s.a_n0);
+    B.load(s.b, ldb, k0, s.K, s.b_n0);
+  }
+  __device__ __forceinline__ void store(uint16_t* As, uint16_t* Bs) const {
+    A.store(As);
+    B.store(Bs);
+  }
+};
 
 // One output tile: the K segments s0 and (if nseg == 2) s1 are summed.
 // Two LDS stages: while the MFMAs consume stage kt & 1, the registers holding
 // k-tile kt+1 are stored into the other stage and the global loads of k-tile
 // kt+2 are issued; one barrier per k-tile.
-template <bool A_DIRECT>
-__device__ __forceinline__ void mma_tile(const TileSrc& s0, const TileSrc& s1, int nseg, float* C,
-                                         int64_t ldc, int rows_valid, int cols_valid,
-                                         uint16_t* As, uint16_t* Bs) {
+template <class C, bool A_DIRECT>
+__device__ __forceinline__ void mma_tile(const TileSrc& s0, const TileSrc& s1, int nseg,
+                                         int64_t lda, int64_t ldb, float* Cp, int64_t ldc,
+                                         int rows_valid, int cols_valid, uint16_t* As,
+                                         uint16_t* Bs) {
   const int l = lane_id(), w = threadIdx.x >> 6;
-  const int wm = w >> 1, wn = w & 1;
-  f32x4 acc[4][4];
+  const int wm = w / C::WGN, wn = w % C::WGN;
+  f32x4 acc[C::FM][C::FN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk0 = (s0.K + BK - 1) / BK;
   const int nk1 = nseg > 1 ? (s1.K + BK - 1) / BK : 0;
   const int total = nk0 + nk1;
   auto k_of = [&](int t) { return (t < nk0 ? t : t - nk0) * BK; };
 
-  Regs RA, RB;
+  Stage<C, A_DIRECT> st;
+  st.init(lda, ldb);
+  // Past the last k-tile the loads and stores below run on: their k offsets
+  // fall outside the buffer bounds (zeros) or inside the tile's own panel, and
+  // the stage they fill is never read, which keeps the loop body one basic
+  // block for the scheduler.
   if (total > 0) {
-    load_tile<A_DIRECT>(RA, RB, pick_seg(s0, s1, 0 < nk0), 0);
-    store_tile<A_DIRECT>(RA, RB, As, Bs);
-    if (total > 1) load_tile<A_DIRECT>(RA, RB, pick_seg(s0, s1, 1 < nk0), k_of(1));
+    st.load(pick_seg(s0, s1, 0 < nk0), 0);
+    st.store(As, Bs);
+    st.load(pick_seg(s0, s1, 1 < nk0), k_of(1));
     __syncthreads();
   }
+  auto frags = [&](const uint16_t* Ac, const uint16_t* Bc, int kk, bf16x8* af, bf16x8* bf) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+      const int row = wm * C::TM + i * 16 + (l & 15);
+      af[i] = *reinterpret_cast<const bf16x8*>(Ac + lds_off(row, 2 * (kk + (l >> 4))));
+    }
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const int col = wn * C::TN + j * 16 + (l & 15);
+      bf[j] = *reinterpret_cast<const bf16x8*>(Bc + lds_off(col, 2 * (kk + (l >> 4))));
+    }
+  };
+  auto mfmas = [&](const bf16x8* af, const bf16x8* bf) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+  };
   for (int kt = 0; kt < total; ++kt) {
-    const int cur = (kt & 1) * (BM * BK);
-    const uint16_t* Ac = As + cur;
-    const uint16_t* Bc = Bs + cur;
-#pragma unroll
-    for (int kk = 0; kk < BK / 8; kk += 4) {
-      bf16x8 af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wm * 64 + i * 16 + (l & 15);
-        af[i] = *reinterpret_cast<const bf16x8*>(Ac + lds_off(row, 2 * (kk + (l >> 4))));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = wn * 64 + j * 16 + (l & 15);
-        bf[j] = *reinterpret_cast<const bf16x8*>(Bc + lds_off(col, 2 * (kk + (l >> 4))));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < total) {
-      const int nxt = ((kt + 1) & 1) * (BM * BK);
-      store_tile<A_DIRECT>(RA, RB, As + nxt, Bs + nxt);
-      if (kt + 2 < total)
-        load_tile<A_DIRECT>(RA, RB, pick_seg(s0, s1, kt + 2 < nk0), k_of(kt + 2));
-    }
+    const int cur = kt & 1;
+    const uint16_t* Ac = As + cur * (C::BM * BK);
+    const uint16_t* Bc = Bs + cur * (C::BN * BK);
+    bf16x8 af[C::FM], bf[C::FN];
+    // first half of the k-tile; the registers of k-tile kt+1 go to the other
+    // stage meanwhile, then the second half overlaps the loads of kt+2
+    frags(Ac, Bc, 0, af, bf);
+    mfmas(af, bf);
+    st.store(As + (cur ^ 1) * (C::BM * BK), Bs + (cur ^ 1) * (C::BN * BK));
+    frags(Ac, Bc, 4, af, bf);
+    st.load(pick_seg(s0, s1, kt + 2 < nk0), k_of(kt + 2));
+    mfmas(af, bf);
     __syncthreads();
   }
   // lane holds C[row = .. + (l & 15)][col = .. + (l >> 4) * 4 + 0..3]
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = wm * 64 + i * 16 + (l & 15);
+  for (int i = 0; i < C::FM; ++i) {
+    const int row = wm * C::TM + i * 16 + (l & 15);
     if (row >= rows_valid) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = wn * 64 + j * 16 + (l >> 4) * 4;
-      if (col < cols_valid) *reinterpret_cast<f32x4*>(C + (int64_t)row * ldc + col) = acc[i][j];
+    for (int j = 0; j < C::FN; ++j) {
+      const int col = wn * C::TN + j * 16 + (l >> 4) * 4;
+      if (col < cols_valid) *reinterpret_cast<f32x4*>(Cp + (int64_t)row * ldc + col) = acc[i][j];
     }
   }
 }
@@ -237,9 +351,14 @@ struct GemmPlan {
   int ntm_w, ntn, nW, nX, G;
 };
 
-__global__ __launch_bounds__(NT) void k_grouped_gemm_bf16(GemmPlan P) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2 * BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2 * BN * BK];
+// CW tiles the dW products, CX the dX products (same block size and tile
+// width; CX may take fewer rows, for experts that keep few rows).
+template <class CW, class CX>
+__global__ __launch_bounds__(CW::NT) void k_grouped_gemm_bf16(GemmPlan P) {
+  static_assert(CW::NT == CX::NT && CW::BN == CX::BN, "one block size and tile width");
+  constexpr int BMX = CW::BM > CX::BM ? CW::BM : CX::BM;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2 * BMX * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2 * CW::BN * BK];
   const GemmArgs& a = P.a;
   const int L = xcd_remap(blockIdx.x, P.G);
   if (L >= P.nW + P.nX) return;
@@ -247,43 +366,45 @@ __global__ __launch_bounds__(NT) void k_grouped_gemm_bf16(GemmPlan P) {
   const bool dx = is_dx_tile(L, P.nW, P.nX, &idx);
   if (!dx) {
     const int per = P.ntm_w * P.ntn;
-    const int e = idx / per, rem = idx % per;
-    const int i0 = (rem / P.ntn) * BM, j0 = (rem % P.ntn) * BN;
+    const int e = idx / per;
+    int ti, tj;
+    raster(idx % per, P.ntm_w, P.ntn, &ti, &tj);
+    const int i0 = ti * CW::BM, j0 = tj * CW::BN;
     const int kb = a.offsets[e];
     const int Me = max(0, min(a.offsets[e + 1], a.max_rows) - kb);
     TileSrc s;
-    s.a = (const uint16_t*)a.Gp + (int64_t)kb * a.d_out; s.lda = a.d_out;
-    s.a_rows_valid = 0; s.a_n0 = i0; s.a_ncols = a.d_out;
-    s.b = (const uint16_t*)a.Xp + (int64_t)kb * a.d_in; s.ldb = a.d_in;
-    s.b_n0 = j0; s.b_ncols = a.d_in;
+    s.a = (const char*)a.Gp + (int64_t)kb * a.d_out * 2;
+    s.b = (const char*)a.Xp + (int64_t)kb * a.d_in * 2;
+    s.a_rows_valid = 0; s.a_n0 = i0; s.b_n0 = j0;
     s.K = Me;
-    float* C = a.dW + (int64_t)e * a.d_out * a.d_in + (int64_t)i0 * a.d_in + j0;
-    mma_tile<false>(s, s, 1, C, a.d_in, min(BM, a.d_out - i0), min(BN, a.d_in - j0), As, Bs);
+    float* Cp = a.dW + (int64_t)e * a.d_out * a.d_in + (int64_t)i0 * a.d_in + j0;
+    mma_tile<CW, false>(s, s, 1, a.d_out, a.d_in, Cp, a.d_in, min(CW::BM, a.d_out - i0),
+                        min(CW::BN, a.d_in - j0), As, Bs);
     return;
   }
-  const int mt = idx / P.ntn, tn = idx % P.ntn;
+  int mt, tn;
+  raster(idx, P.nX / P.ntn, P.ntn, &mt, &tn);
   if (mt >= a.mt_off[a.E]) return;
   const int e = find_expert(a.mt_off, a.E, mt);
-  const int m0 = a.offsets[e] + (mt - a.mt_off[e]) * BM;
-  const int rows = min(BM, min(a.offsets[e + 1], a.max_rows) - m0);
+  const int m0 = a.offsets[e] + (mt - a.mt_off[e]) * CX::BM;
+  const int rows = min(CX::BM, min(a.offsets[e + 1], a.max_rows) - m0);
   if (rows <= 0) return;
-  const int j0 = tn * BN;
+  const int j0 = tn * CX::BN;
   TileSrc s0, s1;
-  s0.a = (const uint16_t*)a.Gp + (int64_t)m0 * a.d_out; s0.lda = a.d_out;
-  s0.a_rows_valid = rows; s0.a_n0 = 0; s0.a_ncols = 0;
-  s0.b = (const uint16_t*)a.W + (int64_t)e * a.w_stride; s0.ldb = a.d_in;
-  s0.b_n0 = j0; s0.b_ncols = a.d_in;
+  s0.a = (const char*)a.Gp + (int64_t)m0 * a.d_out * 2;
+  s0.b = (const char*)a.W + (int64_t)e * a.w_stride * 2;
+  s0.a_rows_valid = rows; s0.a_n0 = 0; s0.b_n0 = j0;
   s0.K = a.d_out;
   s1 = s0;
   int nseg = 1;
-  if (a.Gp2) {
-    s1.a = (const uint16_t*)a.Gp2 + (int64_t)m0 * a.d_out2; s1.lda = a.d_out2;
-    s1.b = (const uint16_t*)a.W2 + (int64_t)e * a.w2_stride;
-    s1.K = a.d_out2;
+  if (a.Gp2) {  // second segment of the same shape (host-checked: d_out2 == d_out)
+    s1.a = (const char*)a.Gp2 + (int64_t)m0 * a.d_out * 2;
+    s1.b = (const char*)a.W2 + (int64_t)e * a.w2_stride * 2;
     nseg = 2;
   }
-  float* C = a.dXp + (int64_t)m0 * a.d_in + j0;
-  mma_tile<true>(s0, s1, nseg, C, a.d_in, rows, min(BN, a.d_in - j0), As, Bs);
+  float* Cp = a.dXp + (int64_t)m0 * a.d_in + j0;
+  mma_tile<CX, true>(s0, s1, nseg, a.d_out, a.d_in, Cp, a.d_in, rows,
+                     min(CX::BN, a.d_in - j0), As, Bs);
 }
 
 // ------------------------------------------------------------------ fp32
@@ -396,31 +517,70 @@ __global__ __launch_bounds__(NT) void k_grouped_gemm_f32(GemmPlan P) {
 
 // ------------------------------------------------------------- launcher
 
-int gemm_row_tile(int bf16) { return bf16 ? BM : FBM; }
+// Tile configurations of the bf16 kernel.
+using CfgS = TileCfg<128, 128, 2, 2>;   // 4 waves of 64x64
+using CfgM = TileCfg<256, 128, 4, 2>;   // 8 waves of 64x64
+using CfgL = TileCfg<256, 256, 2, 4>;   // 8 waves of 128x64
+using CfgXS = TileCfg<64, 256, 1, 8>;   // 8 waves of 64x32 (dX of small experts)
+
+// Plan the combined tile list (dW tiles tmw x tn, dX tiles tmx x tn) and build
+// the dX row-tile prefix on the device.
+static hipError_t plan_tiles(const GemmArgs& a, int tmw, int tmx, int tn, GemmPlan* P,
+                             hipStream_t s) {
+  P->a = a;
+  P->ntn = (a.d_in + tn - 1) / tn;
+  P->ntm_w = (a.d_out + tmw - 1) / tmw;
+  P->nW = a.dW ? a.E * P->ntm_w * P->ntn : 0;
+  P->nX = (a.dXp && a.max_rows > 0) ? ((a.max_rows + tmx - 1) / tmx + a.E) * P->ntn : 0;
+  if (P->nX > 0) {
+    hipError_t err = launch_tile_plan(a.E, tmx, a.offsets, a.mt_off, s);
+    if (err != hipSuccess) return err;
+  }
+  const int64_t total = (int64_t)P->nW + P->nX;
+  if (total > (1ll << 30)) return hipErrorInvalidValue;
+  P->G = (int)((total + 7) & ~7ll);
+  return hipSuccess;
+}
+
+template <class CW, class CX>
+static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
+  GemmPlan P{};
+  hipError_t err = plan_tiles(a, CW::BM, CX::BM, CW::BN, &P, s);
+  if (err != hipSuccess || P.G == 0) return err;
+  LRM_LAUNCH(P.G, CW::NT, 0, s, k_grouped_gemm_bf16<CW, CX>)(P);
+  return hipGetLastError();
+}
+
+// Tile choice: 256x256 dW tiles; 256-row dX tiles when experts keep many rows
+// on average (MFMA-bound), 64-row dX tiles otherwise (a 256-row tile over an
+// expert of a few dozen rows would spend most of its MFMAs on zero rows).
+// LRM_GEMM_TILE=S|M|L|X overrides (benchmarking).
+int gemm_tile_choice(const GemmArgs& a) {
+  const char* env = getenv("LRM_GEMM_TILE");
+  if (env && env[0] == 'S') return 0;
+  if (env && env[0] == 'M') return 1;
+  if (env && env[0] == 'L') return 2;
+  if (env && env[0] == 'X') return 3;
+  const int64_t per_expert = a.E > 0 ? (int64_t)a.max_rows / a.E : 0;
+  return per_expert >= 192 ? 2 : 3;
+}
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s) {
   if (!a.offsets || (a.dXp && (!a.W || !a.mt_off || !a.Gp)) || (a.dW && !a.Gp) ||
-      (a.dW && a.max_rows > 0 && !a.Xp) || (a.Gp2 && !a.W2))
+      (a.dW && a.max_rows > 0 && !a.Xp) || (a.Gp2 && (!a.W2 || a.d_out2 != a.d_out)))
     return hipErrorInvalidValue;
-  const int tm = a.bf16 ? BM : FBM, tn = a.bf16 ? BN : FBN;
-  GemmPlan P{};
-  P.a = a;
-  P.ntn = (a.d_in + tn - 1) / tn;
-  P.ntm_w = (a.d_out + tm - 1) / tm;
-  P.nW = a.dW ? a.E * P.ntm_w * P.ntn : 0;
-  P.nX = (a.dXp && a.max_rows > 0) ? ((a.max_rows + tm - 1) / tm + a.E) * P.ntn : 0;
-  if (P.nX > 0) {
-    hipError_t err = launch_tile_plan(a.E, tm, a.offsets, a.mt_off, s);
-    if (err != hipSuccess) return err;
+  if (a.bf16) {
+    switch (gemm_tile_choice(a)) {
+      case 3: return launch_bf16<CfgL, CfgXS>(a, s);
+      case 2: return launch_bf16<CfgL, CfgL>(a, s);
+      case 1: return launch_bf16<CfgM, CfgM>(a, s);
+      default: return launch_bf16<CfgS, CfgS>(a, s);
+    }
   }
-  const int64_t total = (int64_t)P.nW + P.nX;
-  if (total == 0) return hipSuccess;
-  if (total > (1ll << 30)) return hipErrorInvalidValue;
-  P.G = (int)((total + 7) & ~7ll);
-  if (a.bf16)
-    LRM_LAUNCH(P.G, NT, 0, s, k_grouped_gemm_bf16)(P);
-  else
-    LRM_LAUNCH(P.G, NT, 0, s, k_grouped_gemm_f32)(P);
+  GemmPlan P{};
+  hipError_t err = plan_tiles(a, FBM, FBM, FBN, &P, s);
+  if (err != hipSuccess || P.G == 0) return err;
+  LRM_LAUNCH(P.G, NT, 0, s, k_grouped_gemm_f32)(P);
   return hipGetLastError();
 }
 

@@ -94,7 +94,7 @@ struct GemmArgs {
   float* dXp;  // [max_rows][d_in] or nullptr
   int32_t* mt_off;  // workspace [E+1]
 };
-int gemm_row_tile(int bf16);
+int gemm_tile_choice(const GemmArgs& a);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------ unpermute

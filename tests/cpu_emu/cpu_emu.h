@@ -188,7 +188,40 @@ Launch<KArgs...> launch(dim3 g, dim3 b, size_t sh, hipStream_t, void (*k)(KArgs.
   return Launch<KArgs...>{g, b, sh, k};
 }
 
+// Raw buffer resource: base and byte bound.  A load whose 16 bytes are not
+// all below the bound returns zero, as the hardware range check does for the
+// 16-byte-aligned offsets and bounds the kernels use; reads inside the bound
+// touch real memory, so a bound past the allocation shows up under ASan.
+struct BufRsrc {
+  const char* base;
+  int n;
+};
+inline BufRsrc make_rsrc(const void* p, int n) { return BufRsrc{(const char*)p, n}; }
+typedef unsigned int u32x4_emu __attribute__((ext_vector_type(4)));
+inline u32x4_emu buffer_load16(BufRsrc r, int voff, int soff) {
+  const long long off = (long long)voff + soff;
+  u32x4_emu v = {0u, 0u, 0u, 0u};
+  if (off >= 0 && off + 16 <= r.n) std::memcpy(&v, r.base + off, 16);
+  return v;
+}
+// v_perm_b32: result byte i = byte sel_i of the 8-byte value {s0 (bytes 4..7), s1 (bytes 0..3)}
+inline unsigned perm(unsigned s0, unsigned s1, unsigned sel) {
+  const unsigned long long v = ((unsigned long long)s0 << 32) | s1;
+  unsigned r = 0;
+  for (int i = 0; i < 4; ++i) {
+    const unsigned b = (sel >> (8 * i)) & 0xff;
+    if (b > 7) std::abort();  // constant selectors are not modelled
+    r |= (unsigned)((v >> (8 * b)) & 0xff) << (8 * i);
+  }
+  return r;
+}
+
 }  // namespace emu
+
+typedef ::emu::BufRsrc __amdgpu_buffer_rsrc_t;
+#define __builtin_amdgcn_make_buffer_rsrc(p, stride, n, flags) ::emu::make_rsrc((p), (n))
+#define __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, aux) ::emu::buffer_load16((r), (voff), (soff))
+#define __builtin_amdgcn_perm(s0, s1, sel) ::emu::perm((s0), (s1), (sel))
 
 #define threadIdx (::emu::ctx.tid)
 #define blockIdx (::emu::ctx.bid)

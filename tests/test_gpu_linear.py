@@ -255,6 +255,35 @@ def test_gemm_zero_rows_and_heavy_expert(L):
                                G64[a:b] @ O.f64(W[e].cpu())) < 1e-3
 
 
+@pytest.mark.parametrize("tile", ["S", "M", "L", "X"])
+def test_gemm_tile_configs(L, tile, monkeypatch):
+    """Every bf16 tile configuration on ragged shapes: empty, 1-row and
+    tile-edge experts, a column count and a k extent that leave partial tiles."""
+    monkeypatch.setenv("LRM_GEMM_TILE", tile)
+    say("gemm tile", tile)
+    E, d_in, d_out = 8, 320, 200
+    sizes = [0, 1, 63, 64, 65, 257, 700, 0]
+    W = synth.normal((E, d_out, d_in), 0.02, torch.bfloat16, DEV, "tc", 1)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M = int(offsets[-1])
+    Gp = synth.normal((M, d_out), 1.0, torch.bfloat16, DEV, "tc", 2)
+    Xp = synth.normal((M, d_in), 1.0, torch.bfloat16, DEV, "tc", 3)
+    dW = torch.full((E, d_out, d_in), float("nan"), device=DEV)
+    dXp = torch.full((M, d_in), float("nan"), device=DEV)
+    L.lrm_grouped_bwd(E, torch.as_tensor(offsets, device=DEV), M, Gp, Xp, W, d_in, d_out, dW,
+                      dXp)
+    torch.cuda.synchronize()
+    G64, X64 = Gp.double().cpu().numpy(), Xp.double().cpu().numpy()
+    for e in range(E):
+        a, b = offsets[e], offsets[e + 1]
+        got = dW[e].cpu().numpy()
+        if a == b:
+            assert not got.any()
+            continue
+        assert rel_fro(got, G64[a:b].T @ X64[a:b]) < 1e-5
+        assert rel_fro(dXp[a:b].cpu().numpy(), G64[a:b] @ O.f64(W[e].cpu())) < 1e-5
+
+
 # ------------------------------------------------------------ fused call
 
 @pytest.mark.parametrize("x_rows,g_rows", [("token", "pair"), ("pair", "token")])
