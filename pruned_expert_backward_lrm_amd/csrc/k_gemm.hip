@@ -23,6 +23,8 @@
 // fp32: plain LDS-tiled fp32 FMA (64x64 tile) for fp32 inputs.
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include <type_traits>
 
 #include "common.h"
@@ -80,12 +82,17 @@ __device__ __forceinline__ void raster(int t, int nr, int nc, int* r, int* c) {
 
 // A block tile configuration: BM x BN outputs, k-tiles of 64, WGM x WGN waves,
 // each wave owning a TM x TN sub-tile of FM x FN 16x16 MFMA blocks.
-template <int BM_, int BN_, int WGM_, int WGN_>
+template <int BM_, int BN_, int WGM_, int WGN_, int MINB_ = 1, int STAGES_ = 2>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, BK = 64;
+  static constexpr int MINB = MINB_;      // resident blocks per CU the registers must allow
+  static constexpr int STAGES = STAGES_;  // LDS stages (1: two barriers per k-tile)
   static constexpr int WGM = WGM_, WGN = WGN_, NW = WGM_ * WGN_, NT = 64 * NW;
+  static constexpr int WPE = (MINB * NW + 3) / 4;  // waves per SIMD (launch bound)
   static constexpr int TM = BM / WGM, TN = BN / WGN;
   static constexpr int FM = TM / 16, FN = TN / 16;
+  // A fragments held at once (fewer when two blocks share a CU's registers)
+  static constexpr int FCH = (MINB > 1 && FM > 4) ? 4 : FM;
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile");
 };
 
@@ -265,146 +272,206 @@ struct Stage {
   }
 };
 
-// One output tile: the K segments s0 and (if nseg == 2) s1 are summed.
-// Two LDS stages: while the MFMAs consume stage kt & 1, the registers holding
-// k-tile kt+1 are stored into the other stage and the global loads of k-tile
-// kt+2 are issued; one barrier per k-tile.
-template <class C, bool A_DIRECT>
-__device__ __forceinline__ void mma_tile(const TileSrc& s0, const TileSrc& s1, int nseg,
-                                         int64_t lda, int64_t ldb, float* Cp, int64_t ldc,
-                                         int rows_valid, int cols_valid, uint16_t* As,
-                                         uint16_t* Bs) {
+struct GemmPlan {
+  GemmArgs a;
+  int ntm_w, ntn, nW, nX, G;  // ntn: column tiles of the dW products (and of fp32 dX)
+  int ntn_x;                   // column tiles of the bf16 dX products
+};
+
+// One output tile of the stream: its K segments, k-tile counts and output.
+struct Job {
+  TileSrc s0, s1;
+  int nk0, nk;   // k-tiles of segment 0, of both segments
+  float* C;
+  int rows, cols;  // valid output rows and columns (rows <= 0: no output)
+};
+
+template <class C, bool DX>
+__device__ __forceinline__ Job make_job(const GemmPlan& P, int t) {
+  const GemmArgs& a = P.a;
+  Job j;
+  if constexpr (!DX) {
+    const int per = P.ntm_w * P.ntn;
+    const int e = t / per;
+    int ti, tj;
+    raster(t - e * per, P.ntm_w, P.ntn, &ti, &tj);
+    const int i0 = ti * C::BM, j0 = tj * C::BN;
+    const int kb = a.offsets[e];
+    const int Me = max(0, min(a.offsets[e + 1], a.max_rows) - kb);
+    j.s0.a = (const char*)a.Gp + (int64_t)kb * a.d_out * 2;
+    j.s0.b = (const char*)a.Xp + (int64_t)kb * a.d_in * 2;
+    j.s0.a_rows_valid = 0; j.s0.a_n0 = i0; j.s0.b_n0 = j0;
+    j.s0.K = Me;
+    j.s1 = j.s0;
+    j.nk0 = j.nk = (Me + BK - 1) / BK;
+    j.C = a.dW + (int64_t)e * a.d_out * a.d_in + (int64_t)i0 * a.d_in + j0;
+    j.rows = min(C::BM, a.d_out - i0);
+    j.cols = min(C::BN, a.d_in - j0);
+  } else {
+    int mt, tn;
+    raster(t, a.mt_off[a.E], P.ntn_x, &mt, &tn);
+    const int e = find_expert(a.mt_off, a.E, mt);
+    const int m0 = a.offsets[e] + (mt - a.mt_off[e]) * C::BM;
+    const int rows = min(C::BM, min(a.offsets[e + 1], a.max_rows) - m0);
+    const int j0 = tn * C::BN;
+    j.s0.a = (const char*)a.Gp + (int64_t)m0 * a.d_out * 2;
+    j.s0.b = (const char*)a.W + (int64_t)e * a.w_stride * 2;
+    j.s0.a_rows_valid = rows; j.s0.a_n0 = 0; j.s0.b_n0 = j0;
+    j.s0.K = a.d_out;
+    j.s1 = j.s0;
+    j.nk0 = j.nk = (a.d_out + BK - 1) / BK;
+    if (a.Gp2) {  // second segment of the same shape (host-checked: d_out2 == d_out)
+      j.s1.a = (const char*)a.Gp2 + (int64_t)m0 * a.d_out * 2;
+      j.s1.b = (const char*)a.W2 + (int64_t)e * a.w2_stride * 2;
+      j.nk = 2 * j.nk0;
+    }
+    if (rows <= 0) j.nk = 0;
+    j.C = a.dXp + (int64_t)m0 * a.d_in + j0;
+    j.rows = rows;
+    j.cols = min(C::BN, a.d_in - j0);
+  }
+  return j;
+}
+
+// Writes a tile's accumulators (or zeros) within its valid rows and columns.
+// Lane l holds C[row = .. + (l & 15)][col = .. + (l >> 4) * 4 + 0..3].
+template <class C>
+__device__ __forceinline__ void write_tile(const f32x4 (&acc)[C::FM][C::FN], bool zero,
+                                           float* out, int64_t ldc, int rows, int cols) {
   const int l = lane_id(), w = threadIdx.x >> 6;
   const int wm = w / C::WGN, wn = w % C::WGN;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+    const int row = wm * C::TM + i * 16 + (l & 15);
+    if (row >= rows) continue;
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const int col = wn * C::TN + j * 16 + (l >> 4) * 4;
+      if (col < cols)
+        *reinterpret_cast<f32x4*>(out + (int64_t)row * ldc + col) =
+            zero ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[i][j];
+    }
+  }
+}
+
+// MFMAs of k-granules kk..kk+3 (lane group l >> 4 takes granule kk + (l >> 4))
+// on the LDS stage (Ac, Bc): B fragments once, A fragments FCH at a time.
+template <class C>
+__device__ __forceinline__ void mma_k32(f32x4 (&acc)[C::FM][C::FN], const uint16_t* Ac,
+                                        const uint16_t* Bc, int kk) {
+  const int l = lane_id(), w = threadIdx.x >> 6;
+  const int wm = w / C::WGN, wn = w % C::WGN;
+  bf16x8 bf[C::FN];
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) {
+    const int col = wn * C::TN + j * 16 + (l & 15);
+    bf[j] = *reinterpret_cast<const bf16x8*>(Bc + lds_off(col, 2 * (kk + (l >> 4))));
+  }
+#pragma unroll
+  for (int i0 = 0; i0 < C::FM; i0 += C::FCH) {
+    bf16x8 af[C::FCH];
+#pragma unroll
+    for (int i = 0; i < C::FCH; ++i) {
+      const int row = wm * C::TM + (i0 + i) * 16 + (l & 15);
+      af[i] = *reinterpret_cast<const bf16x8*>(Ac + lds_off(row, 2 * (kk + (l >> 4))));
+    }
+#pragma unroll
+    for (int i = 0; i < C::FCH; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+        acc[i0 + i][j] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i0 + i][j], 0, 0, 0);
+  }
+}
+
+// Persistent tile stream.  Each XCD takes a contiguous eighth of the tile list
+// (consecutive tiles share operand panels in its L2) and its blocks take the
+// tiles of that range in turn.  A block runs the k-tiles of all its tiles as
+// one stream: two LDS stages, the registers of the next k-tile stored into the
+// idle stage while the MFMAs consume the current one, global loads two k-tiles
+// ahead, one barrier per k-tile.  The loads of a tile's first k-tiles are thus
+// in flight while the previous tile's outputs are written.  A tile with no
+// k-tiles (an expert that kept no rows) writes zeros.
+template <class C, bool DX>
+__global__ __launch_bounds__(C::NT, C::WPE) void k_gemm_stream(GemmPlan P) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[C::STAGES * C::BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[C::STAGES * C::BN * BK];
+  const GemmArgs& a = P.a;
+  const int n = DX ? a.mt_off[a.E] * P.ntn_x : P.nW;
+  const int x = blockIdx.x & 7, nbx = gridDim.x >> 3;
+  const int hi = (int)((int64_t)n * (x + 1) / 8);
+  int tc = (int)((int64_t)n * x / 8) + (blockIdx.x >> 3);
+
   f32x4 acc[C::FM][C::FN];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk0 = (s0.K + BK - 1) / BK;
-  const int nk1 = nseg > 1 ? (s1.K + BK - 1) / BK : 0;
-  const int total = nk0 + nk1;
-  auto k_of = [&](int t) { return (t < nk0 ? t : t - nk0) * BK; };
-
-  Stage<C, A_DIRECT> st;
-  st.init(lda, ldb);
-  // Past the last k-tile the loads and stores below run on: their k offsets
-  // fall outside the buffer bounds (zeros) or inside the tile's own panel, and
-  // the stage they fill is never read, which keeps the loop body one basic
-  // block for the scheduler.
-  if (total > 0) {
-    st.load(pick_seg(s0, s1, 0 < nk0), 0);
-    st.store(As, Bs);
-    st.load(pick_seg(s0, s1, 1 < nk0), k_of(1));
-    __syncthreads();
+  // compute cursor: tile tc (job jc), k-tile kc; zero tiles are written as met
+  Job jc;
+  for (; tc < hi; tc += nbx) {
+    jc = make_job<C, DX>(P, tc);
+    if (jc.nk > 0) break;
+    if (jc.rows > 0) write_tile<C>(acc, true, jc.C, a.d_in, jc.rows, jc.cols);
   }
-  auto frags = [&](const uint16_t* Ac, const uint16_t* Bc, int kk, bf16x8* af, bf16x8* bf) {
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-      const int row = wm * C::TM + i * 16 + (l & 15);
-      af[i] = *reinterpret_cast<const bf16x8*>(Ac + lds_off(row, 2 * (kk + (l >> 4))));
-    }
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      const int col = wn * C::TN + j * 16 + (l & 15);
-      bf[j] = *reinterpret_cast<const bf16x8*>(Bc + lds_off(col, 2 * (kk + (l >> 4))));
-    }
-  };
-  auto mfmas = [&](const bf16x8* af, const bf16x8* bf) {
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
-  };
-  for (int kt = 0; kt < total; ++kt) {
-    const int cur = kt & 1;
+  if (tc >= hi) return;
+
+  Stage<C, DX> st;
+  st.init(a.d_out, a.d_in);
+  // load cursor: tile tl (job jl), k-tile kl, two k-tiles ahead of the compute
+  int tl = tc, kl = 0;
+  Job jl = jc;
+#define LRM_ISSUE_LOAD()                                                        \
+  if (tl < hi) {                                                                \
+    const bool first = kl < jl.nk0;                                             \
+    st.load(pick_seg(jl.s0, jl.s1, first), (first ? kl : kl - jl.nk0) * BK);   \
+    if (++kl == jl.nk) {                                                        \
+      kl = 0;                                                                   \
+      for (tl += nbx; tl < hi; tl += nbx) {                                     \
+        jl = make_job<C, DX>(P, tl);                                            \
+        if (jl.nk > 0) break;                                                   \
+      }                                                                         \
+    }                                                                           \
+  }
+  LRM_ISSUE_LOAD();
+  st.store(As, Bs);
+  LRM_ISSUE_LOAD();
+  __syncthreads();
+  int kc = 0;
+  for (int it = 0;; ++it) {
+    const int cur = C::STAGES == 2 ? (it & 1) : 0;
     const uint16_t* Ac = As + cur * (C::BM * BK);
     const uint16_t* Bc = Bs + cur * (C::BN * BK);
-    bf16x8 af[C::FM], bf[C::FN];
-    // first half of the k-tile; the registers of k-tile kt+1 go to the other
-    // stage meanwhile, then the second half overlaps the loads of kt+2
-    frags(Ac, Bc, 0, af, bf);
-    mfmas(af, bf);
-    st.store(As + (cur ^ 1) * (C::BM * BK), Bs + (cur ^ 1) * (C::BN * BK));
-    frags(Ac, Bc, 4, af, bf);
-    st.load(pick_seg(s0, s1, kt + 2 < nk0), k_of(kt + 2));
-    mfmas(af, bf);
+    mma_k32<C>(acc, Ac, Bc, 0);
+    if constexpr (C::STAGES == 2) {
+      // the next k-tile of the stream into the idle stage (stale registers
+      // past the stream's end: the stage they fill is then never read)
+      st.store(As + (cur ^ 1) * (C::BM * BK), Bs + (cur ^ 1) * (C::BN * BK));
+    }
+    mma_k32<C>(acc, Ac, Bc, 4);
+    if constexpr (C::STAGES == 1) {
+      __syncthreads();  // every wave is done with the stage
+      st.store(As, Bs);
+    }
+    LRM_ISSUE_LOAD();
+    if (++kc == jc.nk) {
+      write_tile<C>(acc, false, jc.C, a.d_in, jc.rows, jc.cols);
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      kc = 0;
+      for (tc += nbx; tc < hi; tc += nbx) {
+        jc = make_job<C, DX>(P, tc);
+        if (jc.nk > 0) break;
+        if (jc.rows > 0) write_tile<C>(acc, true, jc.C, a.d_in, jc.rows, jc.cols);
+      }
+      if (tc >= hi) break;
+    }
     __syncthreads();
   }
-  // lane holds C[row = .. + (l & 15)][col = .. + (l >> 4) * 4 + 0..3]
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
-    const int row = wm * C::TM + i * 16 + (l & 15);
-    if (row >= rows_valid) continue;
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      const int col = wn * C::TN + j * 16 + (l >> 4) * 4;
-      if (col < cols_valid) *reinterpret_cast<f32x4*>(Cp + (int64_t)row * ldc + col) = acc[i][j];
-    }
-  }
-}
-
-struct GemmPlan {
-  GemmArgs a;
-  int ntm_w, ntn, nW, nX, G;
-};
-
-// CW tiles the dW products, CX the dX products (same block size and tile
-// width; CX may take fewer rows, for experts that keep few rows).
-template <class CW, class CX>
-__global__ __launch_bounds__(CW::NT) void k_grouped_gemm_bf16(GemmPlan P) {
-  static_assert(CW::NT == CX::NT && CW::BN == CX::BN, "one block size and tile width");
-  constexpr int BMX = CW::BM > CX::BM ? CW::BM : CX::BM;
-  __shared__ __attribute__((aligned(16))) uint16_t As[2 * BMX * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2 * CW::BN * BK];
-  const GemmArgs& a = P.a;
-  const int L = xcd_remap(blockIdx.x, P.G);
-  if (L >= P.nW + P.nX) return;
-  int idx;
-  const bool dx = is_dx_tile(L, P.nW, P.nX, &idx);
-  if (!dx) {
-    const int per = P.ntm_w * P.ntn;
-    const int e = idx / per;
-    int ti, tj;
-    raster(idx % per, P.ntm_w, P.ntn, &ti, &tj);
-    const int i0 = ti * CW::BM, j0 = tj * CW::BN;
-    const int kb = a.offsets[e];
-    const int Me = max(0, min(a.offsets[e + 1], a.max_rows) - kb);
-    TileSrc s;
-    s.a = (const char*)a.Gp + (int64_t)kb * a.d_out * 2;
-    s.b = (const char*)a.Xp + (int64_t)kb * a.d_in * 2;
-    s.a_rows_valid = 0; s.a_n0 = i0; s.b_n0 = j0;
-    s.K = Me;
-    float* Cp = a.dW + (int64_t)e * a.d_out * a.d_in + (int64_t)i0 * a.d_in + j0;
-    mma_tile<CW, false>(s, s, 1, a.d_out, a.d_in, Cp, a.d_in, min(CW::BM, a.d_out - i0),
-                        min(CW::BN, a.d_in - j0), As, Bs);
-    return;
-  }
-  int mt, tn;
-  raster(idx, P.nX / P.ntn, P.ntn, &mt, &tn);
-  if (mt >= a.mt_off[a.E]) return;
-  const int e = find_expert(a.mt_off, a.E, mt);
-  const int m0 = a.offsets[e] + (mt - a.mt_off[e]) * CX::BM;
-  const int rows = min(CX::BM, min(a.offsets[e + 1], a.max_rows) - m0);
-  if (rows <= 0) return;
-  const int j0 = tn * CX::BN;
-  TileSrc s0, s1;
-  s0.a = (const char*)a.Gp + (int64_t)m0 * a.d_out * 2;
-  s0.b = (const char*)a.W + (int64_t)e * a.w_stride * 2;
-  s0.a_rows_valid = rows; s0.a_n0 = 0; s0.b_n0 = j0;
-  s0.K = a.d_out;
-  s1 = s0;
-  int nseg = 1;
-  if (a.Gp2) {  // second segment of the same shape (host-checked: d_out2 == d_out)
-    s1.a = (const char*)a.Gp2 + (int64_t)m0 * a.d_out * 2;
-    s1.b = (const char*)a.W2 + (int64_t)e * a.w2_stride * 2;
-    nseg = 2;
-  }
-  float* Cp = a.dXp + (int64_t)m0 * a.d_in + j0;
-  mma_tile<CX, true>(s0, s1, nseg, a.d_out, a.d_in, Cp, a.d_in, rows,
-                     min(CX::BN, a.d_in - j0), As, Bs);
+#undef LRM_ISSUE_LOAD
 }
 
 // ------------------------------------------------------------------ fp32
@@ -518,20 +585,21 @@ __global__ __launch_bounds__(NT) void k_grouped_gemm_f32(GemmPlan P) {
 // ------------------------------------------------------------- launcher
 
 // Tile configurations of the bf16 kernel.
-using CfgS = TileCfg<128, 128, 2, 2>;   // 4 waves of 64x64
+using CfgS = TileCfg<128, 128, 2, 2, 2>;  // 4 waves of 64x64
 using CfgM = TileCfg<256, 128, 4, 2>;   // 8 waves of 64x64
 using CfgL = TileCfg<256, 256, 2, 4>;   // 8 waves of 128x64
-using CfgXS = TileCfg<64, 256, 1, 8>;   // 8 waves of 64x32 (dX of small experts)
+using CfgXS = TileCfg<64, 256, 1, 8, 2>;  // 8 waves of 64x32 (dX of small experts)
 
 // Plan the combined tile list (dW tiles tmw x tn, dX tiles tmx x tn) and build
 // the dX row-tile prefix on the device.
-static hipError_t plan_tiles(const GemmArgs& a, int tmw, int tmx, int tn, GemmPlan* P,
+static hipError_t plan_tiles(const GemmArgs& a, int tmw, int tnw, int tmx, int tnx, GemmPlan* P,
                              hipStream_t s) {
   P->a = a;
-  P->ntn = (a.d_in + tn - 1) / tn;
+  P->ntn = (a.d_in + tnw - 1) / tnw;
+  P->ntn_x = (a.d_in + tnx - 1) / tnx;
   P->ntm_w = (a.d_out + tmw - 1) / tmw;
   P->nW = a.dW ? a.E * P->ntm_w * P->ntn : 0;
-  P->nX = (a.dXp && a.max_rows > 0) ? ((a.max_rows + tmx - 1) / tmx + a.E) * P->ntn : 0;
+  P->nX = (a.dXp && a.max_rows > 0) ? ((a.max_rows + tmx - 1) / tmx + a.E) * P->ntn_x : 0;
   if (P->nX > 0) {
     hipError_t err = launch_tile_plan(a.E, tmx, a.offsets, a.mt_off, s);
     if (err != hipSuccess) return err;
@@ -542,13 +610,44 @@ static hipError_t plan_tiles(const GemmArgs& a, int tmw, int tmx, int tn, GemmPl
   return hipSuccess;
 }
 
+// Resident blocks of one stream kernel on the current device (cached).
+template <class C, bool DX>
+static int stream_grid_cap() {
+  static int cap[16];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
+  if (cap[dev] == 0) {
+    int cus = 0, occ = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemm_stream<C, DX>, C::NT, 0) !=
+            hipSuccess ||
+        occ <= 0)
+      occ = 1;
+    cap[dev] = cus * occ;
+  }
+  return cap[dev];
+}
+
+template <class C, bool DX>
+static hipError_t launch_stream(const GemmPlan& P, int ntiles_max, hipStream_t s) {
+  if (ntiles_max <= 0) return hipSuccess;
+  // a multiple of 8 blocks (one share per XCD), at most one resident round
+  const int64_t want = ((int64_t)ntiles_max + 7) & ~7ll;
+  const int G = (int)std::min<int64_t>(want, std::max(8, stream_grid_cap<C, DX>() & ~7));
+  LRM_LAUNCH(G, C::NT, 0, s, k_gemm_stream<C, DX>)(P);
+  return hipGetLastError();
+}
+
 template <class CW, class CX>
 static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
   GemmPlan P{};
-  hipError_t err = plan_tiles(a, CW::BM, CX::BM, CW::BN, &P, s);
-  if (err != hipSuccess || P.G == 0) return err;
-  LRM_LAUNCH(P.G, CW::NT, 0, s, k_grouped_gemm_bf16<CW, CX>)(P);
-  return hipGetLastError();
+  hipError_t err = plan_tiles(a, CW::BM, CW::BN, CX::BM, CX::BN, &P, s);
+  if (err != hipSuccess) return err;
+  err = launch_stream<CW, false>(P, P.nW, s);
+  if (err != hipSuccess) return err;
+  return launch_stream<CX, true>(P, P.nX, s);
 }
 
 // Tile choice: 256x256 dW tiles; 256-row dX tiles when experts keep many rows
@@ -578,7 +677,7 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s) {
     }
   }
   GemmPlan P{};
-  hipError_t err = plan_tiles(a, FBM, FBM, FBN, &P, s);
+  hipError_t err = plan_tiles(a, FBM, FBN, FBM, FBN, &P, s);
   if (err != hipSuccess || P.G == 0) return err;
   LRM_LAUNCH(P.G, NT, 0, s, k_grouped_gemm_f32)(P);
   return hipGetLastError();

@@ -54,6 +54,14 @@ inline hipError_t hipMemcpy(void* d, const void* s, size_t n, hipMemcpyKind) {
 }
 inline hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
 inline hipError_t hipGetLastError() { return hipSuccess; }
+inline hipError_t hipGetDevice(int* d) { *d = 0; return hipSuccess; }
+enum hipDeviceAttribute_t { hipDeviceAttributeMultiprocessorCount };
+inline hipError_t hipDeviceGetAttribute(int* v, hipDeviceAttribute_t, int) { *v = 2; return hipSuccess; }
+template <class K>
+inline hipError_t hipOccupancyMaxActiveBlocksPerMultiprocessor(int* n, K, int, size_t) {
+  *n = 1;
+  return hipSuccess;
+}
 typedef void* hipEvent_t;
 inline hipError_t hipEventRecord(hipEvent_t, hipStream_t) { return hipSuccess; }
 
