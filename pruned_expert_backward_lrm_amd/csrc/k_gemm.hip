@@ -384,6 +384,30 @@ __device__ __forceinline__ void mma_k32(f32x4 (&acc)[C::FM][C::FN], const uint16
   }
 }
 
+// First dW tile of share x (of 8) when the tiles, in order, are cut into
+// shares of equal cost; a tile of expert e costs ceil(M_e / 64) + 1 (its
+// k-tiles and its output).  Block-uniform; reads offsets[0..E].
+template <class C>
+__device__ __forceinline__ int dw_tile_at_cost(const GemmPlan& P, int x) {
+  const GemmArgs& a = P.a;
+  const int per = P.ntm_w * P.ntn;
+  if (x >= 8) return P.nW;
+  int64_t total = 0;
+  for (int e = 0; e < a.E; ++e) {
+    const int Me = max(0, min(a.offsets[e + 1], a.max_rows) - a.offsets[e]);
+    total += (int64_t)per * ((Me + BK - 1) / BK + 1);
+  }
+  const int64_t target = total * x / 8;
+  int64_t cum = 0;
+  for (int e = 0; e < a.E; ++e) {
+    const int Me = max(0, min(a.offsets[e + 1], a.max_rows) - a.offsets[e]);
+    const int64_t c = (Me + BK - 1) / BK + 1;
+    if (cum + per * c > target) return e * per + (int)((target - cum + c - 1) / c);
+    cum += per * c;
+  }
+  return P.nW;
+}
+
 // Persistent tile stream.  Each XCD takes a contiguous eighth of the tile list
 // (consecutive tiles share operand panels in its L2) and its blocks take the
 // tiles of that range in turn.  A block runs the k-tiles of all its tiles as
@@ -397,10 +421,19 @@ __global__ __launch_bounds__(C::NT, C::WPE) void k_gemm_stream(GemmPlan P) {
   __shared__ __attribute__((aligned(16))) uint16_t As[C::STAGES * C::BM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[C::STAGES * C::BN * BK];
   const GemmArgs& a = P.a;
-  const int n = DX ? a.mt_off[a.E] * P.ntn_x : P.nW;
   const int x = blockIdx.x & 7, nbx = gridDim.x >> 3;
-  const int hi = (int)((int64_t)n * (x + 1) / 8);
-  int tc = (int)((int64_t)n * x / 8) + (blockIdx.x >> 3);
+  int lo, hi;
+  if constexpr (DX) {
+    // every dX tile runs K = d_out: equal shares of the tile count
+    const int n = a.mt_off[a.E] * P.ntn_x;
+    lo = (int)((int64_t)n * x / 8);
+    hi = (int)((int64_t)n * (x + 1) / 8);
+  } else {
+    // dW tiles of expert e run ceil(M_e / 64) k-tiles: equal shares of the cost
+    lo = dw_tile_at_cost<C>(P, x);
+    hi = dw_tile_at_cost<C>(P, x + 1);
+  }
+  int tc = lo + (blockIdx.x >> 3);
 
   f32x4 acc[C::FM][C::FN];
 #pragma unroll
