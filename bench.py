@@ -8,10 +8,13 @@ unpermute to token layout; SwiGLU workloads chain down -> gate/up stages.
 Prints ONE JSON line.  `value` is kept pairs per second of the fused call
 (for SwiGLU, pairs kept by the down stage).  Stage times come from HIP events
 that the library records on its launch stream at stage boundaries; the
-`roofline` block covers the dominant kernel (the grouped GEMM); the
-`cpu_baseline` block times the fp64 CPU oracle on the host cores.
+`roofline` block covers the dominant kernel: for a linear layer the longer
+of the two grouped-GEMM launches (dW or dX), timed alone with HIP events on
+the packed operands of the same call; its `traffic` comes from the committed
+counter runs when they match the kernel source; the `cpu_baseline` block
+times the fp64 CPU oracle on the host cores.
 
-    python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu] [--full]
 """
 
 from __future__ import annotations
@@ -45,8 +48,11 @@ def parse():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--variant", default=None, help="3b: a real gate/up second selection")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-full", action="store_true",
-                    help="skip the unpruned (keep-all) comparison run")
+    ap.add_argument("--full", action="store_true",
+                    help="also time the unpruned (keep-all) call: its GEMM launches run other "
+                         "shapes, so it is off by default to keep the kernel statistics of a "
+                         "profiled bench run those of the pruned call")
+    ap.add_argument("--no-full", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 512 MiB device copy (a known-size kernel that "
                          "calibrates the HBM byte counters of a profiler pass)")
@@ -173,6 +179,73 @@ def time_fused(W, steps, warmup):
     return wall, per
 
 
+def gemm_kernels(W, steps, warmup):
+    """Times the two grouped-GEMM launches of a linear layer call on their
+    own, on the same packed operands the fused call builds: the dW kernel
+    (dW_e = Gp_e^T Xp_e) and the dX kernel (dXp_e = Gp_e W_e).  HIP events on
+    the launch stream around `steps` launches each.  Returns, per kernel, the
+    average launch duration and its algorithmic bytes and flops."""
+    L, p, r = W.L, W.p, W.r
+    dev = W.out["dW"].device
+    i32 = dict(dtype=torch.int32, device=dev)
+    X, G = L.mat(p["X"], p["X_rows"]), L.mat(p["G"], p["G_rows"])
+    score = torch.empty(r.N, dtype=torch.float32, device=dev)
+    L.lrm_score(W.pairs, X, G, score)
+    pos, kept = torch.empty(r.N, **i32), torch.empty(max(r.N, 1), **i32)
+    offsets = torch.empty(r.E + 1, **i32)
+    L.lrm_select(W.pairs, score, p["quota"], pos, offsets, kept, device=dev)
+    M = int(offsets[-1].item())
+    di, do = p["d_in"], p["d_out"]
+    Xp = torch.empty(max(M, 1), di, dtype=p["X"].dtype, device=dev)
+    Gp = torch.empty(max(M, 1), do, dtype=p["G"].dtype, device=dev)
+    L.lrm_compact(W.pairs, kept, offsets, M, X, G, Xp, Gp)
+    dW = torch.empty(r.E, do, di, dtype=torch.float32, device=dev)
+    dXp = torch.empty(max(M, 1), di, dtype=torch.float32, device=dev)
+    ws = torch.empty(1 << 16, dtype=torch.uint8, device=dev)
+    Me = np.diff(offsets.cpu().numpy().astype(np.int64))
+    act = int(np.count_nonzero(Me))
+    b = p["X"].element_size()
+    runs = {
+        "dW": (lambda: L.lrm_grouped_bwd(r.E, offsets, M, Gp, Xp, p["W"], di, do, dW, None, ws=ws),
+               dict(bytes=r.E * do * di * 4 + M * (di + do) * b, flops=2.0 * M * di * do)),
+        "dX": (lambda: L.lrm_grouped_bwd(r.E, offsets, M, Gp, Xp, p["W"], di, do, None, dXp, ws=ws),
+               dict(bytes=act * do * di * b + M * do * b + M * di * 4, flops=2.0 * M * di * do)),
+    }
+    res = {}
+    for name, (fn, work) in runs.items():
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = dict(work, ms=e0.elapsed_time(e1) / steps)
+    return res
+
+
+def traffic_of(kernel, workload):
+    """HBM bytes per launch from the committed counter runs (profiles/
+    hbm_traffic.json), or None when they were taken on another workload or on
+    another version of the kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    src = os.path.join(ROOT, "pruned_expert_backward_lrm_amd", "csrc", "k_gemm.hip")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        with open(src, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    for e in rec.get("kernels", []):
+        if e.get("kernel") == kernel and e.get("workload") == workload and e.get("source_sha256") == sha:
+            return e.get("hbm_bytes")
+    return None
+
+
 def time_loop(fn, steps, warmup):
     for _ in range(warmup):
         fn()
@@ -239,7 +312,7 @@ def main():
     wall, per = time_fused(W, a.steps, a.warmup)
     M, Me = W.kept()
     ms_full = None
-    if not a.no_full:
+    if a.full and not a.no_full:
         log("bench: timing the unpruned backward (every pair kept)")
         ms_full = time_loop(W.step_full, a.steps, a.warmup) * 1e3
     work = W.work(M, Me)
@@ -251,17 +324,33 @@ def main():
     ridge = peak_tf * 1e12 / (PEAK_HBM_GBS * 1e9)
     gbs = gbytes / t_g / 1e9
     tflops = flops / t_g / 1e12
-    if ai < ridge:
-        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
-    else:
-        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak_tf,
-                "unit": "TFLOP/s", "frac": round(tflops / peak_tf, 4), "traffic": None}
     spec = synth.CONFIGS[a.config]
     if p["kind"] == "linear":
         shape = f"T={r.T} d_in={p['d_in']} d_out={p['d_out']}"
     else:
         shape = f"T={r.T} H={p['H']} I={p['I']}"
+    workload = f"{spec['name']}{'-' + a.variant if a.variant else ''}: {shape} E={r.E} top-{r.k} zipf={spec['zipf']}"
+    kernels = None
+    if p["kind"] == "linear":
+        # the dominant kernel: the longer of the two GEMM launches, timed alone
+        log("bench: timing the grouped-GEMM kernels alone")
+        kernels = gemm_kernels(W, a.steps, a.warmup)
+        name = max(kernels, key=lambda k: kernels[k]["ms"])
+        kd = kernels[name]
+        kname = {"dW": "k_gemm_stream<dW>", "dX": "k_gemm_stream<dX>"}[name]
+        k_ai, k_t = kd["flops"] / kd["bytes"], kd["ms"] * 1e-3
+        k_gbs, k_tf = kd["bytes"] / k_t / 1e9, kd["flops"] / k_t / 1e12
+        traffic = traffic_of(kname, workload)
+    else:
+        # SwiGLU: the GEMM stages as a whole (several launches)
+        kname, k_ai, k_gbs, k_tf, traffic = "gemm stages", ai, gbs, tflops, None
+    if k_ai < ridge:
+        roof = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(k_gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
+    else:
+        roof = {"bound": "mfma", "achieved": round(k_tf, 2), "peak": peak_tf,
+                "unit": "TFLOP/s", "frac": round(k_tf / peak_tf, 4), "traffic": traffic}
+    roof["kernel"] = kname
     mem_stages = [s for s in W.stages if s not in W.gemm_stages]
     sc = [s for s in W.stages if s.startswith("score") or s.startswith("compact")]
     line = {
@@ -277,10 +366,13 @@ def main():
         "vs_baseline": None,
         "dtype": p["dtype"],
         "data": "synthetic",
-        "config": {"workload": f"{spec['name']}{'-' + a.variant if a.variant else ''}: {shape} "
-                               f"E={r.E} top-{r.k} zipf={spec['zipf']}",
+        "config": {"workload": workload,
                    "pairs": r.N, "kept_pairs": M, "active_experts": int(np.count_nonzero(Me))},
         "roofline": roof,
+        "gemm_kernels": ({k: {"ms": round(v["ms"], 4), "bytes": v["bytes"], "flops": v["flops"],
+                              "gbs": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1),
+                              "tflops": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 2)}
+                          for k, v in kernels.items()} if kernels else None),
         "grouped_gemm": {"ms": round(t_g * 1e3, 4), "tflops": round(tflops, 2),
                          "pct_mfma_peak": round(100 * tflops / peak_tf, 2),
                          "gbs": round(gbs, 1), "flops": flops, "bytes": gbytes,

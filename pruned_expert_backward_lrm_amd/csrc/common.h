@@ -48,14 +48,18 @@ __device__ __forceinline__ int wave_sum(int v) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
-// Inclusive scan across a wave (Hillis-Steele over 64 lanes).
+// Inclusive scan across a wave with DPP moves (no LDS round trips):
+// Hillis-Steele inside each 16-lane row (row_shr 1, 2, 4, 8; lanes whose
+// source falls before the row keep the 0 passed as "old"), then row 0's total
+// into row 1 and row 2's into row 3 (row_bcast:15 on rows 1, 3), then rows
+// 0-1's total into rows 2, 3 (row_bcast:31).
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int t = __shfl_up(v, o, kWave);
-    if (l >= o) v += t;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);
   return v;
 }
 

@@ -23,6 +23,8 @@
 namespace lrm {
 
 constexpr int kSelThreads = 1024;
+constexpr int kRowChunks = 16;  // bucket_blocks(N) <= 16 * 64 for every N
+constexpr int kSelRegKeys = 4;  // keys per thread held in registers by k_select
 
 __device__ __forceinline__ bool pair_valid(int64_t p, int T, int E, const int32_t* token,
                                            const int32_t* expert) {
@@ -76,11 +78,22 @@ __device__ void block_scan_array(int n, F get, int32_t* out, int* lds) {
   if (threadIdx.x == 0) out[n] = total;
 }
 
+// tok_off[t] for the tokens t that start at pair p (p in [0, N]): the first
+// pair whose token is >= t.
+__device__ __forceinline__ void token_offsets_at(int64_t p, int N, int T,
+                                                 const int32_t* __restrict__ token,
+                                                 int32_t* __restrict__ tok_off) {
+  const int lo = (p == 0) ? 0 : min(max(token[p - 1], -1), T - 1) + 1;
+  const int hi = (p == N) ? T : min(max(token[p], 0), T);
+  for (int t = lo; t <= hi; ++t) tok_off[t] = (int32_t)p;
+}
+
 __global__ __launch_bounds__(256) void k_bucket_count(int N, int T, int E, int chunk,
                                                       const int32_t* __restrict__ token,
                                                       const int32_t* __restrict__ expert,
                                                       int32_t* __restrict__ blkcnt,
-                                                      uint32_t* __restrict__ err) {
+                                                      uint32_t* __restrict__ err,
+                                                      int32_t* __restrict__ tok_off) {
   LRM_DYN_SHARED(int, hist);
   for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
   __syncthreads();
@@ -94,7 +107,9 @@ __global__ __launch_bounds__(256) void k_bucket_count(int N, int T, int E, int c
     if (t < 0 || t >= T) bad |= kErrTokenRange;
     if (p > 0 && token[p - 1] > t) bad |= kErrTokenOrder;
     if (e >= 0 && e < E && t >= 0 && t < T) atomicAdd(&hist[e], 1);
+    if (tok_off) token_offsets_at(p, N, T, token, tok_off);
   }
+  if (tok_off && p1 == N && threadIdx.x == 0) token_offsets_at(N, N, T, token, tok_off);
   if (bad) atomicOr(err, bad);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256) blkcnt[(int64_t)e * gridDim.x + blockIdx.x] = hist[e];
@@ -112,13 +127,23 @@ __global__ __launch_bounds__(kSelThreads) void k_bucket_scan(int nblk, int E,
   LRM_DYN_SHARED(int, counts);  // [E]
   __shared__ int lds[kSelThreads / kWave + 1];
   const int w = threadIdx.x >> 6, l = lane_id();
+  // (nblk <= kMaxBucketBlocks: a row is at most kRowChunks loads per lane,
+  // all issued before the scan)
   for (int e = w; e < E; e += kSelThreads / kWave) {
     int32_t* row = blkcnt + (int64_t)e * nblk;
+    int v[kRowChunks];
+#pragma unroll
+    for (int j = 0; j < kRowChunks; ++j) {
+      const int b = j * kWave + l;
+      v[j] = b < nblk ? row[b] : 0;
+    }
     int run = 0;
-    for (int b0 = 0; b0 < nblk; b0 += kWave) {
-      const int v = (b0 + l < nblk) ? row[b0 + l] : 0;
-      const int incl = wave_incl_scan(v);
-      if (b0 + l < nblk) row[b0 + l] = run + incl - v;
+#pragma unroll
+    for (int j = 0; j < kRowChunks; ++j) {
+      if (j * kWave >= nblk) break;
+      const int b = j * kWave + l;
+      const int incl = wave_incl_scan(v[j]);
+      if (b < nblk) row[b] = run + incl - v[j];
       run += __shfl(incl, kWave - 1, kWave);
     }
     if (l == 0) counts[e] = run;
@@ -228,15 +253,33 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const int32_t* __restric
     for (int i = tid; i < n; i += kSelThreads) pos[id_of(c0 + i)] = -1;
     return;
   }
-  // radix search for the m-th largest key (rank r counted from the top)
+  // radix search for the m-th largest key (rank r counted from the top); the
+  // keys of experts with up to kSelRegKeys * kSelThreads candidates are read
+  // once into registers
+  const bool in_regs = n <= kSelRegKeys * kSelThreads;
+  uint32_t kr[kSelRegKeys];
+#pragma unroll
+  for (int j = 0; j < kSelRegKeys; ++j) {
+    const int i = tid + j * kSelThreads;
+    kr[j] = (in_regs && i < n) ? keys[c0 + i] : 0u;
+  }
   uint32_t prefix = 0, pmask = 0;
   int r = m;
   for (int shift = 24; shift >= 0; shift -= 8) {
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += kSelThreads) {
-      const uint32_t k = keys[c0 + i];
-      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
+    if (in_regs) {
+#pragma unroll
+      for (int j = 0; j < kSelRegKeys; ++j) {
+        const uint32_t k = kr[j];
+        if (tid + j * kSelThreads < n && (k & pmask) == prefix)
+          atomicAdd(&hist[(k >> shift) & 255u], 1);
+      }
+    } else {
+      for (int i = tid; i < n; i += kSelThreads) {
+        const uint32_t k = keys[c0 + i];
+        if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
+      }
     }
     __syncthreads();
     if (tid < kWave) {
@@ -270,7 +313,14 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const int32_t* __restric
   for (int base = 0; base < n; base += kSelThreads) {
     const int i = base + tid;
     const bool valid = i < n;
-    const uint32_t k = valid ? keys[c0 + i] : 0u;
+    uint32_t k = 0u;
+    if (in_regs) {
+#pragma unroll
+      for (int j = 0; j < kSelRegKeys; ++j)
+        if (base == j * kSelThreads) k = kr[j];
+    } else if (valid) {
+      k = keys[c0 + i];
+    }
     const int eq = (valid && k == K) ? 1 : 0;
     const int gt = (valid && k > K) ? 1 : 0;
     int tot;
@@ -297,9 +347,7 @@ __global__ __launch_bounds__(256) void k_token_offsets(int N, int T,
                                                        int32_t* __restrict__ tok_off) {
   const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (p > N) return;
-  const int lo = (p == 0) ? 0 : min(max(token[p - 1], -1), T - 1) + 1;
-  const int hi = (p == N) ? T : min(max(token[p], 0), T);
-  for (int t = lo; t <= hi; ++t) tok_off[t] = (int32_t)p;
+  token_offsets_at(p, N, T, token, tok_off);
 }
 
 // mt_off[e] = sum over e' < e of ceil(M_e' / bm)  (row tiles of the dX GEMM)
@@ -328,9 +376,10 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s) {
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s) {
   const int nblk = bucket_blocks(a.N);
   const int chunk = bucket_chunk(a.N);
+  if (nblk > kRowChunks * kWave) return hipErrorInvalidValue;
   if (a.N > 0) {
     LRM_LAUNCH(nblk, 256, a.E * sizeof(int), s, k_bucket_count)(a.N, a.T, a.E, chunk, a.token,
-                                                        a.expert, a.blkcnt, a.err);
+                                                        a.expert, a.blkcnt, a.err, a.tok_off);
   }
   LRM_LAUNCH(1, kSelThreads, a.E * sizeof(int), s, k_bucket_scan)(nblk, a.E, a.blkcnt, a.quota,
                                                           a.cand_off, a.offsets);

@@ -47,6 +47,7 @@ struct BucketArgs {
   int32_t* pos;          // [N]
   int keep_all;          // pos written here (every valid pair kept, cand = kept)
   uint32_t* err;
+  int32_t* tok_off;      // [T+1] first pair of each token, or nullptr (not wanted)
 };
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s);
 hipError_t launch_select(int E, const int32_t* cand_off, const int32_t* offsets,

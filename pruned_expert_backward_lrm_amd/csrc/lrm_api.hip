@@ -159,9 +159,11 @@ SelectWs carve_select(Carve& c, int N, int E) {
 // Bucket the pairs by expert and select the top quota of each expert.
 // quota_host == nullptr keeps everything (then kept is filled by the bucket
 // scatter and no keys are gathered).
+// tok_off (optional, [T+1]): the first pair of each token, computed on the way
+// when there is at least one pair.
 lrm_status run_select(const lrm_pairs* p, const float* score, const int32_t* quota_host,
                       int32_t* pos, int32_t* offsets, int32_t* kept, const SelectWs& w,
-                      hipStream_t s) {
+                      hipStream_t s, int32_t* tok_off = nullptr) {
   const bool keep_all = quota_host == nullptr;
   if (!keep_all) {
     LRM_TRY_HIP(hipMemcpyAsync(w.quota, quota_host, sizeof(int32_t) * p->E,
@@ -174,7 +176,7 @@ lrm_status run_select(const lrm_pairs* p, const float* score, const int32_t* quo
   b.blkcnt = w.blkcnt; b.cand_off = w.cand_off; b.offsets = offsets;
   b.cand = keep_all ? kept : w.cand;
   b.keys = keep_all ? nullptr : w.keys;
-  b.pos = pos; b.keep_all = keep_all; b.err = w.err;
+  b.pos = pos; b.keep_all = keep_all; b.err = w.err; b.tok_off = tok_off;
   LRM_TRY_HIP(launch_bucket(b, s));
   if (!keep_all) LRM_TRY_HIP(launch_select(p->E, w.cand_off, offsets, w.keys, w.cand, pos, kept, s));
   return LRM_OK;
@@ -631,8 +633,10 @@ lrm_status run_linear(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   if (!keep_all) LRM_TRY_HIP(run_score(p, &pb->X, &pb->G, L.score, L.sc, s));
   LRM_TRY_HIP(mark(1));
   // 2. per-expert top-quota selection and packed rows
+  // (the token offsets of the unpermute step come out of the bucketing pass)
+  const bool tok_out = pb->X.rows != LRM_ROWS_PAIR;
   LRM_TRY(run_select(p, L.score, keep_all ? nullptr : pb->quota, L.pos, L.offsets, L.kept,
-                     L.sel, s));
+                     L.sel, s, tok_out && p->N > 0 ? L.tok_off : nullptr));
   LRM_TRY_HIP(mark(2));
   // 3. compaction: Xp = w x, Gp = g
   CompactArgs ca{};
@@ -656,7 +660,7 @@ lrm_status run_linear(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   sa.N = p->N; sa.T = p->T; sa.d = pb->d_in; sa.out_pair = pb->X.rows == LRM_ROWS_PAIR;
   sa.token = p->token; sa.weight = p->weight; sa.pos[0] = L.pos; sa.src[0] = L.dXp;
   if (!sa.out_pair) {
-    LRM_TRY_HIP(launch_token_offsets(p->N, p->T, p->token, L.tok_off, s));
+    if (p->N == 0) LRM_TRY_HIP(launch_token_offsets(p->N, p->T, p->token, L.tok_off, s));
     sa.tok_off = L.tok_off;
   }
   sa.dX = out->dX;
@@ -679,8 +683,10 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   // ---- down projection: input h = silu(a) * b, gradient g = G row
   if (!keep_all) LRM_TRY_HIP(run_score_glu(p, &pb->A, &pb->B, &pb->G, L.score, L.sc, s));
   LRM_TRY_HIP(mark(1));
+  // (the token offsets of the unpermute step come out of the bucketing pass)
+  const bool tok_out = pb->X.rows != LRM_ROWS_PAIR;
   LRM_TRY(run_select(p, L.score, keep_all ? nullptr : pb->quota_down, L.pos, L.offsets, L.kept,
-                     L.sel, s));
+                     L.sel, s, tok_out && p->N > 0 ? L.tok_off : nullptr));
   LRM_TRY_HIP(mark(2));
   CompactArgs cd{};
   cd.T = p->T; cd.bf16 = bf16; cd.max_rows = (int)z.Md; cd.E = E;
@@ -785,7 +791,7 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   }
   LRM_TRY_HIP(mark(8));
   if (x_tok) {
-    LRM_TRY_HIP(launch_token_offsets(p->N, p->T, p->token, L.tok_off, s));
+    if (p->N == 0) LRM_TRY_HIP(launch_token_offsets(p->N, p->T, p->token, L.tok_off, s));
     sa.tok_off = L.tok_off;
   }
   sa.dX = out->dX;

@@ -231,6 +231,30 @@ typedef ::emu::BufRsrc __amdgpu_buffer_rsrc_t;
 #define __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, aux) ::emu::buffer_load16((r), (voff), (soff))
 #define __builtin_amdgcn_perm(s0, s1, sel) ::emu::perm((s0), (s1), (sel))
 
+namespace emu {
+// DPP model for the controls the kernels use: row_shr:n (0x110 + n),
+// row_bcast:15 (0x142), row_bcast:31 (0x143); bound_ctrl off (lanes without a
+// valid source, or in rows outside row_mask, get old).
+inline int update_dpp(int old, int src, int ctrl, int row_mask) {
+  const int lane = ctx.lane, row = lane >> 4, i = lane & 15;
+  int from = -1;
+  if (ctrl > 0x110 && ctrl < 0x120) {
+    const int n = ctrl - 0x110;
+    if (i >= n) from = lane - n;
+  } else if (ctrl == 0x142) {
+    if (row >= 1) from = 16 * row - 1;
+  } else if (ctrl == 0x143) {
+    if (row >= 2) from = 31;
+  } else {
+    std::abort();
+  }
+  const int got = exchange(src, from >= 0 ? from : lane);
+  return (from >= 0 && ((row_mask >> row) & 1)) ? got : old;
+}
+}  // namespace emu
+#define __builtin_amdgcn_update_dpp(old, src, ctrl, rmask, bmask, bc) \
+  ::emu::update_dpp((old), (src), (ctrl), (rmask))
+
 #define threadIdx (::emu::ctx.tid)
 #define blockIdx (::emu::ctx.bid)
 #define blockDim (::emu::g_blockDim)
