@@ -384,28 +384,52 @@ __device__ __forceinline__ void mma_k32(f32x4 (&acc)[C::FM][C::FN], const uint16
   }
 }
 
-// First dW tile of share x (of 8) when the tiles, in order, are cut into
-// shares of equal cost; a tile of expert e costs ceil(M_e / 64) + 1 (its
-// k-tiles and its output).  Block-uniform; reads offsets[0..E].
-template <class C>
-__device__ __forceinline__ int dw_tile_at_cost(const GemmPlan& P, int x) {
+// dW shares: the tiles, in order, are cut into 8 shares of equal cost, a tile
+// of expert e costing ceil(M_e / 64) + kStoreCost: its k-tiles, plus its fp32
+// output, weighted as two k-tiles (the best of 1, 2, 3, 4, 8 and count-only
+// shares measured over the Qwen3 linear, GLM-4.5 local-32 and large SwiGLU
+// shapes).  Computed by every wave alike (no barrier): per-expert costs 64
+// experts at a time, wave sums and scans, the boundary expert found with a
+// ballot.
+constexpr int kStoreCost = 2;
+
+__device__ __forceinline__ int dw_cost(const GemmArgs& a, int e) {
+  const int Me = max(0, min(a.offsets[e + 1], a.max_rows) - a.offsets[e]);
+  return (Me + BK - 1) / BK + kStoreCost;
+}
+
+// First dW tile whose start cost is >= target (target <= total cost).
+__device__ __forceinline__ int dw_tile_at(const GemmArgs& a, int per, int64_t target) {
+  const int l = lane_id();
+  int64_t cum = 0;  // cost of the experts before this chunk
+  for (int e0 = 0; e0 < a.E; e0 += kWave) {
+    const int e = e0 + l;
+    const int c = e < a.E ? dw_cost(a, e) : 0;
+    const int incl = wave_incl_scan(c);
+    const int64_t end = cum + (int64_t)per * incl;  // cost through expert e
+    const uint64_t past = __ballot(e < a.E && end > target);
+    if (past) {
+      const int f = __builtin_ctzll(past);
+      const int cf = __shfl(c, f, kWave);
+      const int64_t before = cum + (int64_t)per * (__shfl(incl, f, kWave) - cf);
+      return (e0 + f) * per + (int)((target - before + cf - 1) / cf);
+    }
+    cum += (int64_t)per * __shfl(incl, kWave - 1, kWave);
+  }
+  return a.E * per;
+}
+
+__device__ __forceinline__ void dw_share(const GemmPlan& P, int x, int* lo, int* hi) {
   const GemmArgs& a = P.a;
   const int per = P.ntm_w * P.ntn;
-  if (x >= 8) return P.nW;
   int64_t total = 0;
-  for (int e = 0; e < a.E; ++e) {
-    const int Me = max(0, min(a.offsets[e + 1], a.max_rows) - a.offsets[e]);
-    total += (int64_t)per * ((Me + BK - 1) / BK + 1);
+  for (int e0 = 0; e0 < a.E; e0 += kWave) {
+    const int e = e0 + lane_id();
+    total += (int64_t)per * wave_sum(e < a.E ? dw_cost(a, e) : 0);
   }
-  const int64_t target = total * x / 8;
-  int64_t cum = 0;
-  for (int e = 0; e < a.E; ++e) {
-    const int Me = max(0, min(a.offsets[e + 1], a.max_rows) - a.offsets[e]);
-    const int64_t c = (Me + BK - 1) / BK + 1;
-    if (cum + per * c > target) return e * per + (int)((target - cum + c - 1) / c);
-    cum += per * c;
-  }
-  return P.nW;
+  // wave-uniform values: keep them (and the tile cursors built on them) scalar
+  *lo = __builtin_amdgcn_readfirstlane(dw_tile_at(a, per, total * x / 8));
+  *hi = __builtin_amdgcn_readfirstlane(x == 7 ? P.nW : dw_tile_at(a, per, total * (x + 1) / 8));
 }
 
 // Persistent tile stream.  Each XCD takes a contiguous eighth of the tile list
@@ -430,8 +454,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void k_gemm_stream(GemmPlan P) {
     hi = (int)((int64_t)n * (x + 1) / 8);
   } else {
     // dW tiles of expert e run ceil(M_e / 64) k-tiles: equal shares of the cost
-    lo = dw_tile_at_cost<C>(P, x);
-    hi = dw_tile_at_cost<C>(P, x + 1);
+    dw_share(P, x, &lo, &hi);
   }
   int tc = lo + (blockIdx.x >> 3);
 

@@ -274,6 +274,7 @@ inline float __uint_as_float(unsigned u) { float f; std::memcpy(&f, &u, 4); retu
 inline int __clz(int x) { return x == 0 ? 32 : __builtin_clz((unsigned)x); }
 inline int __popcll(unsigned long long x) { return __builtin_popcountll(x); }
 inline unsigned long long __ballot(int p) { return ::emu::ballot(p != 0); }
+inline int __builtin_amdgcn_readfirstlane(int v) { return ::emu::exchange(v, 0); }
 template <typename T>
 inline T __shfl_xor(T v, int o, int = 64) { return ::emu::exchange(v, ::emu::ctx.lane ^ o); }
 template <typename T>

@@ -44,6 +44,20 @@ def test_fused_swiglu_small(L, dtype, variant):
     say("  ", s)
 
 
+@pytest.mark.parametrize("tile", ["S", "M", "L", "X"])
+@pytest.mark.parametrize("variant", ["same", "second"])
+def test_fused_swiglu_tile_configs(L, variant, tile, monkeypatch):
+    """Every bf16 GEMM tile configuration inside the fused SwiGLU call: the
+    dual-K input-gradient product (same quotas) and the separate gate/up
+    products (second selection); H and I leave partial tiles."""
+    monkeypatch.setenv("LRM_GEMM_TILE", tile)
+    say("swiglu tiles", variant, tile)
+    p = synth.make_swiglu(700, 6, 2, 200, 136, dtype="bf16", seed=15, zipf=1.2,
+                          quotas=QUOTAS[variant], g_std=1e-2)
+    s = judge_swiglu(p, run_swiglu(L, p, DEV))
+    say("  ", s)
+
+
 def test_fused_swiglu_keep_all(L):
     p = synth.make_swiglu(300, 5, 2, 128, 64, dtype="bf16", seed=6, zipf=1.0)
     s = judge_swiglu(p, run_swiglu(L, p, DEV, flags=L.LRM_KEEP_ALL), keep_all=True)
