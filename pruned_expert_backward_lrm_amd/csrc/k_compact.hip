@@ -4,7 +4,8 @@
 // weight is folded into the activation side here (Xp = w x), so the grouped
 // GEMM computes dW_e = Gp_e^T Xp_e directly.
 //
-// HBM-bound row copy: one wave per packed row, 16-byte loads and stores.
+// HBM-bound row copy: one wave per packed row, 16-byte loads and stores, a
+// row's loads issued before its stores.
 #include "common.h"
 #include "launch.h"
 
@@ -46,6 +47,49 @@ __device__ __forceinline__ u32x4 glu_chunk_f32(u32x4 va, u32x4 vb, float w) {
   return o;
 }
 
+// One row of nch 16-byte chunks, f applied per chunk; each lane loads up to
+// kCpBatch chunks before it stores any, so a row's loads are in flight
+// together.
+constexpr int kCpBatch = 8;
+template <class F>
+__device__ __forceinline__ void copy_row(u32x4* dst, const u32x4* src, int nch, F f) {
+  const int l = lane_id();
+  for (int c0 = 0; c0 < nch; c0 += kCpBatch * kWave) {
+    u32x4 v[kCpBatch];
+#pragma unroll
+    for (int i = 0; i < kCpBatch; ++i) {
+      const int c = c0 + i * kWave + l;
+      if (c < nch) v[i] = src[c];
+    }
+#pragma unroll
+    for (int i = 0; i < kCpBatch; ++i) {
+      const int c = c0 + i * kWave + l;
+      if (c < nch) dst[c] = f(v[i]);
+    }
+  }
+}
+template <class F>
+__device__ __forceinline__ void copy_row2(u32x4* dst, const u32x4* src, const u32x4* src2,
+                                          int nch, F f) {
+  const int l = lane_id();
+  for (int c0 = 0; c0 < nch; c0 += kCpBatch / 2 * kWave) {
+    u32x4 va[kCpBatch / 2], vb[kCpBatch / 2];
+#pragma unroll
+    for (int i = 0; i < kCpBatch / 2; ++i) {
+      const int c = c0 + i * kWave + l;
+      if (c < nch) {
+        va[i] = src[c];
+        vb[i] = src2[c];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kCpBatch / 2; ++i) {
+      const int c = c0 + i * kWave + l;
+      if (c < nch) dst[c] = f(va[i], vb[i]);
+    }
+  }
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   constexpr int kEsz = BF16 ? 2 : 4;
@@ -64,20 +108,19 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
       if (a.glu) {
         const u32x4* src2 =
             reinterpret_cast<const u32x4*>((const char*)a.X2 + xr * a.ldx2 * kEsz);
-        for (int c = lane_id(); c < a.xcols / kEpc; c += kWave)
-          dst[c] = BF16 ? glu_chunk_bf16(src[c], src2[c], w) : glu_chunk_f32(src[c], src2[c], w);
+        copy_row2(dst, src, src2, a.xcols / kEpc, [w](u32x4 va, u32x4 vb) {
+          return BF16 ? glu_chunk_bf16(va, vb, w) : glu_chunk_f32(va, vb, w);
+        });
       } else {
-        for (int c = lane_id(); c < a.xcols / kEpc; c += kWave) {
-          const u32x4 v = src[c];
-          dst[c] = BF16 ? scale_chunk_bf16(v, w) : scale_chunk_f32(v, w);
-        }
+        copy_row(dst, src, a.xcols / kEpc,
+                 [w](u32x4 v) { return BF16 ? scale_chunk_bf16(v, w) : scale_chunk_f32(v, w); });
       }
     }
     if (a.Gp) {
       const int64_t gr = a.g_by_id ? (int64_t)id : (a.g_pair ? (int64_t)p : (int64_t)t);
       const u32x4* src = reinterpret_cast<const u32x4*>((const char*)a.G + gr * a.ldg * kEsz);
       u32x4* dst = reinterpret_cast<u32x4*>((char*)a.Gp + (int64_t)j * a.gcols * kEsz);
-      for (int c = lane_id(); c < a.gcols / kEpc; c += kWave) dst[c] = src[c];
+      copy_row(dst, src, a.gcols / kEpc, [](u32x4 v) { return v; });
     }
   }
 }

@@ -22,57 +22,82 @@ __device__ __forceinline__ f32x4 ld4(const float* p) {
   return *reinterpret_cast<const f32x4*>(p);
 }
 
-// Columns held in registers per pass: kUnpChunks x 64 lanes x 4 floats.
-constexpr int kUnpChunks = 8;
+// Token layout: one wave per (token, block of kUnpCols columns), so that every
+// wave has a short dependency chain (offsets -> descriptors -> rows) and the
+// whole grid is resident at once.  The token's pair descriptors (source rows,
+// weight) are loaded once, one pair per lane, and broadcast with shuffles; the
+// rows of kUnpBatch pairs are then loaded together with buffer loads (a pair
+// with nothing kept takes an offset outside the bound and reads zeros, so no
+// branch stands between the loads) before they are summed in pair order.
+constexpr int kUnpChunks = 2;  // 16-byte chunks per lane
+constexpr int kUnpCols = kUnpChunks * kWave * 4;
+constexpr int kUnpBatch = 4;
 
-// One wave per token.  The token's pair descriptors (source rows, weight) are
-// loaded once, one pair per lane, and broadcast with shuffles; each pair then
-// issues kUnpChunks independent 16-byte loads per lane.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const float* p, int64_t nbytes) {
+  const int n = nbytes <= 0 ? 0 : (nbytes > 0x7ffffff0ll ? 0x7ffffff0 : (int)nbytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), (short)0, n, 0x00020000);
+}
+
 __global__ __launch_bounds__(256) void k_unpermute_token(ScatterArgs a) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.T) return;
+  const int nblk = (a.d + kUnpCols - 1) / kUnpCols;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (gw >= (int64_t)a.T * nblk) return;
+  const int t = (int)(gw / nblk), cb = (int)(gw % nblk) * kUnpCols;
   const int l = lane_id();
   const int p0 = min(max(a.tok_off[t], 0), a.N);
   const int p1 = min(max(a.tok_off[t + 1], p0), a.N);
-  float* out = a.dX + (int64_t)t * a.d;
-  for (int cb = 0; cb < a.d; cb += kUnpChunks * kWave * 4) {
-    f32x4 acc[kUnpChunks];
+  // columns of this lane
+  int col[kUnpChunks];
 #pragma unroll
-    for (int u = 0; u < kUnpChunks; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int pb = p0; pb < p1; pb += kWave) {
-      const int pi = pb + l;
-      int r0 = -1, r1 = -1;
-      float w = 0.f;
-      if (pi < p1) {
-        w = a.weight[pi];
-        r0 = src_row(a, 0, pi);
-        r1 = src_row(a, 1, pi);
-      }
-      const int np = min(kWave, p1 - pb);
-      for (int j = 0; j < np; ++j) {
-        const float wj = __shfl(w, j, kWave);
-        const int rj0 = __shfl(r0, j, kWave);
-        const int rj1 = __shfl(r1, j, kWave);
-        if (rj0 >= 0) {
-          const float* src = a.src[0] + (int64_t)rj0 * a.d + cb + l * 4;
+  for (int u = 0; u < kUnpChunks; ++u) col[u] = cb + (u * kWave + l) * 4;
+  f32x4 acc[kUnpChunks];
 #pragma unroll
-          for (int u = 0; u < kUnpChunks; ++u)
-            if (cb + (u * kWave + l) * 4 < a.d) acc[u] += wj * ld4(src + u * kWave * 4);
-        }
-        if (rj1 >= 0) {
-          const float* src = a.src[1] + (int64_t)rj1 * a.d + cb + l * 4;
-#pragma unroll
-          for (int u = 0; u < kUnpChunks; ++u)
-            if (cb + (u * kWave + l) * 4 < a.d) acc[u] += wj * ld4(src + u * kWave * 4);
-        }
-      }
+  for (int u = 0; u < kUnpChunks; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int pb = p0; pb < p1; pb += kWave) {
+    const int pi = pb + l;
+    int r0 = -1, r1 = -1;
+    float w = 0.f;
+    if (pi < p1) {
+      w = a.weight[pi];
+      r0 = src_row(a, 0, pi);
+      r1 = src_row(a, 1, pi);
     }
+    const int np = min(kWave, p1 - pb);
+    for (int j0 = 0; j0 < np; j0 += kUnpBatch) {
+      f32x4 v[kUnpBatch][2][kUnpChunks];
+      float wj[kUnpBatch];
 #pragma unroll
-    for (int u = 0; u < kUnpChunks; ++u) {
-      const int c = cb + (u * kWave + l) * 4;
-      if (c < a.d) *reinterpret_cast<f32x4*>(out + c) = acc[u];
+      for (int jj = 0; jj < kUnpBatch; ++jj) {
+        const int j = min(j0 + jj, kWave - 1);
+        const bool in = j0 + jj < np;
+        wj[jj] = __shfl(w, j, kWave);
+        // one buffer resource per source row (wave-uniform): the row itself,
+        // or an empty one for a pair whose row is not kept
+        const int rj[2] = {__builtin_amdgcn_readfirstlane(in ? __shfl(r0, j, kWave) : -1),
+                           __builtin_amdgcn_readfirstlane(in ? __shfl(r1, j, kWave) : -1)};
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const __amdgpu_buffer_rsrc_t rs =
+              rows_rsrc(a.src[k] + (int64_t)max(rj[k], 0) * a.d, rj[k] >= 0 ? (int64_t)a.d * 4 : 0);
+#pragma unroll
+          for (int u = 0; u < kUnpChunks; ++u)
+            v[jj][k][u] = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                           rs, col[u] < a.d ? col[u] * 4 : 0x7ffffff0, 0, 0));
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < kUnpBatch; ++jj)
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int u = 0; u < kUnpChunks; ++u) acc[u] += wj[jj] * v[jj][k][u];
     }
   }
+  float* out = a.dX + (int64_t)t * a.d;
+#pragma unroll
+  for (int u = 0; u < kUnpChunks; ++u)
+    if (col[u] < a.d) *reinterpret_cast<f32x4*>(out + col[u]) = acc[u];
 }
 
 __global__ __launch_bounds__(256) void k_unpermute_pair(ScatterArgs a) {
@@ -95,7 +120,9 @@ hipError_t launch_unpermute(const ScatterArgs& a, hipStream_t s) {
   if (a.out_pair) {
     if (a.N > 0) LRM_LAUNCH((a.N + 3) / 4, 256, 0, s, k_unpermute_pair)(a);
   } else {
-    if (a.T > 0) LRM_LAUNCH((a.T + 3) / 4, 256, 0, s, k_unpermute_token)(a);
+    const int64_t waves = (int64_t)a.T * ((a.d + kUnpCols - 1) / kUnpCols);
+    if (waves > (1ll << 33)) return hipErrorInvalidValue;
+    if (a.T > 0) LRM_LAUNCH((unsigned)((waves + 3) / 4), 256, 0, s, k_unpermute_token)(a);
   }
   return hipGetLastError();
 }
