@@ -656,7 +656,7 @@ static hipError_t plan_tiles(const GemmArgs& a, int tmw, int tnw, int tmx, int t
   P->ntm_w = (a.d_out + tmw - 1) / tmw;
   P->nW = a.dW ? a.E * P->ntm_w * P->ntn : 0;
   P->nX = (a.dXp && a.max_rows > 0) ? ((a.max_rows + tmx - 1) / tmx + a.E) * P->ntn_x : 0;
-  if (P->nX > 0) {
+  if (P->nX > 0 && !a.mt_ready) {
     hipError_t err = launch_tile_plan(a.E, tmx, a.offsets, a.mt_off, s);
     if (err != hipSuccess) return err;
   }
@@ -718,6 +718,16 @@ int gemm_tile_choice(const GemmArgs& a) {
   if (env && env[0] == 'X') return 3;
   const int64_t per_expert = a.E > 0 ? (int64_t)a.max_rows / a.E : 0;
   return per_expert >= 192 ? 2 : 3;
+}
+
+int gemm_dx_tile_rows(const GemmArgs& a) {
+  if (!a.bf16) return FBM;
+  switch (gemm_tile_choice(a)) {
+    case 3: return CfgXS::BM;
+    case 2: return CfgL::BM;
+    case 1: return CfgM::BM;
+    default: return CfgS::BM;
+  }
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s) {

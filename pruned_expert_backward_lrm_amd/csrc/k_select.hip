@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void k_bucket_count(int N, int T, int E, int c
                                                       const int32_t* __restrict__ token,
                                                       const int32_t* __restrict__ expert,
                                                       int32_t* __restrict__ blkcnt,
-                                                      uint32_t* __restrict__ err,
+                                                      uint32_t* __restrict__ blkerr,
                                                       int32_t* __restrict__ tok_off) {
   LRM_DYN_SHARED(int, hist);
   for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
@@ -110,8 +110,14 @@ __global__ __launch_bounds__(256) void k_bucket_count(int N, int T, int E, int c
     if (tok_off) token_offsets_at(p, N, T, token, tok_off);
   }
   if (tok_off && p1 == N && threadIdx.x == 0) token_offsets_at(N, N, T, token, tok_off);
-  if (bad) atomicOr(err, bad);
+  // this block's error bits: one word per block, written every call (no
+  // zeroing pass); the scan kernel folds them into the call's error word
+  __shared__ uint32_t berr;
+  if (threadIdx.x == 0) berr = 0u;
   __syncthreads();
+  if (bad) atomicOr(&berr, bad);
+  __syncthreads();
+  if (threadIdx.x == 0) blkerr[blockIdx.x] = berr;
   for (int e = threadIdx.x; e < E; e += 256) blkcnt[(int64_t)e * gridDim.x + blockIdx.x] = hist[e];
 }
 
@@ -119,13 +125,27 @@ __global__ __launch_bounds__(256) void k_bucket_count(int N, int T, int E, int c
 // one expert's block counts, 64 at a time); cand_off = prefix of the
 // per-expert counts; offsets = prefix of M_e = min(quota_e, n_e)
 // (quota == nullptr: keep all).
+// Also: err[0] = OR of the blocks' error bits; mt_off (optional) = prefix of
+// ceil(M_e / mt_bm), the dX row tiles of the grouped GEMM.
 __global__ __launch_bounds__(kSelThreads) void k_bucket_scan(int nblk, int E,
                                                              int32_t* __restrict__ blkcnt,
                                                              const int32_t* __restrict__ quota,
                                                              int32_t* __restrict__ cand_off,
-                                                             int32_t* __restrict__ offsets) {
+                                                             int32_t* __restrict__ offsets,
+                                                             const uint32_t* __restrict__ blkerr,
+                                                             uint32_t* __restrict__ err,
+                                                             int32_t* __restrict__ mt_off,
+                                                             int mt_bm) {
   LRM_DYN_SHARED(int, counts);  // [E]
   __shared__ int lds[kSelThreads / kWave + 1];
+  __shared__ uint32_t eor;
+  if (threadIdx.x == 0) eor = 0u;
+  __syncthreads();
+  {
+    uint32_t bad = 0u;
+    for (int b = threadIdx.x; b < nblk; b += kSelThreads) bad |= blkerr[b];
+    if (bad) atomicOr(&eor, bad);
+  }
   const int w = threadIdx.x >> 6, l = lane_id();
   // (nblk <= kMaxBucketBlocks: a row is at most kRowChunks loads per lane,
   // all issued before the scan)
@@ -157,6 +177,17 @@ __global__ __launch_bounds__(kSelThreads) void k_bucket_scan(int nblk, int E,
         return quota ? min(max(quota[e], 0), n) : n;
       },
       offsets, lds);
+  if (mt_off) {
+    block_scan_array<kSelThreads>(
+        E,
+        [&](int e) {
+          const int n = counts[e];
+          const int m = quota ? min(max(quota[e], 0), n) : n;
+          return (m + mt_bm - 1) / mt_bm;
+        },
+        mt_off, lds);
+  }
+  if (threadIdx.x == 0) err[0] = eor;
 }
 
 // Stage-two offsets: candidates of e are cand_off[e]..cand_off[e+1].
@@ -379,10 +410,12 @@ hipError_t launch_bucket(const BucketArgs& a, hipStream_t s) {
   if (nblk > kRowChunks * kWave) return hipErrorInvalidValue;
   if (a.N > 0) {
     LRM_LAUNCH(nblk, 256, a.E * sizeof(int), s, k_bucket_count)(a.N, a.T, a.E, chunk, a.token,
-                                                        a.expert, a.blkcnt, a.err, a.tok_off);
+                                                        a.expert, a.blkcnt, a.blkerr, a.tok_off);
   }
+  if (a.mt_off && a.mt_bm < 1) return hipErrorInvalidValue;
   LRM_LAUNCH(1, kSelThreads, a.E * sizeof(int), s, k_bucket_scan)(nblk, a.E, a.blkcnt, a.quota,
-                                                          a.cand_off, a.offsets);
+                                                          a.cand_off, a.offsets, a.blkerr,
+                                                          a.err, a.mt_off, a.mt_bm);
   if (a.N > 0) {
     LRM_LAUNCH(nblk, 64, a.E * sizeof(int), s, k_bucket_scatter)(a.N, a.T, a.E, chunk, a.token,
                                                          a.expert, a.blkcnt, a.cand_off, a.score,

@@ -46,8 +46,11 @@ struct BucketArgs {
   uint32_t* keys;        // [N] or nullptr
   int32_t* pos;          // [N]
   int keep_all;          // pos written here (every valid pair kept, cand = kept)
-  uint32_t* err;
+  uint32_t* err;         // one word: the error bits of this call
+  uint32_t* blkerr;      // [bucket_blocks(N)] per-block error bits (scratch)
   int32_t* tok_off;      // [T+1] first pair of each token, or nullptr (not wanted)
+  int32_t* mt_off;       // [E+1] row-tile prefix of the kept blocks for dX tiles
+  int mt_bm;             //   of mt_bm rows (mt_off == nullptr: not wanted)
 };
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s);
 hipError_t launch_select(int E, const int32_t* cand_off, const int32_t* offsets,
@@ -94,8 +97,11 @@ struct GemmArgs {
   float* dW;   // [E][d_out][d_in] or nullptr
   float* dXp;  // [max_rows][d_in] or nullptr
   int32_t* mt_off;  // workspace [E+1]
+  int mt_ready;     // mt_off already holds the prefix for gemm_dx_tile_rows(*this)
 };
 int gemm_tile_choice(const GemmArgs& a);
+// Rows of a dX tile of the bf16 kernels (the prefix mt_off is built for it).
+int gemm_dx_tile_rows(const GemmArgs& a);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------ unpermute

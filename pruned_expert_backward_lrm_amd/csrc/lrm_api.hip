@@ -138,6 +138,7 @@ hipError_t run_score_glu(const lrm_pairs* p, const lrm_mat* A, const lrm_mat* B,
 
 struct SelectWs {
   uint32_t* err;
+  uint32_t* blkerr;
   int32_t* quota;
   int32_t* blkcnt;
   int32_t* cand_off;
@@ -148,6 +149,7 @@ struct SelectWs {
 SelectWs carve_select(Carve& c, int N, int E) {
   SelectWs w;
   w.err = c.take<uint32_t>(64);
+  w.blkerr = c.take<uint32_t>(bucket_blocks(N));
   w.quota = c.take<int32_t>(E);
   w.blkcnt = c.take<int32_t>((int64_t)bucket_blocks(N) * E);
   w.cand_off = c.take<int32_t>(E + 1);
@@ -160,10 +162,12 @@ SelectWs carve_select(Carve& c, int N, int E) {
 // quota_host == nullptr keeps everything (then kept is filled by the bucket
 // scatter and no keys are gathered).
 // tok_off (optional, [T+1]): the first pair of each token, computed on the way
-// when there is at least one pair.
+// when there is at least one pair.  mt_off (optional, [E+1]): the prefix of
+// ceil(M_e / mt_bm), the dX row tiles of the grouped GEMM.
 lrm_status run_select(const lrm_pairs* p, const float* score, const int32_t* quota_host,
                       int32_t* pos, int32_t* offsets, int32_t* kept, const SelectWs& w,
-                      hipStream_t s, int32_t* tok_off = nullptr) {
+                      hipStream_t s, int32_t* tok_off = nullptr, int32_t* mt_off = nullptr,
+                      int mt_bm = 0) {
   const bool keep_all = quota_host == nullptr;
   if (!keep_all) {
     LRM_TRY_HIP(hipMemcpyAsync(w.quota, quota_host, sizeof(int32_t) * p->E,
@@ -176,7 +180,8 @@ lrm_status run_select(const lrm_pairs* p, const float* score, const int32_t* quo
   b.blkcnt = w.blkcnt; b.cand_off = w.cand_off; b.offsets = offsets;
   b.cand = keep_all ? kept : w.cand;
   b.keys = keep_all ? nullptr : w.keys;
-  b.pos = pos; b.keep_all = keep_all; b.err = w.err; b.tok_off = tok_off;
+  b.pos = pos; b.keep_all = keep_all; b.err = w.err; b.blkerr = w.blkerr; b.tok_off = tok_off;
+  b.mt_off = mt_off; b.mt_bm = mt_bm;
   LRM_TRY_HIP(launch_bucket(b, s));
   if (!keep_all) LRM_TRY_HIP(launch_select(p->E, w.cand_off, offsets, w.keys, w.cand, pos, kept, s));
   return LRM_OK;
@@ -280,7 +285,6 @@ lrm_status lrm_select(const lrm_pairs* pairs, const float* score, const int32_t*
   Carve r(ws);
   SelectWs w = carve_select(r, pairs->N, pairs->E);
   hipStream_t s = as_stream(stream);
-  LRM_TRY_HIP(launch_fill_u32(w.err, 0u, 1, s));
   return run_select(pairs, score, keep_all ? nullptr : quota, pos, offsets, kept, w, s);
 }
 
@@ -627,8 +631,12 @@ lrm_status run_linear(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   Carve c(ws);
   LinearPlan L = carve_linear(c, pb, out, Mcap);
   const int bf16 = pb->dtype == LRM_BF16;
+  // the grouped GEMM's launch shape (its dX row-tile prefix is built by the
+  // selection pass)
+  GemmArgs g{};
+  g.E = p->E; g.bf16 = bf16; g.max_rows = (int)Mcap;
+  const int dx_rows = gemm_dx_tile_rows(g);
   LRM_TRY_HIP(mark(0));
-  LRM_TRY_HIP(launch_fill_u32(L.sel.err, 0u, 1, s));
   // 1. LRM score of every pair
   if (!keep_all) LRM_TRY_HIP(run_score(p, &pb->X, &pb->G, L.score, L.sc, s));
   LRM_TRY_HIP(mark(1));
@@ -636,7 +644,7 @@ lrm_status run_linear(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   // (the token offsets of the unpermute step come out of the bucketing pass)
   const bool tok_out = pb->X.rows != LRM_ROWS_PAIR;
   LRM_TRY(run_select(p, L.score, keep_all ? nullptr : pb->quota, L.pos, L.offsets, L.kept,
-                     L.sel, s, tok_out && p->N > 0 ? L.tok_off : nullptr));
+                     L.sel, s, tok_out && p->N > 0 ? L.tok_off : nullptr, L.mt_off, dx_rows));
   LRM_TRY_HIP(mark(2));
   // 3. compaction: Xp = w x, Gp = g
   CompactArgs ca{};
@@ -649,10 +657,9 @@ lrm_status run_linear(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   LRM_TRY_HIP(launch_compact(ca, s));
   LRM_TRY_HIP(mark(3));
   // 4. grouped GEMM: dW_e = Gp_e^T Xp_e, dXp_e = Gp_e W_e
-  GemmArgs g{};
-  g.E = p->E; g.bf16 = bf16; g.max_rows = (int)Mcap; g.d_in = pb->d_in; g.d_out = pb->d_out;
+  g.d_in = pb->d_in; g.d_out = pb->d_out;
   g.offsets = L.offsets; g.Gp = L.Gp; g.Xp = L.Xp; g.W = pb->W; g.w_stride = pb->w_stride;
-  g.dW = out->dW; g.dXp = L.dXp; g.mt_off = L.mt_off;
+  g.dW = out->dW; g.dXp = L.dXp; g.mt_off = L.mt_off; g.mt_ready = 1;
   LRM_TRY_HIP(launch_grouped_gemm(g, s));
   LRM_TRY_HIP(mark(4));
   // 5. back to the layout of X, times the routing weight
@@ -678,15 +685,17 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   GluPlan L = carve_glu(c, pb, out, z.Md, z.Mg, z.Mu, z.pass_through);
   const int bf16 = pb->dtype == LRM_BF16;
   const int H = pb->H, I = pb->I, E = p->E;
+  GemmArgs gd{};
+  gd.E = E; gd.bf16 = bf16; gd.max_rows = (int)z.Md;
+  const int dx_rows = gemm_dx_tile_rows(gd);
   LRM_TRY_HIP(mark(0));
-  LRM_TRY_HIP(launch_fill_u32(L.sel.err, 0u, 1, s));
   // ---- down projection: input h = silu(a) * b, gradient g = G row
   if (!keep_all) LRM_TRY_HIP(run_score_glu(p, &pb->A, &pb->B, &pb->G, L.score, L.sc, s));
   LRM_TRY_HIP(mark(1));
   // (the token offsets of the unpermute step come out of the bucketing pass)
   const bool tok_out = pb->X.rows != LRM_ROWS_PAIR;
   LRM_TRY(run_select(p, L.score, keep_all ? nullptr : pb->quota_down, L.pos, L.offsets, L.kept,
-                     L.sel, s, tok_out && p->N > 0 ? L.tok_off : nullptr));
+                     L.sel, s, tok_out && p->N > 0 ? L.tok_off : nullptr, L.mt_off, dx_rows));
   LRM_TRY_HIP(mark(2));
   CompactArgs cd{};
   cd.T = p->T; cd.bf16 = bf16; cd.max_rows = (int)z.Md; cd.E = E;
@@ -697,11 +706,10 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   cd.Gp = L.Gd;
   LRM_TRY_HIP(launch_compact(cd, s));
   LRM_TRY_HIP(mark(3));
-  GemmArgs gd{};
-  gd.E = E; gd.bf16 = bf16; gd.max_rows = (int)z.Md; gd.d_in = I; gd.d_out = H;
+  gd.d_in = I; gd.d_out = H;
   gd.offsets = L.offsets; gd.Gp = L.Gd; gd.Xp = L.Hd;
   gd.W = pb->W_down; gd.w_stride = (int64_t)H * I;
-  gd.dW = out->dW_down; gd.dXp = L.U; gd.mt_off = L.mt_off;
+  gd.dW = out->dW_down; gd.dXp = L.U; gd.mt_off = L.mt_off; gd.mt_ready = 1;
   LRM_TRY_HIP(launch_grouped_gemm(gd, s));
   LRM_TRY_HIP(mark(4));
   // ---- SwiGLU backward and the gate/up scores
