@@ -490,6 +490,13 @@ __global__ __launch_bounds__(C::NT, C::WPE) void k_gemm_stream(GemmPlan P) {
       }                                                                         \
     }                                                                           \
   }
+  // Where the registers allow, the loads of k-tile i+2 are issued as soon as
+  // k-tile i+1 has left the registers for LDS, in the middle of k-tile i's
+  // MFMAs, which gives them a whole k-tile of MFMAs to arrive (issued after
+  // the MFMAs, they get half of one).  256x256 dX tiles keep the late issue:
+  // their larger job state leaves no room for loads in flight across the
+  // second half of the MFMAs.
+  constexpr bool kEarlyLoad = C::STAGES == 2 && (!DX || C::FM * C::FN < 32);
   LRM_ISSUE_LOAD();
   st.store(As, Bs);
   LRM_ISSUE_LOAD();
@@ -505,12 +512,13 @@ __global__ __launch_bounds__(C::NT, C::WPE) void k_gemm_stream(GemmPlan P) {
       // past the stream's end: the stage they fill is then never read)
       st.store(As + (cur ^ 1) * (C::BM * BK), Bs + (cur ^ 1) * (C::BN * BK));
     }
+    if constexpr (kEarlyLoad) LRM_ISSUE_LOAD();
     mma_k32<C>(acc, Ac, Bc, 4);
     if constexpr (C::STAGES == 1) {
       __syncthreads();  // every wave is done with the stage
       st.store(As, Bs);
     }
-    LRM_ISSUE_LOAD();
+    if constexpr (!kEarlyLoad) LRM_ISSUE_LOAD();
     if (++kc == jc.nk) {
       write_tile<C>(acc, false, jc.C, a.d_in, jc.rows, jc.cols);
 #pragma unroll
