@@ -23,15 +23,9 @@
 namespace lrm {
 
 constexpr int kSelThreads = 1024;
-constexpr int kRowChunks = 16;  // bucket_blocks(N) <= 16 * 64 for every N
 constexpr int kSelRegKeys = 4;  // keys per thread held in registers by k_select
-
-__device__ __forceinline__ bool pair_valid(int64_t p, int T, int E, const int32_t* token,
-                                           const int32_t* expert) {
-  const int e = expert[p];
-  const int t = token[p];
-  return e >= 0 && e < E && t >= 0 && t < T;
-}
+constexpr int kScanTile = 8192;  // block counts staged in LDS per round by k_bucket_scan
+constexpr int kScatBatch = 8;   // 64-pair groups per wave loaded ahead by k_bucket_scatter
 
 // Exclusive scan of one int per thread over an NT-thread block.  lds must hold
 // NT/64 + 1 ints.  Returns the exclusive prefix; *total gets the block sum.
@@ -147,26 +141,44 @@ __global__ __launch_bounds__(kSelThreads) void k_bucket_scan(int nblk, int E,
     if (bad) atomicOr(&eor, bad);
   }
   const int w = threadIdx.x >> 6, l = lane_id();
-  // (nblk <= kMaxBucketBlocks: a row is at most kRowChunks loads per lane,
-  // all issued before the scan)
-  for (int e = w; e < E; e += kSelThreads / kWave) {
-    int32_t* row = blkcnt + (int64_t)e * nblk;
-    int v[kRowChunks];
+  constexpr int NW = kSelThreads / kWave;
+  constexpr int PER = kScanTile / kSelThreads;
+  // Rounds of R whole rows (rows of consecutive experts are contiguous in
+  // blkcnt): the block loads a round's counts with coalesced loads, issued
+  // before the previous round is scanned, stages them in LDS, and wave w
+  // scans rows w, w + NW, ... of the round from there.
+  __shared__ int stage[kScanTile];
+  const int R = nblk > 0 ? kScanTile / nblk : E;  // nblk <= kScanTile
+  int v[PER];
+  auto load_round = [&](int e0) {
+    const int cnt = min(R, E - e0) * nblk;
+    const int32_t* src = blkcnt + (int64_t)e0 * nblk;
 #pragma unroll
-    for (int j = 0; j < kRowChunks; ++j) {
-      const int b = j * kWave + l;
-      v[j] = b < nblk ? row[b] : 0;
+    for (int u = 0; u < PER; ++u) {
+      const int idx = threadIdx.x + u * kSelThreads;
+      v[u] = idx < cnt ? src[idx] : 0;
     }
-    int run = 0;
+  };
+  if (E > 0) load_round(0);
+  for (int e0 = 0; e0 < E; e0 += R) {
+    const int rows = min(R, E - e0);
 #pragma unroll
-    for (int j = 0; j < kRowChunks; ++j) {
-      if (j * kWave >= nblk) break;
-      const int b = j * kWave + l;
-      const int incl = wave_incl_scan(v[j]);
-      if (b < nblk) row[b] = run + incl - v[j];
-      run += __shfl(incl, kWave - 1, kWave);
+    for (int u = 0; u < PER; ++u) stage[threadIdx.x + u * kSelThreads] = v[u];
+    __syncthreads();
+    if (e0 + R < E) load_round(e0 + R);
+    for (int r = w; r < rows; r += NW) {
+      int32_t* row = blkcnt + (int64_t)(e0 + r) * nblk;
+      int run = 0;
+      for (int b0 = 0; b0 < nblk; b0 += kWave) {
+        const int b = b0 + l;
+        const int x = b < nblk ? stage[r * nblk + b] : 0;
+        const int incl = wave_incl_scan(x);
+        if (b < nblk) row[b] = run + incl - x;
+        run += __shfl(incl, kWave - 1, kWave);
+      }
+      if (l == 0) counts[e0 + r] = run;
     }
-    if (l == 0) counts[e] = run;
+    __syncthreads();
   }
   __syncthreads();
   block_scan_array<kSelThreads>(E, [&](int e) { return counts[e]; }, cand_off, lds);
@@ -224,31 +236,48 @@ __global__ __launch_bounds__(64) void k_bucket_scatter(int N, int T, int E, int 
   const int64_t p0 = (int64_t)blockIdx.x * chunk;
   const int64_t p1 = min<int64_t>(p0 + chunk, N);
   const uint64_t lt_mask = (l == 0) ? 0ull : (~0ull >> (64 - l));
-  for (int64_t base = p0; base < p1; base += kWave) {
-    const int64_t p = base + l;
-    const bool in = p < p1;
-    const bool valid = in && pair_valid(p, T, E, token, expert);
-    const int e = valid ? expert[p] : 0;
-    uint64_t m = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t bb = __ballot(bit);
-      m &= bit ? bb : ~bb;
+  // groups of 64 pairs are taken kScatBatch at a time, their expert, token
+  // and score loaded before the first is ranked
+  for (int64_t base0 = p0; base0 < p1; base0 += kScatBatch * kWave) {
+    int ev[kScatBatch], tv[kScatBatch];
+    float sv[kScatBatch];
+#pragma unroll
+    for (int u = 0; u < kScatBatch; ++u) {
+      const int64_t p = base0 + u * kWave + l;
+      const bool in = p < p1;
+      ev[u] = in ? expert[p] : -1;
+      tv[u] = in ? token[p] : -1;
+      sv[u] = (in && keys) ? score[p] : 0.f;
     }
-    const int rank = __popcll(m & lt_mask);
-    const int dst = valid ? run[e] + rank : 0;
-    // every lane has read its expert's running offset before the group
-    // leader advances it (lockstep within the wave)
-    __builtin_amdgcn_wave_barrier();
-    if (valid) {
-      cand[dst] = (int32_t)p;
-      if (keys) keys[dst] = __float_as_uint(score[p]);
-      if (keep_all) pos[p] = dst;
-      if (rank == 0) run[e] += __popcll(m);
-    } else if (in) {
-      pos[p] = -1;
+#pragma unroll
+    for (int u = 0; u < kScatBatch; ++u) {
+      const int64_t base = base0 + u * kWave;
+      if (base >= p1) break;
+      const int64_t p = base + l;
+      const bool in = p < p1;
+      const bool valid = in && ev[u] >= 0 && ev[u] < E && tv[u] >= 0 && tv[u] < T;
+      const int e = valid ? ev[u] : 0;
+      uint64_t m = __ballot(valid);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
+      }
+      const int rank = __popcll(m & lt_mask);
+      const int dst = valid ? run[e] + rank : 0;
+      // every lane has read its expert's running offset before the group
+      // leader advances it (lockstep within the wave)
+      __builtin_amdgcn_wave_barrier();
+      if (valid) {
+        cand[dst] = (int32_t)p;
+        if (keys) keys[dst] = __float_as_uint(sv[u]);
+        if (keep_all) pos[p] = dst;
+        if (rank == 0) run[e] += __popcll(m);
+      } else if (in) {
+        pos[p] = -1;
+      }
+      __builtin_amdgcn_wave_barrier();
     }
-    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -266,10 +295,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const int32_t* __restric
   const int o = offsets[e];
   const int m = offsets[e + 1] - o;
   const int tid = threadIdx.x;
-  __shared__ int hist[256];
+  // two histograms and two result slots, alternating between radix passes,
+  // so that a pass needs two barriers (after the counts, after the search)
+  __shared__ int hist[2][256];
   __shared__ int lds[kSelThreads / kWave + 1];
-  __shared__ uint32_t sh_prefix;
-  __shared__ int sh_rank;
+  __shared__ uint32_t sh_prefix[2];
+  __shared__ int sh_rank[2];
   auto id_of = [&](int c) -> int { return cand ? cand[c] : c; };
 
   if (m >= n) {
@@ -296,20 +327,24 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const int32_t* __restric
   }
   uint32_t prefix = 0, pmask = 0;
   int r = m;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
+  if (tid < 256) hist[0][tid] = 0;
+  __syncthreads();
+  for (int shift = 24, buf = 0; shift >= 0; shift -= 8, buf ^= 1) {
+    int* h = hist[buf];
+    // the other histogram was last read before the previous pass's second
+    // barrier: clear it for the next pass
+    if (tid < 256) hist[buf ^ 1][tid] = 0;
     if (in_regs) {
 #pragma unroll
       for (int j = 0; j < kSelRegKeys; ++j) {
         const uint32_t k = kr[j];
         if (tid + j * kSelThreads < n && (k & pmask) == prefix)
-          atomicAdd(&hist[(k >> shift) & 255u], 1);
+          atomicAdd(&h[(k >> shift) & 255u], 1);
       }
     } else {
       for (int i = tid; i < n; i += kSelThreads) {
         const uint32_t k = keys[c0 + i];
-        if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
+        if ((k & pmask) == prefix) atomicAdd(&h[(k >> shift) & 255u], 1);
       }
     }
     __syncthreads();
@@ -319,28 +354,29 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const int32_t* __restric
       int local = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        c[j] = hist[255 - 4 * tid - j];
+        c[j] = h[255 - 4 * tid - j];
         local += c[j];
       }
       int before = wave_incl_scan(local) - local;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (before < r && before + c[j] >= r) {
-          sh_prefix = prefix | ((uint32_t)(255 - 4 * tid - j) << shift);
-          sh_rank = r - before;
+          sh_prefix[buf] = prefix | ((uint32_t)(255 - 4 * tid - j) << shift);
+          sh_rank[buf] = r - before;
         }
         before += c[j];
       }
     }
     __syncthreads();
-    prefix = sh_prefix;
-    r = sh_rank;
+    prefix = sh_prefix[buf];
+    r = sh_rank[buf];
     pmask |= 0xffu << shift;
-    __syncthreads();
   }
-  // keep keys above the threshold, and the first r keys equal to it
+  // keep keys above the threshold, and the first r keys equal to it: one
+  // block scan of the packed counts (greater << 16 | equal, each < 2^16 per
+  // round); a kept key's slot is (greater before) + min(equal before, r)
   const uint32_t K = prefix;
-  int eq_carry = 0, keep_carry = 0;
+  int eq_carry = 0, gt_carry = 0;
   for (int base = 0; base < n; base += kSelThreads) {
     const int i = base + tid;
     const bool valid = i < n;
@@ -355,16 +391,18 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const int32_t* __restric
     const int eq = (valid && k == K) ? 1 : 0;
     const int gt = (valid && k > K) ? 1 : 0;
     int tot;
-    const int eq_before = block_excl_scan<kSelThreads>(eq, lds, &tot) + eq_carry;
-    eq_carry += tot;
-    const int keep = (gt || (eq && eq_before < r)) ? 1 : 0;
-    const int kp_before = block_excl_scan<kSelThreads>(keep, lds, &tot) + keep_carry;
-    keep_carry += tot;
+    const int ex = block_excl_scan<kSelThreads>((gt << 16) | eq, lds, &tot);
+    const int eq_before = eq_carry + (ex & 0xffff);
+    const int gt_before = gt_carry + (ex >> 16);
+    eq_carry += tot & 0xffff;
+    gt_carry += tot >> 16;
+    const bool keep = gt || (eq && eq_before < r);
     if (valid) {
       const int id = id_of(c0 + i);
       if (keep) {
-        kept[o + kp_before] = id;
-        pos[id] = o + kp_before;
+        const int slot = gt_before + min(eq_before, r);
+        kept[o + slot] = id;
+        pos[id] = o + slot;
       } else {
         pos[id] = -1;
       }
@@ -407,7 +445,7 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s) {
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s) {
   const int nblk = bucket_blocks(a.N);
   const int chunk = bucket_chunk(a.N);
-  if (nblk > kRowChunks * kWave) return hipErrorInvalidValue;
+  if (nblk > kScanTile) return hipErrorInvalidValue;
   if (a.N > 0) {
     LRM_LAUNCH(nblk, 256, a.E * sizeof(int), s, k_bucket_count)(a.N, a.T, a.E, chunk, a.token,
                                                         a.expert, a.blkcnt, a.blkerr, a.tok_off);
