@@ -130,16 +130,17 @@ __global__ __launch_bounds__(kSelThreads) void k_bucket_scan(int nblk, int E,
                                                              uint32_t* __restrict__ err,
                                                              int32_t* __restrict__ mt_off,
                                                              int mt_bm) {
-  LRM_DYN_SHARED(int, counts);  // [E]
+  LRM_DYN_SHARED(int, counts);  // [2E]: counts, then kept counts min(quota, count)
   __shared__ int lds[kSelThreads / kWave + 1];
   __shared__ uint32_t eor;
   if (threadIdx.x == 0) eor = 0u;
-  __syncthreads();
-  {
-    uint32_t bad = 0u;
-    for (int b = threadIdx.x; b < nblk; b += kSelThreads) bad |= blkerr[b];
-    if (bad) atomicOr(&eor, bad);
-  }
+  // the error words, the quotas and the first round of counts are all
+  // requested before any of them is waited for
+  uint32_t bad = 0u;
+  for (int b = threadIdx.x; b < nblk; b += kSelThreads) bad |= blkerr[b];
+  int* mcount = counts + E;
+  auto quota_of = [&](int e) { return quota ? max(quota[e], 0) : 0x7fffffff; };
+  const int q0 = threadIdx.x < E ? quota_of(threadIdx.x) : 0;
   const int w = threadIdx.x >> 6, l = lane_id();
   constexpr int NW = kSelThreads / kWave;
   constexpr int PER = kScanTile / kSelThreads;
@@ -160,6 +161,10 @@ __global__ __launch_bounds__(kSelThreads) void k_bucket_scan(int nblk, int E,
     }
   };
   if (E > 0) load_round(0);
+  if (threadIdx.x < E) mcount[threadIdx.x] = q0;
+  for (int e = threadIdx.x + kSelThreads; e < E; e += kSelThreads) mcount[e] = quota_of(e);
+  __syncthreads();  // eor and mcount initialised
+  if (bad) atomicOr(&eor, bad);
   for (int e0 = 0; e0 < E; e0 += R) {
     const int rows = min(R, E - e0);
 #pragma unroll
@@ -176,28 +181,19 @@ __global__ __launch_bounds__(kSelThreads) void k_bucket_scan(int nblk, int E,
         if (b < nblk) row[b] = run + incl - x;
         run += __shfl(incl, kWave - 1, kWave);
       }
-      if (l == 0) counts[e0 + r] = run;
+      if (l == 0) {
+        counts[e0 + r] = run;
+        mcount[e0 + r] = min(mcount[e0 + r], run);
+      }
     }
     __syncthreads();
   }
   __syncthreads();
   block_scan_array<kSelThreads>(E, [&](int e) { return counts[e]; }, cand_off, lds);
-  block_scan_array<kSelThreads>(
-      E,
-      [&](int e) {
-        const int n = counts[e];
-        return quota ? min(max(quota[e], 0), n) : n;
-      },
-      offsets, lds);
+  block_scan_array<kSelThreads>(E, [&](int e) { return mcount[e]; }, offsets, lds);
   if (mt_off) {
     block_scan_array<kSelThreads>(
-        E,
-        [&](int e) {
-          const int n = counts[e];
-          const int m = quota ? min(max(quota[e], 0), n) : n;
-          return (m + mt_bm - 1) / mt_bm;
-        },
-        mt_off, lds);
+        E, [&](int e) { return (mcount[e] + mt_bm - 1) / mt_bm; }, mt_off, lds);
   }
   if (threadIdx.x == 0) err[0] = eor;
 }
@@ -230,17 +226,14 @@ __global__ __launch_bounds__(64) void k_bucket_scatter(int N, int T, int E, int 
                                                        int32_t* __restrict__ pos, int keep_all) {
   LRM_DYN_SHARED(int, run);  // [E]
   const int l = lane_id();
-  for (int e = l; e < E; e += kWave) run[e] = cand_off[e] + blkcnt[(int64_t)e * gridDim.x + blockIdx.x];
-  __syncthreads();
-  const int nbits = (E > 1) ? 32 - __clz(E - 1) : 0;
   const int64_t p0 = (int64_t)blockIdx.x * chunk;
   const int64_t p1 = min<int64_t>(p0 + chunk, N);
-  const uint64_t lt_mask = (l == 0) ? 0ull : (~0ull >> (64 - l));
   // groups of 64 pairs are taken kScatBatch at a time, their expert, token
-  // and score loaded before the first is ranked
-  for (int64_t base0 = p0; base0 < p1; base0 += kScatBatch * kWave) {
-    int ev[kScatBatch], tv[kScatBatch];
-    float sv[kScatBatch];
+  // and score loaded before the first is ranked (the first batch before the
+  // running offsets are read)
+  int ev[kScatBatch], tv[kScatBatch];
+  float sv[kScatBatch];
+  auto load_batch = [&](int64_t base0) {
 #pragma unroll
     for (int u = 0; u < kScatBatch; ++u) {
       const int64_t p = base0 + u * kWave + l;
@@ -249,6 +242,14 @@ __global__ __launch_bounds__(64) void k_bucket_scatter(int N, int T, int E, int 
       tv[u] = in ? token[p] : -1;
       sv[u] = (in && keys) ? score[p] : 0.f;
     }
+  };
+  load_batch(p0);
+  for (int e = l; e < E; e += kWave) run[e] = cand_off[e] + blkcnt[(int64_t)e * gridDim.x + blockIdx.x];
+  __syncthreads();
+  const int nbits = (E > 1) ? 32 - __clz(E - 1) : 0;
+  const uint64_t lt_mask = (l == 0) ? 0ull : (~0ull >> (64 - l));
+  for (int64_t base0 = p0; base0 < p1; base0 += kScatBatch * kWave) {
+    if (base0 != p0) load_batch(base0);
 #pragma unroll
     for (int u = 0; u < kScatBatch; ++u) {
       const int64_t base = base0 + u * kWave;
@@ -320,10 +321,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const int32_t* __restric
   // once into registers
   const bool in_regs = n <= kSelRegKeys * kSelThreads;
   uint32_t kr[kSelRegKeys];
+  int idr[kSelRegKeys];  // their ids, requested with the keys
 #pragma unroll
   for (int j = 0; j < kSelRegKeys; ++j) {
     const int i = tid + j * kSelThreads;
-    kr[j] = (in_regs && i < n) ? keys[c0 + i] : 0u;
+    const bool ld = in_regs && i < n;
+    kr[j] = ld ? keys[c0 + i] : 0u;
+    idr[j] = ld ? id_of(c0 + i) : 0;
   }
   uint32_t prefix = 0, pmask = 0;
   int r = m;
@@ -381,12 +385,17 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const int32_t* __restric
     const int i = base + tid;
     const bool valid = i < n;
     uint32_t k = 0u;
+    int id = 0;
     if (in_regs) {
 #pragma unroll
       for (int j = 0; j < kSelRegKeys; ++j)
-        if (base == j * kSelThreads) k = kr[j];
+        if (base == j * kSelThreads) {
+          k = kr[j];
+          id = idr[j];
+        }
     } else if (valid) {
       k = keys[c0 + i];
+      id = id_of(c0 + i);
     }
     const int eq = (valid && k == K) ? 1 : 0;
     const int gt = (valid && k > K) ? 1 : 0;
@@ -398,7 +407,6 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const int32_t* __restric
     gt_carry += tot >> 16;
     const bool keep = gt || (eq && eq_before < r);
     if (valid) {
-      const int id = id_of(c0 + i);
       if (keep) {
         const int slot = gt_before + min(eq_before, r);
         kept[o + slot] = id;
@@ -451,7 +459,7 @@ hipError_t launch_bucket(const BucketArgs& a, hipStream_t s) {
                                                         a.expert, a.blkcnt, a.blkerr, a.tok_off);
   }
   if (a.mt_off && a.mt_bm < 1) return hipErrorInvalidValue;
-  LRM_LAUNCH(1, kSelThreads, a.E * sizeof(int), s, k_bucket_scan)(nblk, a.E, a.blkcnt, a.quota,
+  LRM_LAUNCH(1, kSelThreads, 2 * a.E * sizeof(int), s, k_bucket_scan)(nblk, a.E, a.blkcnt, a.quota,
                                                           a.cand_off, a.offsets, a.blkerr,
                                                           a.err, a.mt_off, a.mt_bm);
   if (a.N > 0) {
