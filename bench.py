@@ -15,6 +15,11 @@ counter runs when they match the kernel source; the `cpu_baseline` block
 times the fp64 CPU oracle on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu] [--full]
+
+The HBM-traffic record the `roofline.traffic` field reads is written on any
+host, without a GPU, from two profiler passes over `--copy-probe` runs:
+
+    python bench.py --record-traffic FETCH_DIR WRITE_DIR [--config 2]
 """
 
 from __future__ import annotations
@@ -56,7 +61,114 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 512 MiB device copy (a known-size kernel that "
                          "calibrates the HBM byte counters of a profiler pass)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/hbm_traffic.json from the output folders of a "
+                         "rocprofv3 --pmc FETCH_SIZE and a --pmc WRITE_SIZE pass over "
+                         "`bench.py --no-cpu --copy-probe` (no GPU needed)")
     return ap.parse_args()
+
+
+COPY_KIB = 512 * 1024  # bytes moved each way by one copy of copy_probe, in KiB
+TRAFFIC_PATH = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+GEMM_SRC = os.path.join(ROOT, "pruned_expert_backward_lrm_amd", "csrc", "k_gemm.hip")
+
+
+def gemm_source_sha():
+    import hashlib
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def workload_name(spec, T, E, k, shape, variant=None):
+    return f"{spec['name']}{'-' + variant if variant else ''}: {shape} E={E} top-{k} zipf={spec['zipf']}"
+
+
+def gemm_work(E, Me, d_in, d_out, b):
+    """Algorithmic bytes and flops of the two grouped-GEMM launches of a
+    linear layer call with kept counts Me: the dW launch writes every
+    expert's fp32 dW and reads the packed rows once; the dX launch reads W of
+    the active experts and the packed G rows, and writes the fp32 dX rows."""
+    M, act = int(np.sum(Me)), int(np.count_nonzero(Me))
+    return {
+        "dW": dict(bytes=E * d_out * d_in * 4 + M * (d_in + d_out) * b, flops=2.0 * M * d_in * d_out),
+        "dX": dict(bytes=act * d_out * d_in * b + M * d_out * b + M * d_in * 4,
+                   flops=2.0 * M * d_in * d_out),
+    }
+
+
+def record_traffic(fetch_dir, write_dir, cfg):
+    """profiles/hbm_traffic.json from two counter passes: per GEMM launch, the
+    average FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by what the same
+    counter reads for the three 512 MiB copies of --copy-probe."""
+    import csv
+    import glob
+
+    from pruned_expert_backward_lrm_amd import synth
+    spec = synth.CONFIGS[cfg]
+    if spec["kind"] != "linear":
+        raise SystemExit("--record-traffic covers the linear workloads (one dW and one dX launch)")
+    r = synth.make_routing(spec["T"], spec["E"], spec["k"], spec["zipf"], "cfg", cfg,
+                           local=spec.get("local"))
+    q = synth._quotas(cfg, r, None)["quota"]
+    Me = np.minimum(np.maximum(q, 0), r.counts).astype(np.int64)
+    b = torch.tensor([], dtype=synth.torch_dtype(spec["dtype"])).element_size()
+    work = gemm_work(r.E, Me, spec["d_in"], spec["d_out"], b)
+    workload = workload_name(spec, r.T, r.E, r.k,
+                             f"T={r.T} d_in={spec['d_in']} d_out={spec['d_out']}")
+    per, scale, names = {"dW": {}, "dX": {}}, {}, {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [row for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"),
+                                       recursive=True)
+                for row in csv.DictReader(open(f)) if row["Counter_Name"] == counter]
+        rows.sort(key=lambda row: int(row["Dispatch_Id"]))
+        copies = [float(row["Counter_Value"]) for row in rows
+                  if row["Kernel_Name"] == "__amd_rocclr_copyBuffer"][:3]
+        if len(copies) != 3:
+            raise SystemExit(f"{d}: no --copy-probe copies found for {counter}")
+        scale[counter] = float(np.mean(copies)) / COPY_KIB
+        for kind, tail in (("dW", "false>(lrm::GemmPlan)"), ("dX", "true>(lrm::GemmPlan)")):
+            vals = [float(row["Counter_Value"]) for row in rows
+                    if "k_gemm_stream<" in row["Kernel_Name"] and row["Kernel_Name"].endswith(tail)]
+            if not vals:
+                raise SystemExit(f"{d}: no {kind} grouped-GEMM dispatches")
+            names[kind] = next(row["Kernel_Name"] for row in rows
+                               if "k_gemm_stream<" in row["Kernel_Name"]
+                               and row["Kernel_Name"].endswith(tail))
+            per[kind][counter] = (float(np.mean(vals)), len(vals))
+    sha = gemm_source_sha()
+    kernels = []
+    for kind in ("dW", "dX"):
+        fk, n = per[kind]["FETCH_SIZE"]
+        wk, _ = per[kind]["WRITE_SIZE"]
+        fb = fk / scale["FETCH_SIZE"] * 1024
+        wb = wk / scale["WRITE_SIZE"] * 1024
+        alg = work[kind]["bytes"]
+        kernels.append({"kernel": f"k_gemm_stream<{kind}>", "profiler_name": names[kind],
+                        "workload": workload, "source_sha256": sha, "dispatches": n,
+                        "fetch_kib_raw": round(fk, 1), "write_kib_raw": round(wk, 1),
+                        "fetch_bytes": int(round(fb)), "write_bytes": int(round(wb)),
+                        "hbm_bytes": int(round(fb + wb)), "algorithmic_bytes": int(alg),
+                        "traffic_over_algorithmic": round((fb + wb) / alg, 3)})
+    rec = {
+        "note": ("HBM bytes per launch of the grouped-GEMM kernels, from two rocprofv3 --pmc "
+                 "passes (FETCH_SIZE, WRITE_SIZE, KiB per dispatch) scaled by what the same "
+                 f"counters read for a 512 MiB device copy (FETCH_SIZE reads "
+                 f"{scale['FETCH_SIZE']:.4f}, WRITE_SIZE {scale['WRITE_SIZE']:.4f} of the true "
+                 "bytes). source_sha256 is the hash of csrc/k_gemm.hip the counters were "
+                 "taken on."),
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d " + fetch_dir
+            + f" -o run -- python bench.py --config {cfg} --no-cpu --copy-probe --steps 5 --warmup 2",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d " + write_dir
+            + f" -o run -- python bench.py --config {cfg} --no-cpu --copy-probe --steps 5 --warmup 2",
+            f"python bench.py --config {cfg} --record-traffic {fetch_dir} {write_dir}",
+        ],
+        "kernels": kernels,
+    }
+    with open(TRAFFIC_PATH, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
 
 
 def copy_probe(dev):
@@ -203,13 +315,12 @@ def gemm_kernels(W, steps, warmup):
     dXp = torch.empty(max(M, 1), di, dtype=torch.float32, device=dev)
     ws = torch.empty(1 << 16, dtype=torch.uint8, device=dev)
     Me = np.diff(offsets.cpu().numpy().astype(np.int64))
-    act = int(np.count_nonzero(Me))
-    b = p["X"].element_size()
+    work = gemm_work(r.E, Me, di, do, p["X"].element_size())
     runs = {
         "dW": (lambda: L.lrm_grouped_bwd(r.E, offsets, M, Gp, Xp, p["W"], di, do, dW, None, ws=ws),
-               dict(bytes=r.E * do * di * 4 + M * (di + do) * b, flops=2.0 * M * di * do)),
+               work["dW"]),
         "dX": (lambda: L.lrm_grouped_bwd(r.E, offsets, M, Gp, Xp, p["W"], di, do, None, dXp, ws=ws),
-               dict(bytes=act * do * di * b + M * do * b + M * di * 4, flops=2.0 * M * di * do)),
+               work["dX"]),
     }
     res = {}
     for name, (fn, work) in runs.items():
@@ -230,14 +341,10 @@ def traffic_of(kernel, workload):
     """HBM bytes per launch from the committed counter runs (profiles/
     hbm_traffic.json), or None when they were taken on another workload or on
     another version of the kernel source."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-    src = os.path.join(ROOT, "pruned_expert_backward_lrm_amd", "csrc", "k_gemm.hip")
     try:
-        with open(path) as f:
+        with open(TRAFFIC_PATH) as f:
             rec = json.load(f)
-        with open(src, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = gemm_source_sha()
     except (OSError, ValueError):
         return None
     for e in rec.get("kernels", []):
@@ -294,6 +401,9 @@ def cpu_baseline(p, M, Me):
 
 def main():
     a = parse()
+    if a.record_traffic:
+        record_traffic(a.record_traffic[0], a.record_traffic[1], a.config)
+        return
     if a.gpus != 1:
         log("bench.py: this build runs on exactly one GPU (one GPU's share of the experts); "
             "--gpus must be 1")
@@ -329,7 +439,7 @@ def main():
         shape = f"T={r.T} d_in={p['d_in']} d_out={p['d_out']}"
     else:
         shape = f"T={r.T} H={p['H']} I={p['I']}"
-    workload = f"{spec['name']}{'-' + a.variant if a.variant else ''}: {shape} E={r.E} top-{r.k} zipf={spec['zipf']}"
+    workload = workload_name(spec, r.T, r.E, r.k, shape, a.variant)
     kernels = None
     if p["kind"] == "linear":
         # the dominant kernel: the longer of the two GEMM launches, timed alone
