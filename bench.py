@@ -16,6 +16,10 @@ times the fp64 CPU oracle on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu] [--full]
 
+`--sweep` instead prints one JSON line of the keep-ratio sweep: the fused call
+with every quota at floor(r * n_e) for r in 0.1, 0.25, 0.5, 0.75, 1.0 (all
+projections alike), and the unpruned call, on the chosen workload.
+
 The HBM-traffic record the `roofline.traffic` field reads is written on any
 host, without a GPU, from two profiler passes over `--copy-probe` runs:
 
@@ -61,6 +65,8 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 512 MiB device copy (a known-size kernel that "
                          "calibrates the HBM byte counters of a profiler pass)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="keep-ratio sweep (quota = floor(r n_e)) instead of the bench line")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/hbm_traffic.json from the output folders of a "
                          "rocprofv3 --pmc FETCH_SIZE and a --pmc WRITE_SIZE pass over "
@@ -353,6 +359,61 @@ def traffic_of(kernel, workload):
     return None
 
 
+def copy_gbs(dev, reps=10):
+    """Measured device-copy bandwidth (read + write bytes of a 512 MiB copy
+    per second): the practical ceiling of a streaming kernel on this GPU."""
+    n = 512 * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2 * n * 4 / (ms * 1e-3) / 1e9
+
+
+def attainable_tflops(ai, peak_tf):
+    """min(MFMA peak, arithmetic intensity x HBM peak), in TFLOP/s."""
+    return min(peak_tf, ai * PEAK_HBM_GBS / 1000.0)
+
+
+def keep_sweep(L, synth, p, dev, steps, warmup, cfg):
+    """Fused-call time with every quota at floor(r n_e), r in RATIOS, and the
+    unpruned (keep-all) call, on one workload."""
+    ratios = ((1, 10), (1, 4), (1, 2), (3, 4), (1, 1))
+    r = p["routing"]
+    W = Workload(L, p, dev)
+    points = []
+    for num, den in ratios:
+        q = ((num * r.counts.astype(np.int64)) // den).astype(np.int32)
+        if p["kind"] == "linear":
+            pb = L.linear_problem(W.pairs, p["X"], p["X_rows"], p["G"], p["G_rows"], p["W"], q)
+        else:
+            pb = L.swiglu_problem(W.pairs, p["X"], "token", p["G"], "token", p["A"], p["B"],
+                                  p["W_gate"], p["W_up"], p["W_down"], q, q, q)
+        ws = torch.empty(L.lrm_workspace_size(pb), dtype=torch.uint8, device=dev)
+        fn = lambda: L.lrm_expert_backward(pb, W.out, ws=ws)  # noqa: E731
+        t = time_loop(fn, steps, warmup)
+        M = int(W.out["offsets"][-1].item())
+        points.append({"r": num / den, "kept_pairs": M, "kept_fraction": round(M / r.N, 4),
+                       "ms": round(t * 1e3, 4), "kept_pairs_per_s": round(M / t, 1)})
+        del pb, ws
+    t_full = time_loop(W.step_full, steps, warmup)
+    for pt in points:
+        pt["time_over_unpruned"] = round(pt["ms"] / (t_full * 1e3), 4)
+    spec = synth.CONFIGS[cfg]
+    return {"metric": "keep-ratio sweep of the fused call", "config": {"workload": spec["name"],
+            "pairs": r.N}, "unit": "ms", "steps": steps, "warmup": warmup,
+            "unpruned_ms": round(t_full * 1e3, 4), "points": points}
+
+
 def time_loop(fn, steps, warmup):
     for _ in range(warmup):
         fn()
@@ -416,6 +477,10 @@ def main():
         copy_probe(dev)
     log(f"bench: generating config {a.config}")
     p = synth.make_config(a.config, device=dev, variant=a.variant)
+    if a.sweep:
+        log("bench: keep-ratio sweep")
+        print(json.dumps(keep_sweep(L, synth, p, dev, a.steps, a.warmup, a.config)), flush=True)
+        return
     W = Workload(L, p, dev)
     r = p["routing"]
     log("bench: timing the pruned backward")
@@ -462,6 +527,8 @@ def main():
                 "unit": "TFLOP/s", "frac": round(k_tf / peak_tf, 4), "traffic": traffic}
     roof["kernel"] = kname
     mem_stages = [s for s in W.stages if s not in W.gemm_stages]
+    log("bench: measuring device-copy bandwidth")
+    cgbs = copy_gbs(dev)
     sc = [s for s in W.stages if s.startswith("score") or s.startswith("compact")]
     line = {
         "metric": METRIC,
@@ -481,14 +548,21 @@ def main():
         "roofline": roof,
         "gemm_kernels": ({k: {"ms": round(v["ms"], 4), "bytes": v["bytes"], "flops": v["flops"],
                               "gbs": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1),
-                              "tflops": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 2)}
+                              "tflops": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 2),
+                              "pct_attainable": round(
+                                  100 * v["flops"] / (v["ms"] * 1e-3) / 1e12
+                                  / attainable_tflops(v["flops"] / v["bytes"], peak_tf), 2)}
                           for k, v in kernels.items()} if kernels else None),
         "grouped_gemm": {"ms": round(t_g * 1e3, 4), "tflops": round(tflops, 2),
                          "pct_mfma_peak": round(100 * tflops / peak_tf, 2),
+                         "pct_attainable": round(100 * tflops / attainable_tflops(ai, peak_tf), 2),
                          "gbs": round(gbs, 1), "flops": flops, "bytes": gbytes,
                          "arith_intensity": round(ai, 1)},
         "stages_ms": {s: round(v, 4) for s, v in per.items()},
         "stages_gbs": {s: round(work[s]["bytes"] / (per[s] * 1e-3) / 1e9, 1) for s in mem_stages},
+        "copy_gbs": round(cgbs, 1),
+        "stages_frac_of_copy": {s: round(work[s]["bytes"] / (per[s] * 1e-3) / 1e9 / cgbs, 3)
+                                for s in mem_stages},
         "score_compact_gbs": round(sum(work[s]["bytes"] for s in sc)
                                    / (sum(per[s] for s in sc) * 1e-3) / 1e9, 1),
         "unpruned_ms_per_step": round(ms_full, 4) if ms_full else None,
