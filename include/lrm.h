@@ -69,9 +69,11 @@ typedef enum lrm_status {
   LRM_ERR_ALIGN = 5,       /* a pointer or leading dimension breaks 16-byte row alignment */
   LRM_ERR_QUOTA = 6,       /* a negative quota */
   LRM_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than required */
-  LRM_ERR_INDEX = 8,       /* device-detected: expert or token index out of range / order */
+  LRM_ERR_INDEX = 8,       /* device-detected: expert or token index out of range / order,
+                              or a replica assignment that does not match the kept counts */
   LRM_ERR_HIP = 9,         /* a HIP runtime call or kernel launch failed */
-  LRM_ERR_UNSUPPORTED = 10 /* valid request outside what this library implements */
+  LRM_ERR_UNSUPPORTED = 10, /* valid request outside what this library implements */
+  LRM_ERR_INFEASIBLE = 11  /* kept pairs that no replica (or no capacity) can take */
 } lrm_status;
 
 typedef enum lrm_dtype { LRM_F32 = 0, LRM_BF16 = 1 } lrm_dtype;
@@ -189,6 +191,58 @@ lrm_status lrm_unpermute(const lrm_pairs* pairs, const int32_t* pos, const float
                          void* stream);
 size_t lrm_unpermute_workspace_size(const lrm_pairs* pairs);
 
+/* ----------------------------------------- redistribution onto replicas */
+
+/* Redistribution of the kept pairs over the copies of their expert (page 1,
+ * section "Что делает LRMoE: полный прямой проход, обрезанный обратный",
+ * bullet "Перераспределение"; page 2, same section, bullet
+ * "Redistribution"): an integer assignment of each expert's kept pairs to
+ * the GPUs holding a replica of it, minimising the peak per-GPU load; no
+ * replica is created.  HOST function: it enqueues nothing and touches no
+ * device memory (a controller-side step on E x G numbers).
+ *   kept:    host [E], M_e >= 0 kept pairs of expert e (offsets[e+1] -
+ *            offsets[e] of a selection).
+ *   replica: host [E][G] uint8, nonzero where GPU g holds a copy of expert e.
+ *   base:    host [G] load already on GPU g (pairs, >= 0), or NULL for zeros.
+ *   cap:     host [G] most pairs GPU g may take (>= 0), or NULL for no limit.
+ *   assign:  host [E][G] int32 output x[e][g] >= 0, zero where there is no
+ *            replica, each row summing to kept[e].
+ *   peak:    host output, max over g of base[g] + sum_e x[e][g], the minimum
+ *            over all such assignments (exact).
+ * Load is counted in pairs: the experts of one layer have equal shapes, so a
+ * kept pair costs the same work on any replica.  The optimum is unique, the
+ * assignment in general is not; this one is deterministic.
+ * host_ws: host scratch of lrm_redistribute_workspace_size(E, G) bytes.
+ * E in 1..4096, G in 1..1024.  LRM_ERR_INFEASIBLE if an expert with kept
+ * pairs has no replica or the capacities cannot hold every kept pair (assign
+ * and peak are then not written). */
+lrm_status lrm_redistribute(int32_t E, int32_t G, const int32_t* kept, const uint8_t* replica,
+                            const int64_t* base, const int64_t* cap, int32_t* assign,
+                            int64_t* peak, void* host_ws, size_t host_ws_bytes);
+size_t lrm_redistribute_workspace_size(int32_t E, int32_t G);
+
+/* Receiver-major layout of the packed rows (page 1, bullet "Физическое
+ * уплотнение": dense blocks per receiver and expert) for an assignment of
+ * lrm_redistribute copied to the device:
+ *   offsets:  device [E+1] of a selection (expert e's rows offsets[e] ..).
+ *   assign:   device [E][G] int32 x[e][g].
+ *   send_off: device [G+1] output, first row of receiver g's block.
+ *   blk_off:  device [G][E+1] output, first row of expert e inside receiver
+ *             g's block, relative to send_off[g] (blk_off[g][E] = its rows).
+ *   dst:      device [max_rows] output, dst[m] = receiver-major row of packed
+ *             row m, for m < min(offsets[E], max_rows); later rows untouched.
+ * Receiver g's block holds experts 0..E-1 in order, x[e][g] rows each;
+ * expert e's rows, in packed order, go to its replicas in ascending g.
+ * ws: device scratch of lrm_receiver_layout_workspace_size(E, G) bytes; its
+ * first word is the device error word: lrm_check_device_errors(ws) reports
+ * LRM_ERR_INDEX if some x[e][g] < 0 or a row of assign does not sum to
+ * offsets[e+1] - offsets[e] (dst is then unspecified). */
+lrm_status lrm_receiver_layout(int32_t E, int32_t G, const int32_t* offsets,
+                               const int32_t* assign, int32_t max_rows, int32_t* send_off,
+                               int32_t* blk_off, int32_t* dst, void* ws, size_t ws_bytes,
+                               void* stream);
+size_t lrm_receiver_layout_workspace_size(int32_t E, int32_t G);
+
 /* ------------------------------------------------------- the fused call */
 
 typedef struct lrm_problem {
@@ -283,9 +337,10 @@ size_t lrm_workspace_size(const lrm_problem* prob);
 int64_t lrm_max_kept(int32_t N, int32_t E, const int32_t* quota);
 
 /* Synchronises the stream, then reads the device error word at the start of
- * a workspace used by lrm_select or lrm_expert_backward: LRM_OK, or
- * LRM_ERR_INDEX if an expert index was out of range or token[] was out of
- * range or decreasing (such pairs are treated as absent), and clears it. */
+ * a workspace used by lrm_select, lrm_expert_backward or lrm_receiver_layout:
+ * LRM_OK, or LRM_ERR_INDEX if an expert index was out of range or token[]
+ * was out of range or decreasing (such pairs are treated as absent), or a
+ * replica assignment did not match the kept counts, and clears it. */
 lrm_status lrm_check_device_errors(void* ws, void* stream);
 
 /* Static description of a status code. */

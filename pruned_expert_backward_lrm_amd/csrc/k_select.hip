@@ -27,51 +27,6 @@ constexpr int kSelRegKeys = 4;  // keys per thread held in registers by k_select
 constexpr int kScanTile = 8192;  // block counts staged in LDS per round by k_bucket_scan
 constexpr int kScatBatch = 8;   // 64-pair groups per wave loaded ahead by k_bucket_scatter
 
-// Exclusive scan of one int per thread over an NT-thread block.  lds must hold
-// NT/64 + 1 ints.  Returns the exclusive prefix; *total gets the block sum.
-template <int NT>
-__device__ __forceinline__ int block_excl_scan(int v, int* lds, int* total) {
-  constexpr int NW = NT / kWave;
-  const int incl = wave_incl_scan(v);
-  const int w = threadIdx.x >> 6, l = lane_id();
-  if (l == kWave - 1) lds[w] = incl;
-  __syncthreads();
-  if (threadIdx.x < kWave) {
-    const int t = (l < NW) ? lds[l] : 0;
-    const int ti = wave_incl_scan(t);
-    if (l < NW) lds[l] = ti - t;
-    if (l == NW - 1) lds[NW] = ti;
-  }
-  __syncthreads();
-  const int res = lds[w] + incl - v;
-  *total = lds[NW];
-  __syncthreads();
-  return res;
-}
-
-// Exclusive scan of n values (n <= 4 * NT) given by get(i) into out[0..n],
-// out[n] = total.  Values are handled in contiguous runs of 4 per thread.
-template <int NT, typename F>
-__device__ void block_scan_array(int n, F get, int32_t* out, int* lds) {
-  const int per = 4;
-  const int i0 = threadIdx.x * per;
-  int v[per];
-  int local = 0;
-#pragma unroll
-  for (int j = 0; j < per; ++j) {
-    v[j] = (i0 + j < n) ? get(i0 + j) : 0;
-    local += v[j];
-  }
-  int total;
-  int run = block_excl_scan<NT>(local, lds, &total);
-#pragma unroll
-  for (int j = 0; j < per; ++j) {
-    if (i0 + j < n) out[i0 + j] = run;
-    run += v[j];
-  }
-  if (threadIdx.x == 0) out[n] = total;
-}
-
 // tok_off[t] for the tokens t that start at pair p (p in [0, N]): the first
 // pair whose token is >= t.
 __device__ __forceinline__ void token_offsets_at(int64_t p, int N, int T,

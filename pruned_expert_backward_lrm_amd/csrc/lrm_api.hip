@@ -203,9 +203,10 @@ const char* lrm_status_string(lrm_status s) {
     case LRM_ERR_ALIGN: return "rows are not 16-byte aligned";
     case LRM_ERR_QUOTA: return "negative quota";
     case LRM_ERR_WORKSPACE: return "workspace missing or too small";
-    case LRM_ERR_INDEX: return "expert or token index out of range or out of order";
+    case LRM_ERR_INDEX: return "expert or token index out of range or out of order, or an assignment not matching the kept counts";
     case LRM_ERR_HIP: return "HIP runtime error";
     case LRM_ERR_UNSUPPORTED: return "unsupported request";
+    case LRM_ERR_INFEASIBLE: return "kept pairs that no replica or capacity can take";
   }
   return "unknown status";
 }

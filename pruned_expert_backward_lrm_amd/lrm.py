@@ -24,7 +24,9 @@ _lib = C.CDLL(LIB_PATH)
 # ------------------------------------------------------------------ constants
 LRM_OK = 0
 STATUS_NAMES = ["OK", "ERR_NULL", "ERR_SHAPE", "ERR_DTYPE", "ERR_LAYOUT", "ERR_ALIGN",
-                "ERR_QUOTA", "ERR_WORKSPACE", "ERR_INDEX", "ERR_HIP", "ERR_UNSUPPORTED"]
+                "ERR_QUOTA", "ERR_WORKSPACE", "ERR_INDEX", "ERR_HIP", "ERR_UNSUPPORTED",
+                "ERR_INFEASIBLE"]
+LRM_ERR_INDEX, LRM_ERR_INFEASIBLE = 8, 11
 LRM_F32, LRM_BF16 = 0, 1
 LRM_ROWS_TOKEN, LRM_ROWS_PAIR = 0, 1
 LRM_LINEAR, LRM_SWIGLU = 0, 1
@@ -94,6 +96,10 @@ _sigs = {
                                              _SZ, _P, C.POINTER(C.c_void_p), _I32]),
     "lrm_workspace_size": (_SZ, [C.POINTER(lrm_problem)]),
     "lrm_check_device_errors": (C.c_int, [_P, _P]),
+    "lrm_redistribute": (C.c_int, [_I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ]),
+    "lrm_redistribute_workspace_size": (_SZ, [_I32, _I32]),
+    "lrm_receiver_layout": (C.c_int, [_I32, _I32, _P, _P, _I32, _P, _P, _P, _P, _SZ, _P]),
+    "lrm_receiver_layout_workspace_size": (_SZ, [_I32, _I32]),
 }
 for _name, (_res, _args) in _sigs.items():
     _f = getattr(_lib, _name)
@@ -228,6 +234,40 @@ def lrm_unpermute(pairs: Pairs, pos, dXp, d_in: int, out_rows, dX, ws=None, stre
 def lrm_max_kept(N: int, quota) -> int:
     q = _quota_arr(quota)
     return int(_lib.lrm_max_kept(int(N), int(q.shape[0]), q.ctypes.data))
+
+
+def lrm_redistribute(kept, replica, base=None, cap=None):
+    """Host call: the peak-minimising integer assignment of each expert's kept
+    pairs to its replicas.  kept [E], replica [E][G] (bool), base/cap [G] or
+    None.  Returns (peak, assign int32 [E][G]) as NumPy."""
+    k = np.ascontiguousarray(np.asarray(kept, dtype=np.int32))
+    rep = np.ascontiguousarray(np.asarray(replica).astype(np.uint8))
+    E, G = rep.shape
+    b = None if base is None else np.ascontiguousarray(np.asarray(base, dtype=np.int64))
+    c = None if cap is None else np.ascontiguousarray(np.asarray(cap, dtype=np.int64))
+    assign = np.zeros((E, G), np.int32)
+    peak = np.zeros(1, np.int64)
+    ws = np.empty(max(int(_lib.lrm_redistribute_workspace_size(E, G)), 64), np.uint8)
+    _check(_lib.lrm_redistribute(E, G, _ptr(k), _ptr(rep), _ptr(b), _ptr(c), _ptr(assign),
+                                 _ptr(peak), _ptr(ws), ws.nbytes), "lrm_redistribute")
+    return int(peak[0]), assign
+
+
+def lrm_receiver_layout(offsets, assign, max_rows: int, ws=None, stream=None):
+    """Device call: receiver-major layout of the packed rows for a device
+    assignment [E][G].  Returns (send_off [G+1], blk_off [G][E+1], dst
+    [max_rows], ws) device int32 tensors."""
+    E, G = int(assign.shape[0]), int(assign.shape[1])
+    dev = offsets.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    send_off = torch.empty(G + 1, **i32)
+    blk_off = torch.empty(G, E + 1, **i32)
+    dst = torch.empty(max(int(max_rows), 1), **i32)
+    ws = _ws(_lib.lrm_receiver_layout_workspace_size(E, G), dev, ws)
+    _check(_lib.lrm_receiver_layout(E, G, _ptr(offsets), _ptr(assign), int(max_rows),
+                                    _ptr(send_off), _ptr(blk_off), _ptr(dst), _ptr(ws),
+                                    ws.numel(), _stream(stream)), "lrm_receiver_layout")
+    return send_off, blk_off, dst, ws
 
 
 def lrm_check_device_errors(ws, stream=None) -> int:

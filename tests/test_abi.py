@@ -38,8 +38,9 @@ def test_struct_layouts_match_header():
 
 
 def test_status_strings_and_version():
-    for s in range(11):
+    for s in range(12):
         assert L._lib.lrm_status_string(s)
+        assert L._lib.lrm_status_string(s) != b"unknown status"
     assert L._lib.lrm_status_string(999) == b"unknown status"
     assert L._lib.lrm_version() >= 100
 
@@ -159,3 +160,18 @@ def test_swiglu_workspace_sizes_from_quotas():
     assert same > 0 and second > 0 and same != second
     pb.A = _m(rows=L.LRM_ROWS_TOKEN, cols=32, ld=32)
     assert lib.lrm_workspace_size(C.byref(pb)) == 0
+
+
+def test_receiver_layout_validation_returns_before_launch():
+    lib = L._lib
+    d = C.c_void_p(0x4000)
+    assert lib.lrm_receiver_layout_workspace_size(0, 2) == 0
+    assert lib.lrm_receiver_layout_workspace_size(4, 1025) == 0
+    n = lib.lrm_receiver_layout_workspace_size(4, 2)
+    assert n >= 4 * 3 * 4
+    assert lib.lrm_receiver_layout(0, 2, d, d, 8, d, d, d, d, n, None) == 2
+    assert lib.lrm_receiver_layout(4, 2, None, d, 8, d, d, d, d, n, None) == 1
+    assert lib.lrm_receiver_layout(4, 2, d, d, 8, d, d, None, d, n, None) == 1
+    assert lib.lrm_receiver_layout(4, 2, d, d, 8, d, d, d, d, n - 1, None) == 7
+    assert lib.lrm_receiver_layout(4, 2, d, d, -1, d, d, d, d, n, None) == 2
+
