@@ -16,6 +16,11 @@ times the fp64 CPU oracle on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu] [--full]
 
+`--redistribute` instead prints one JSON line on the redistribution of the
+kept pairs over G=8 GPUs (each expert owned by one, the 16 most loaded
+replicated on all): the host solver's time and the device layout's time on
+the workload's real selection, and the optimal peak against fixed ownership.
+
 `--sweep` instead prints one JSON line of the keep-ratio sweep: the fused call
 with every quota at floor(r * n_e) for r in 0.1, 0.25, 0.5, 0.75, 1.0 (all
 projections alike), and the unpruned call, on the chosen workload.
@@ -65,6 +70,8 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 512 MiB device copy (a known-size kernel that "
                          "calibrates the HBM byte counters of a profiler pass)")
+    ap.add_argument("--redistribute", action="store_true",
+                    help="time the redistribution onto replicas instead of the bench line")
     ap.add_argument("--sweep", action="store_true",
                     help="keep-ratio sweep (quota = floor(r n_e)) instead of the bench line")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -414,6 +421,47 @@ def keep_sweep(L, synth, p, dev, steps, warmup, cfg):
             "unpruned_ms": round(t_full * 1e3, 4), "points": points}
 
 
+def redistribution(L, p, dev, steps, warmup, G=8, hot=16):
+    """Redistribution of one layer call's kept pairs over G GPUs: the host
+    solver (lrm_redistribute) and the device receiver-major layout
+    (lrm_receiver_layout, HIP events on its stream)."""
+    r = p["routing"]
+    W = Workload(L, p, dev)
+    W.step()
+    offsets = W.out["offsets"]
+    Me = np.diff(offsets.cpu().numpy().astype(np.int64))
+    Rm = np.zeros((r.E, G), bool)
+    Rm[np.arange(r.E), np.arange(r.E) % G] = True
+    Rm[np.argsort(-Me, kind="stable")[:hot]] = True
+    fixed = int(max(Me[np.arange(r.E) % G == g].sum() for g in range(G)))
+    for _ in range(warmup):
+        L.lrm_redistribute(Me, Rm)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        peak, x = L.lrm_redistribute(Me, Rm)
+    t_host = (time.perf_counter() - t0) / steps
+    xd = torch.as_tensor(x, device=dev)
+    M = int(Me.sum())
+    ws = None
+    for _ in range(warmup):
+        *_, ws = L.lrm_receiver_layout(offsets, xd, M, ws=ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        L.lrm_receiver_layout(offsets, xd, M, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    if L.lrm_check_device_errors(ws) != 0:
+        raise RuntimeError("receiver layout flagged the assignment")
+    return {"metric": "redistribution of kept pairs onto replicas", "gpus": G,
+            "replicated_experts": hot, "kept_pairs": M, "peak_pairs": peak,
+            "fixed_ownership_peak_pairs": fixed, "mean_pairs": round(M / G, 1),
+            "solver_host_us": round(t_host * 1e6, 1),
+            "layout_device_us": round(e0.elapsed_time(e1) / steps * 1e3, 2),
+            "steps": steps, "warmup": warmup}
+
+
 def time_loop(fn, steps, warmup):
     for _ in range(warmup):
         fn()
@@ -477,6 +525,12 @@ def main():
         copy_probe(dev)
     log(f"bench: generating config {a.config}")
     p = synth.make_config(a.config, device=dev, variant=a.variant)
+    if a.redistribute:
+        log("bench: redistribution onto replicas")
+        line = redistribution(L, p, dev, a.steps, a.warmup)
+        line["config"] = {"workload": synth.CONFIGS[a.config]["name"]}
+        print(json.dumps(line), flush=True)
+        return
     if a.sweep:
         log("bench: keep-ratio sweep")
         print(json.dumps(keep_sweep(L, synth, p, dev, a.steps, a.warmup, a.config)), flush=True)
