@@ -21,6 +21,10 @@ kept pairs over G=8 GPUs (each expert owned by one, the 16 most loaded
 replicated on all): the host solver's time and the device layout's time on
 the workload's real selection, and the optimal peak against fixed ownership.
 
+`--controller` instead prints one JSON line comparing the fused call under
+the workload's own quotas with the same pair budget spent by the quota
+controller (water-filling caps, lrm_quota_waterfill).
+
 `--sweep` instead prints one JSON line of the keep-ratio sweep: the fused call
 with every quota at floor(r * n_e) for r in 0.1, 0.25, 0.5, 0.75, 1.0 (all
 projections alike), and the unpruned call, on the chosen workload.
@@ -70,6 +74,8 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 512 MiB device copy (a known-size kernel that "
                          "calibrates the HBM byte counters of a profiler pass)")
+    ap.add_argument("--controller", action="store_true",
+                    help="compare the workload's quotas with water-filling quotas of equal budget")
     ap.add_argument("--redistribute", action="store_true",
                     help="time the redistribution onto replicas instead of the bench line")
     ap.add_argument("--sweep", action="store_true",
@@ -421,6 +427,37 @@ def keep_sweep(L, synth, p, dev, steps, warmup, cfg):
             "unpruned_ms": round(t_full * 1e3, 4), "points": points}
 
 
+def controller(L, p, dev, steps, warmup):
+    """The fused call under the workload's quotas and under water-filling
+    quotas (lrm_quota_waterfill) with the same pair budget: kept pairs, the
+    largest per-expert kept count, the host controller's time, ms per call."""
+    r = p["routing"]
+    W = Workload(L, p, dev)
+    key = "quota" if p["kind"] == "linear" else "quota_down"
+    own = np.asarray(p[key], np.int64)
+    budget = int(np.minimum(own, r.counts).sum())
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        wf = L.lrm_quota_waterfill(r.counts, budget)
+    t_ctl = (time.perf_counter() - t0) / steps
+    res = {}
+    for name, q in (("workload_quotas", own.astype(np.int32)), ("waterfill", wf)):
+        if p["kind"] == "linear":
+            pb = L.linear_problem(W.pairs, p["X"], p["X_rows"], p["G"], p["G_rows"], p["W"], q)
+        else:
+            pb = L.swiglu_problem(W.pairs, p["X"], "token", p["G"], "token", p["A"], p["B"],
+                                  p["W_gate"], p["W_up"], p["W_down"], q, q, q)
+        ws = torch.empty(L.lrm_workspace_size(pb), dtype=torch.uint8, device=dev)
+        t = time_loop(lambda: L.lrm_expert_backward(pb, W.out, ws=ws), steps, warmup)
+        Me = np.diff(W.out["offsets"].cpu().numpy().astype(np.int64))
+        res[name] = {"kept_pairs": int(Me.sum()), "max_expert_kept": int(Me.max()),
+                     "ms": round(t * 1e3, 4), "kept_pairs_per_s": round(Me.sum() / t, 1)}
+        del pb, ws
+    return {"metric": "quota controller (water-filling caps) at the workload's pair budget",
+            "budget_pairs": budget, "controller_host_us": round(t_ctl * 1e6, 2),
+            "steps": steps, "warmup": warmup, **res}
+
+
 def redistribution(L, p, dev, steps, warmup, G=8, hot=16):
     """Redistribution of one layer call's kept pairs over G GPUs: the host
     solver (lrm_redistribute) and the device receiver-major layout
@@ -525,6 +562,12 @@ def main():
         copy_probe(dev)
     log(f"bench: generating config {a.config}")
     p = synth.make_config(a.config, device=dev, variant=a.variant)
+    if a.controller:
+        log("bench: quota controller")
+        line = controller(L, p, dev, a.steps, a.warmup)
+        line["config"] = {"workload": synth.CONFIGS[a.config]["name"]}
+        print(json.dumps(line), flush=True)
+        return
     if a.redistribute:
         log("bench: redistribution onto replicas")
         line = redistribution(L, p, dev, a.steps, a.warmup)

@@ -191,6 +191,24 @@ lrm_status lrm_unpermute(const lrm_pairs* pairs, const int32_t* pos, const float
                          void* stream);
 size_t lrm_unpermute_workspace_size(const lrm_pairs* pairs);
 
+/* ------------------------------------------------------ quota controller */
+
+/* Quotas before the computation (page 1, section "Что делает LRMoE: полный
+ * прямой проход, обрезанный обратный", bullet "Квоты до вычислений"; page 2,
+ * bullet "Des quotas avant le calcul"): from the number of pairs routed to
+ * each expert and one budget of pairs this GPU may carry through the
+ * backward pass (the memory and network limits), water-filling caps that
+ * trim the most loaded experts first.  HOST function, no GPU work:
+ *   tau = the largest integer with sum_e min(counts[e], tau) <= budget;
+ *   quota[e] = min(counts[e], tau), plus one for the first
+ *   budget - sum_e min(counts[e], tau) experts (lowest index) with
+ *   counts[e] > tau; with budget >= sum counts, quota = counts.
+ * So sum quota = min(budget, sum counts) and the largest quota is the
+ * smallest possible for that total.
+ * counts: host [E] >= 0; quota: host [E] output (may alias counts).
+ * LRM_ERR_QUOTA if a count or the budget is negative. */
+lrm_status lrm_quota_waterfill(int32_t E, const int32_t* counts, int64_t budget, int32_t* quota);
+
 /* ----------------------------------------- redistribution onto replicas */
 
 /* Redistribution of the kept pairs over the copies of their expert (page 1,

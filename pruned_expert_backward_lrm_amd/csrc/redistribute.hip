@@ -11,6 +11,10 @@
 // GPU in R_e -> sink (min(cap_g, T - base_g)), which is integral.  The flow
 // is Dinic's algorithm on arrays carved from the caller's host workspace.
 //
+// lrm_quota_waterfill (host): the controller's quotas before the backward
+// pass (bullet "Квоты до вычислений"): water-filling caps under one pair
+// budget, the most loaded experts trimmed first.
+//
 // lrm_receiver_layout (device): given the assignment, the destination of
 // every expert-major packed row in a receiver-major buffer: receiver g's block
 // holds experts e = 0..E-1 in order, x[e][g] rows each; an expert's rows go
@@ -278,6 +282,44 @@ lrm_status lrm_redistribute(int32_t E, int32_t G, const int32_t* kept, const uin
       assign[(int64_t)e * G + g] = a < 0 ? 0 : (int32_t)(n.orig[a] - n.cap[a]);
     }
   *peak = lo;
+  return LRM_OK;
+}
+
+lrm_status lrm_quota_waterfill(int32_t E, const int32_t* counts, int64_t budget, int32_t* quota) {
+  if (E < 1 || E > kMaxE) return LRM_ERR_SHAPE;
+  if (!counts || !quota) return LRM_ERR_NULL;
+  if (budget < 0) return LRM_ERR_QUOTA;
+  int64_t total = 0;
+  int32_t nmax = 0;
+  for (int e = 0; e < E; ++e) {
+    if (counts[e] < 0) return LRM_ERR_QUOTA;
+    total += counts[e];
+    nmax = std::max(nmax, counts[e]);
+  }
+  if (budget >= total) {
+    for (int e = 0; e < E; ++e) quota[e] = counts[e];
+    return LRM_OK;
+  }
+  auto kept_at = [&](int64_t tau) {
+    int64_t s = 0;
+    for (int e = 0; e < E; ++e) s += std::min<int64_t>(counts[e], tau);
+    return s;
+  };
+  int64_t lo = 0, hi = nmax;  // largest tau with kept_at(tau) <= budget
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) / 2;
+    if (kept_at(mid) <= budget) lo = mid; else hi = mid - 1;
+  }
+  int64_t left = budget - kept_at(lo);
+  for (int e = 0; e < E; ++e) {  // (counts may alias quota: read before write)
+    const int32_t n = counts[e];
+    int32_t q = (int32_t)std::min<int64_t>(n, lo);
+    if (left > 0 && n > lo) {
+      ++q;
+      --left;
+    }
+    quota[e] = q;
+  }
   return LRM_OK;
 }
 

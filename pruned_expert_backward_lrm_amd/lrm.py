@@ -96,6 +96,7 @@ _sigs = {
                                              _SZ, _P, C.POINTER(C.c_void_p), _I32]),
     "lrm_workspace_size": (_SZ, [C.POINTER(lrm_problem)]),
     "lrm_check_device_errors": (C.c_int, [_P, _P]),
+    "lrm_quota_waterfill": (C.c_int, [_I32, _P, C.c_int64, _P]),
     "lrm_redistribute": (C.c_int, [_I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ]),
     "lrm_redistribute_workspace_size": (_SZ, [_I32, _I32]),
     "lrm_receiver_layout": (C.c_int, [_I32, _I32, _P, _P, _I32, _P, _P, _P, _P, _SZ, _P]),
@@ -234,6 +235,16 @@ def lrm_unpermute(pairs: Pairs, pos, dXp, d_in: int, out_rows, dX, ws=None, stre
 def lrm_max_kept(N: int, quota) -> int:
     q = _quota_arr(quota)
     return int(_lib.lrm_max_kept(int(N), int(q.shape[0]), q.ctypes.data))
+
+
+def lrm_quota_waterfill(counts, budget: int) -> np.ndarray:
+    """Host call: water-filling quotas [E] for candidate counts [E] under a
+    pair budget."""
+    n = np.ascontiguousarray(np.asarray(counts, dtype=np.int32))
+    q = np.zeros_like(n)
+    _check(_lib.lrm_quota_waterfill(int(n.shape[0]), _ptr(n), int(budget), _ptr(q)),
+           "lrm_quota_waterfill")
+    return q
 
 
 def lrm_redistribute(kept, replica, base=None, cap=None):
