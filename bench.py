@@ -74,6 +74,8 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 512 MiB device copy (a known-size kernel that "
                          "calibrates the HBM byte counters of a profiler pass)")
+    ap.add_argument("--dw-bf16", action="store_true",
+                    help="weight gradients stored as bf16 (LRM_DW_BF16) instead of fp32")
     ap.add_argument("--controller", action="store_true",
                     help="compare the workload's quotas with water-filling quotas of equal budget")
     ap.add_argument("--redistribute", action="store_true",
@@ -204,8 +206,11 @@ def copy_probe(dev):
 class Workload:
     """Problem descriptors, outputs and workspaces of one layer call."""
 
-    def __init__(self, L, p, dev):
+    def __init__(self, L, p, dev, dw_bf16=False):
         self.L, self.p, self.r = L, p, p["routing"]
+        self.dwb = dw_bf16
+        fl = L.LRM_DW_BF16 if dw_bf16 else 0
+        wdt = torch.bfloat16 if dw_bf16 else torch.float32
         r = self.r
         self.pairs = L.Pairs.from_routing(r, dev)
         f32 = dict(dtype=torch.float32, device=dev)
@@ -213,24 +218,26 @@ class Workload:
         self.kind = p["kind"]
         if self.kind == "linear":
             X, G, W = p["X"], p["G"], p["W"]
-            self.pb = L.linear_problem(self.pairs, X, p["X_rows"], G, p["G_rows"], W, p["quota"])
+            self.pb = L.linear_problem(self.pairs, X, p["X_rows"], G, p["G_rows"], W, p["quota"],
+                                       fl)
             self.pb_full = L.linear_problem(self.pairs, X, p["X_rows"], G, p["G_rows"], W, None,
-                                            L.LRM_KEEP_ALL)
+                                            L.LRM_KEEP_ALL | fl)
             rows = r.T if p["X_rows"] == "token" else r.N
-            self.out = dict(dW=torch.empty(r.E, p["d_out"], p["d_in"], **f32),
+            self.out = dict(dW=torch.empty(r.E, p["d_out"], p["d_in"], dtype=wdt, device=dev),
                             dX=torch.empty(rows, p["d_in"], **f32))
             self.stages = ["score", "select", "compact", "grouped_gemm", "unpermute"]
             self.gemm_stages = ["grouped_gemm"]
         else:
             t = [p[k] for k in ("X", "G", "A", "B", "W_gate", "W_up", "W_down")]
             q = (p["quota_down"], p["quota_gate"], p["quota_up"])
-            self.pb = L.swiglu_problem(self.pairs, t[0], "token", t[1], "token", *t[2:], *q)
+            self.pb = L.swiglu_problem(self.pairs, t[0], "token", t[1], "token", *t[2:], *q, fl)
             self.pb_full = L.swiglu_problem(self.pairs, t[0], "token", t[1], "token", *t[2:],
-                                            None, None, None, L.LRM_KEEP_ALL)
+                                            None, None, None, L.LRM_KEEP_ALL | fl)
             H, I = p["H"], p["I"]
-            self.out = dict(dW_gate=torch.empty(r.E, I, H, **f32),
-                            dW_up=torch.empty(r.E, I, H, **f32),
-                            dW_down=torch.empty(r.E, H, I, **f32), dX=torch.empty(r.T, H, **f32))
+            wd = dict(dtype=wdt, device=dev)
+            self.out = dict(dW_gate=torch.empty(r.E, I, H, **wd),
+                            dW_up=torch.empty(r.E, I, H, **wd),
+                            dW_down=torch.empty(r.E, H, I, **wd), dX=torch.empty(r.T, H, **f32))
             self.stages = ["score_down", "select_down", "compact_down", "gemm_down", "glu_bwd",
                            "select_gate_up", "compact_gate_up", "gemm_gate_up", "unpermute"]
             self.gemm_stages = ["gemm_down", "gemm_gate_up"]
@@ -260,6 +267,7 @@ class Workload:
         move, with the packed rows counted once and fp32 outputs."""
         p, r = self.p, self.r
         b = self.p["X"].element_size()
+        wb = 2 if self.dwb else 4  # bytes of a stored weight-gradient element
         act = int(np.count_nonzero(Me))
         E, N, T = r.E, r.N, r.T
         if self.kind == "linear":
@@ -270,7 +278,7 @@ class Workload:
                 "score": dict(bytes=(xr * di + gr * do) * b + N * 12),
                 "select": dict(bytes=N * 8 + M * 4),
                 "compact": dict(bytes=2 * M * (di + do) * b),
-                "grouped_gemm": dict(bytes=E * do * di * 4 + act * do * di * b
+                "grouped_gemm": dict(bytes=E * do * di * wb + act * do * di * b
                                      + M * (di + do) * b + M * di * 4,
                                      flops=4.0 * M * di * do),
                 "unpermute": dict(bytes=M * di * 4 + T * di * 4),
@@ -280,12 +288,12 @@ class Workload:
             "score_down": dict(bytes=T * H * b + 2 * N * I * b + N * 12),
             "select_down": dict(bytes=N * 8 + M * 4),
             "compact_down": dict(bytes=2 * M * H * b + 3 * M * I * b),
-            "gemm_down": dict(bytes=act * H * I * b + E * H * I * 4 + M * (H + I) * b
+            "gemm_down": dict(bytes=act * H * I * b + E * H * I * wb + M * (H + I) * b
                               + M * I * 4, flops=4.0 * M * H * I),
             "glu_bwd": dict(bytes=T * H * b + M * I * 4 + 4 * M * I * b),
             "select_gate_up": dict(bytes=2 * (M * 8)),
             "compact_gate_up": dict(bytes=2 * M * H * b),
-            "gemm_gate_up": dict(bytes=2 * act * I * H * b + 2 * E * I * H * 4
+            "gemm_gate_up": dict(bytes=2 * act * I * H * b + 2 * E * I * H * wb
                                  + M * (2 * I + H) * b + M * H * 4, flops=8.0 * M * H * I),
             "unpermute": dict(bytes=M * H * 4 + T * H * 4),
         }
@@ -578,7 +586,7 @@ def main():
         log("bench: keep-ratio sweep")
         print(json.dumps(keep_sweep(L, synth, p, dev, a.steps, a.warmup, a.config)), flush=True)
         return
-    W = Workload(L, p, dev)
+    W = Workload(L, p, dev, a.dw_bf16)
     r = p["routing"]
     log("bench: timing the pruned backward")
     wall, per = time_fused(W, a.steps, a.warmup)
@@ -603,7 +611,7 @@ def main():
         shape = f"T={r.T} H={p['H']} I={p['I']}"
     workload = workload_name(spec, r.T, r.E, r.k, shape, a.variant)
     kernels = None
-    if p["kind"] == "linear":
+    if p["kind"] == "linear" and not a.dw_bf16:
         # the dominant kernel: the longer of the two GEMM launches, timed alone
         log("bench: timing the grouped-GEMM kernels alone")
         kernels = gemm_kernels(W, a.steps, a.warmup)
@@ -640,7 +648,7 @@ def main():
         "vs_baseline": None,
         "dtype": p["dtype"],
         "data": "synthetic",
-        "config": {"workload": workload,
+        "config": {"workload": workload, "dw_dtype": "bf16" if a.dw_bf16 else "f32",
                    "pairs": r.N, "kept_pairs": M, "active_experts": int(np.count_nonzero(Me))},
         "roofline": roof,
         "gemm_kernels": ({k: {"ms": round(v["ms"], 4), "bytes": v["bytes"], "flops": v["flops"],

@@ -86,6 +86,12 @@ typedef enum lrm_kind { LRM_LINEAR = 0, LRM_SWIGLU = 1 } lrm_kind;
 
 /* Flags of lrm_expert_backward. */
 #define LRM_KEEP_ALL 1u /* unpruned baseline: every pair kept, no score/select */
+/* Weight gradients stored as bf16: dW (or dW_gate, dW_up, dW_down) point to
+ * bf16 arrays of the same shape, each element the fp32 result rounded to
+ * nearest even (accumulation stays fp32; the other outputs are unchanged).
+ * Halves the dW bytes, which are fixed per expert and dominate when few pairs
+ * are kept.  bf16 inputs only (LRM_ERR_UNSUPPORTED otherwise). */
+#define LRM_DW_BF16 2u
 
 /* The routed pairs of one layer call (the page's "pair": one token -> expert
  * choice; page 1 introduction). */
@@ -295,6 +301,7 @@ typedef struct lrm_problem {
 } lrm_problem;
 
 typedef struct lrm_outputs {
+  /* dW pointers: fp32, or bf16 storage with LRM_DW_BF16 */
   float* dW;      /* LINEAR: device [E][d_out][d_in] */
   float* dW_gate; /* SWIGLU: device [E][I][H] */
   float* dW_up;   /* SWIGLU: device [E][I][H] */

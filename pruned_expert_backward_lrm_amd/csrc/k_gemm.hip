@@ -354,6 +354,41 @@ __device__ __forceinline__ void write_tile(const f32x4 (&acc)[C::FM][C::FN], boo
   }
 }
 
+// The same tile rounded to bf16 (nearest even): 4 columns per lane as 8 bytes.
+template <class C>
+__device__ __forceinline__ void write_tile_bf16(const f32x4 (&acc)[C::FM][C::FN], bool zero,
+                                                uint16_t* out, int64_t ldc, int rows, int cols) {
+  const int l = lane_id(), w = threadIdx.x >> 6;
+  const int wm = w / C::WGN, wn = w % C::WGN;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+    const int row = wm * C::TM + i * 16 + (l & 15);
+    if (row >= rows) continue;
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const int col = wn * C::TN + j * 16 + (l >> 4) * 4;
+      if (col < cols) {
+        u32x2 v;
+        v[0] = zero ? 0u : pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+        v[1] = zero ? 0u : pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+        *reinterpret_cast<u32x2*>(out + (int64_t)row * ldc + col) = v;
+      }
+    }
+  }
+}
+
+// A finished (or zero) output tile at out (an element of dW or dXp): dW
+// tiles go out as bf16 when the call asks for it.
+template <class C, bool DWB>
+__device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x4 (&acc)[C::FM][C::FN],
+                                           bool zero, float* out, int rows, int cols) {
+  if constexpr (DWB)
+    write_tile_bf16<C>(acc, zero, reinterpret_cast<uint16_t*>(a.dW) + (out - a.dW), a.d_in,
+                       rows, cols);
+  else
+    write_tile<C>(acc, zero, out, a.d_in, rows, cols);
+}
+
 // MFMAs of k-granules kk..kk+3 (lane group l >> 4 takes granule kk + (l >> 4))
 // on the LDS stage (Ac, Bc): B fragments once, A fragments FCH at a time.
 template <class C>
@@ -440,8 +475,8 @@ __device__ __forceinline__ void dw_share(const GemmPlan& P, int x, int* lo, int*
 // ahead, one barrier per k-tile.  The loads of a tile's first k-tiles are thus
 // in flight while the previous tile's outputs are written.  A tile with no
 // k-tiles (an expert that kept no rows) writes zeros.
-template <class C, bool DX>
-__global__ __launch_bounds__(C::NT, C::WPE) void k_gemm_stream(GemmPlan P) {
+template <class C, bool DX, bool DWB>
+__device__ __forceinline__ void gemm_stream(const GemmPlan& P) {
   __shared__ __attribute__((aligned(16))) uint16_t As[C::STAGES * C::BM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[C::STAGES * C::BN * BK];
   const GemmArgs& a = P.a;
@@ -469,7 +504,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void k_gemm_stream(GemmPlan P) {
   for (; tc < hi; tc += nbx) {
     jc = make_job<C, DX>(P, tc);
     if (jc.nk > 0) break;
-    if (jc.rows > 0) write_tile<C>(acc, true, jc.C, a.d_in, jc.rows, jc.cols);
+    if (jc.rows > 0) store_tile<C, DWB>(a, acc, true, jc.C, jc.rows, jc.cols);
   }
   if (tc >= hi) return;
 
@@ -520,7 +555,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void k_gemm_stream(GemmPlan P) {
     }
     if constexpr (!kEarlyLoad) LRM_ISSUE_LOAD();
     if (++kc == jc.nk) {
-      write_tile<C>(acc, false, jc.C, a.d_in, jc.rows, jc.cols);
+      store_tile<C, DWB>(a, acc, false, jc.C, jc.rows, jc.cols);
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -529,13 +564,25 @@ __global__ __launch_bounds__(C::NT, C::WPE) void k_gemm_stream(GemmPlan P) {
       for (tc += nbx; tc < hi; tc += nbx) {
         jc = make_job<C, DX>(P, tc);
         if (jc.nk > 0) break;
-        if (jc.rows > 0) write_tile<C>(acc, true, jc.C, a.d_in, jc.rows, jc.cols);
+        if (jc.rows > 0) store_tile<C, DWB>(a, acc, true, jc.C, jc.rows, jc.cols);
       }
       if (tc >= hi) break;
     }
     __syncthreads();
   }
 #undef LRM_ISSUE_LOAD
+}
+
+template <class C, bool DX>
+__global__ __launch_bounds__(C::NT, C::WPE) void k_gemm_stream(GemmPlan P) {
+  gemm_stream<C, DX, false>(P);
+}
+
+// dW products stored as bf16 (a separate kernel: the fp32 kernels keep their
+// code and registers)
+template <class C>
+__global__ __launch_bounds__(C::NT, C::WPE) void k_gemm_stream_dwbf16(GemmPlan P) {
+  gemm_stream<C, false, true>(P);
 }
 
 // ------------------------------------------------------------------ fp32
@@ -675,7 +722,7 @@ static hipError_t plan_tiles(const GemmArgs& a, int tmw, int tnw, int tmx, int t
 }
 
 // Resident blocks of one stream kernel on the current device (cached).
-template <class C, bool DX>
+template <class C, bool DX, bool DWB = false>
 static int stream_grid_cap() {
   static int cap[16];
   int dev = 0;
@@ -685,10 +732,12 @@ static int stream_grid_cap() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemm_stream<C, DX>, C::NT, 0) !=
-            hipSuccess ||
-        occ <= 0)
-      occ = 1;
+    hipError_t e;
+    if constexpr (DWB)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemm_stream_dwbf16<C>, C::NT, 0);
+    else
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemm_stream<C, DX>, C::NT, 0);
+    if (e != hipSuccess || occ <= 0) occ = 1;
     cap[dev] = cus * occ;
   }
   return cap[dev];
@@ -699,6 +748,14 @@ static hipError_t launch_stream(const GemmPlan& P, int ntiles_max, hipStream_t s
   if (ntiles_max <= 0) return hipSuccess;
   // a multiple of 8 blocks (one share per XCD), at most one resident round
   const int64_t want = ((int64_t)ntiles_max + 7) & ~7ll;
+  if constexpr (!DX) {
+    if (P.a.dw_bf16) {
+      const int G =
+          (int)std::min<int64_t>(want, std::max(8, stream_grid_cap<C, false, true>() & ~7));
+      LRM_LAUNCH(G, C::NT, 0, s, k_gemm_stream_dwbf16<C>)(P);
+      return hipGetLastError();
+    }
+  }
   const int G = (int)std::min<int64_t>(want, std::max(8, stream_grid_cap<C, DX>() & ~7));
   LRM_LAUNCH(G, C::NT, 0, s, k_gemm_stream<C, DX>)(P);
   return hipGetLastError();
@@ -750,6 +807,7 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s) {
       default: return launch_bf16<CfgS, CfgS>(a, s);
     }
   }
+  if (a.dw_bf16) return hipErrorInvalidValue;  // bf16 dW needs the bf16 kernels
   GemmPlan P{};
   hipError_t err = plan_tiles(a, FBM, FBN, FBM, FBN, &P, s);
   if (err != hipSuccess || P.G == 0) return err;

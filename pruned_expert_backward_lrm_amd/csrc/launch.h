@@ -98,6 +98,7 @@ struct GemmArgs {
   float* dXp;  // [max_rows][d_in] or nullptr
   int32_t* mt_off;  // workspace [E+1]
   int mt_ready;     // mt_off already holds the prefix for gemm_dx_tile_rows(*this)
+  int dw_bf16;      // dW is stored as bf16 (round to nearest even), bf16 kernels only
 };
 int gemm_tile_choice(const GemmArgs& a);
 // Rows of a dX tile of the bf16 kernels (the prefix mt_off is built for it).

@@ -551,8 +551,9 @@ GluSizes glu_sizes(const lrm_problem* pb) {
 lrm_status check_problem(const lrm_problem* pb, const lrm_outputs* out) {
   if (!pb) return LRM_ERR_NULL;
   LRM_TRY(check_pairs(&pb->pairs));
-  if (pb->flags & ~LRM_KEEP_ALL) return LRM_ERR_UNSUPPORTED;
+  if (pb->flags & ~(LRM_KEEP_ALL | LRM_DW_BF16)) return LRM_ERR_UNSUPPORTED;
   if (pb->dtype != LRM_F32 && pb->dtype != LRM_BF16) return LRM_ERR_DTYPE;
+  if ((pb->flags & LRM_DW_BF16) && pb->dtype != LRM_BF16) return LRM_ERR_UNSUPPORTED;
   const lrm_pairs* p = &pb->pairs;
   const bool keep_all = (pb->flags & LRM_KEEP_ALL) != 0;
   const int q = 16 / esize(pb->dtype);
@@ -661,6 +662,7 @@ lrm_status run_linear(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   g.d_in = pb->d_in; g.d_out = pb->d_out;
   g.offsets = L.offsets; g.Gp = L.Gp; g.Xp = L.Xp; g.W = pb->W; g.w_stride = pb->w_stride;
   g.dW = out->dW; g.dXp = L.dXp; g.mt_off = L.mt_off; g.mt_ready = 1;
+  g.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
   LRM_TRY_HIP(launch_grouped_gemm(g, s));
   LRM_TRY_HIP(mark(4));
   // 5. back to the layout of X, times the routing weight
@@ -711,6 +713,7 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   gd.offsets = L.offsets; gd.Gp = L.Gd; gd.Xp = L.Hd;
   gd.W = pb->W_down; gd.w_stride = (int64_t)H * I;
   gd.dW = out->dW_down; gd.dXp = L.U; gd.mt_off = L.mt_off; gd.mt_ready = 1;
+  gd.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
   LRM_TRY_HIP(launch_grouped_gemm(gd, s));
   LRM_TRY_HIP(mark(4));
   // ---- SwiGLU backward and the gate/up scores
@@ -760,11 +763,13 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
     gg.W = pb->W_gate; gg.w_stride = (int64_t)I * H;
     gg.Gp2 = L.GB; gg.W2 = pb->W_up; gg.w2_stride = (int64_t)I * H; gg.d_out2 = I;
     gg.dW = out->dW_gate; gg.dXp = L.dXp; gg.mt_off = L.mt_off;
+    gg.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
     LRM_TRY_HIP(launch_grouped_gemm(gg, s));
     GemmArgs gu{};
     gu.E = E; gu.bf16 = bf16; gu.max_rows = (int)z.Md; gu.d_in = H; gu.d_out = I;
     gu.offsets = L.offsets; gu.Gp = L.GB; gu.Xp = L.Xgu;
     gu.dW = out->dW_up; gu.dXp = nullptr; gu.mt_off = L.mt_off;
+    gu.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
     LRM_TRY_HIP(launch_grouped_gemm(gu, s));
     sa.pos[0] = L.pos; sa.src[0] = L.dXp;
   } else {
@@ -794,6 +799,7 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
       gk.offsets = offv[k]; gk.Gp = Gpv[k]; gk.Xp = Xpv[k];
       gk.W = Wv[k]; gk.w_stride = (int64_t)I * H;
       gk.dW = dWv[k]; gk.dXp = dXv[k]; gk.mt_off = L.mt_off;
+      gk.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
       LRM_TRY_HIP(launch_grouped_gemm(gk, s));
       sa.pos[k] = L.pos; sa.pos2[k] = posv[k]; sa.src[k] = dXv[k];
     }

@@ -31,6 +31,7 @@ LRM_F32, LRM_BF16 = 0, 1
 LRM_ROWS_TOKEN, LRM_ROWS_PAIR = 0, 1
 LRM_LINEAR, LRM_SWIGLU = 0, 1
 LRM_KEEP_ALL = 1
+LRM_DW_BF16 = 2
 ROWS = {"token": LRM_ROWS_TOKEN, "pair": LRM_ROWS_PAIR}
 
 

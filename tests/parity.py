@@ -82,7 +82,9 @@ def run_linear(L, p: dict, device: str, flags: int = 0, ws=None):
                           None if flags & L.LRM_KEEP_ALL else p["quota"], flags)
     rows = r.T if p["X_rows"] == "token" else r.N
     f32, i32 = dict(dtype=torch.float32, device=device), dict(dtype=torch.int32, device=device)
-    out = dict(dW=torch.full((r.E, p["d_out"], p["d_in"]), float("nan"), **f32),
+    wdt = torch.bfloat16 if flags & L.LRM_DW_BF16 else torch.float32
+    out = dict(dW=torch.full((r.E, p["d_out"], p["d_in"]), float("nan"), dtype=wdt,
+                             device=device),
                dX=torch.full((rows, p["d_in"]), float("nan"), **f32),
                score=torch.full((max(r.N, 1),), float("nan"), **f32),
                pos=torch.full((max(r.N, 1),), -7, **i32),
@@ -108,8 +110,9 @@ def run_swiglu(L, p: dict, device: str, flags: int = 0, ws=None):
     Md = N if keep_all else max(L.lrm_max_kept(N, p["quota_down"]), 1)
     f32, i32 = dict(dtype=torch.float32, device=device), dict(dtype=torch.int32, device=device)
     nan = float("nan")
-    out = dict(dW_gate=torch.full((E, I, H), nan, **f32), dW_up=torch.full((E, I, H), nan, **f32),
-               dW_down=torch.full((E, H, I), nan, **f32), dX=torch.full((r.T, H), nan, **f32),
+    wd = dict(dtype=torch.bfloat16 if flags & L.LRM_DW_BF16 else torch.float32, device=device)
+    out = dict(dW_gate=torch.full((E, I, H), nan, **wd), dW_up=torch.full((E, I, H), nan, **wd),
+               dW_down=torch.full((E, H, I), nan, **wd), dX=torch.full((r.T, H), nan, **f32),
                score=torch.full((max(N, 1),), nan, **f32),
                pos=torch.full((max(N, 1),), -7, **i32),
                offsets=torch.full((E + 1,), -7, **i32),

@@ -297,6 +297,38 @@ def test_fused_linear_small(L, dtype, x_rows, g_rows):
     say("  ", s)
 
 
+@pytest.mark.parametrize("shape", [(600, 10, 4, 136, 200), (4096, 8, 2, 520, 264)])
+def test_fused_linear_dw_bf16_is_rounded_fp32(L, shape):
+    """LRM_DW_BF16: dW equals the fp32 path's dW rounded to nearest even, bit
+    for bit, and every other output is unchanged (small experts use the 64-row
+    dX tiles, large ones the 256x256 tiles; ragged d_in and d_out)."""
+    T, E, k, d_in, d_out = shape
+    say("fused linear, bf16 dW", shape)
+    p = synth.make_linear(T, E, k, d_in, d_out, dtype="bf16", seed=12, zipf=1.2,
+                          quota=lambda c: (3 * c) // 4)
+    ref = run_linear(L, p, DEV)
+    got = run_linear(L, p, DEV, flags=L.LRM_DW_BF16)
+    assert got["dW"].dtype == torch.bfloat16
+    assert torch.equal(got["dW"].view(torch.int16), ref["dW"].to(torch.bfloat16).view(torch.int16))
+    for key in ("dX", "score", "pos", "offsets"):
+        assert torch.equal(got[key], ref[key]), key
+
+
+def test_fused_linear_dw_bf16_needs_bf16_inputs(L):
+    import ctypes as C
+    p = synth.make_linear(64, 4, 2, 32, 32, dtype="f32", seed=3)
+    r = p["routing"]
+    pairs = L.Pairs.from_routing(r, DEV)
+    X, G, W = (p[k].to(DEV) for k in ("X", "G", "W"))
+    pb = L.linear_problem(pairs, X, "token", G, "pair", W, p["quota"], L.LRM_DW_BF16)
+    out = dict(dW=torch.empty(r.E, 32, 32, device=DEV), dX=torch.empty(r.T, 32, device=DEV))
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=DEV)
+    assert L._lib.lrm_workspace_size(C.byref(pb.c)) == 0
+    st = L._lib.lrm_expert_backward(C.byref(pb.c), C.byref(L._outputs(out)), ws.data_ptr(),
+                                    ws.numel(), None)
+    assert st == 10  # LRM_ERR_UNSUPPORTED, before any launch
+
+
 def test_fused_linear_config1(L):
     p = synth.make_config(1)
     res = run_linear(L, p, DEV)

@@ -72,6 +72,22 @@ def test_fused_swiglu_quota_zero(L):
         assert not res[k].any(), k
 
 
+@pytest.mark.parametrize("variant", ["same", "second"])
+def test_fused_swiglu_dw_bf16_is_rounded_fp32(L, variant):
+    """LRM_DW_BF16: every weight gradient equals the fp32 path's rounded to
+    nearest even, bit for bit; the other outputs are unchanged."""
+    say("swiglu bf16 dW", variant)
+    p = synth.make_swiglu(700, 6, 2, 200, 136, dtype="bf16", seed=16, zipf=1.2,
+                          quotas=QUOTAS[variant], g_std=1e-2)
+    ref = run_swiglu(L, p, DEV)
+    got = run_swiglu(L, p, DEV, flags=L.LRM_DW_BF16)
+    for k in ("dW_gate", "dW_up", "dW_down"):
+        assert got[k].dtype == torch.bfloat16
+        assert torch.equal(got[k].view(torch.int16), ref[k].to(torch.bfloat16).view(torch.int16)), k
+    for k in ("dX", "score", "pos", "score_gate", "pos_gate", "pos_up", "dH"):
+        assert torch.equal(got[k], ref[k]), k
+
+
 def test_fused_swiglu_deterministic(L):
     p = synth.make_swiglu(500, 8, 2, 256, 128, dtype="bf16", seed=8, zipf=1.1,
                           quotas=QUOTAS["second"])
