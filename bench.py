@@ -74,6 +74,9 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 512 MiB device copy (a known-size kernel that "
                          "calibrates the HBM byte counters of a profiler pass)")
+    ap.add_argument("--h-table", action="store_true",
+                    help="SwiGLU: pass the per-pair |silu(a) b|^2 a forward pass would save "
+                         "(computed before timing), so the down score reads no A/B rows")
     ap.add_argument("--dw-bf16", action="store_true",
                     help="weight gradients stored as bf16 (LRM_DW_BF16) instead of fp32")
     ap.add_argument("--controller", action="store_true",
@@ -206,9 +209,18 @@ def copy_probe(dev):
 class Workload:
     """Problem descriptors, outputs and workspaces of one layer call."""
 
-    def __init__(self, L, p, dev, dw_bf16=False):
+    def __init__(self, L, p, dev, dw_bf16=False, h_table=False):
         self.L, self.p, self.r = L, p, p["routing"]
         self.dwb = dw_bf16
+        self.htab = None
+        if h_table and p["kind"] != "linear":
+            # what a forward pass would save: |silu(a) b|^2 per pair, fp64
+            A, B = p["A"], p["B"]
+            self.htab = torch.empty(A.shape[0], dtype=torch.float64, device=dev)
+            for i in range(0, A.shape[0], 1 << 16):
+                a, b = A[i:i + (1 << 16)].float(), B[i:i + (1 << 16)].float()
+                h = a * torch.sigmoid(a) * b
+                self.htab[i:i + (1 << 16)] = (h * h).sum(dim=1, dtype=torch.float64)
         fl = L.LRM_DW_BF16 if dw_bf16 else 0
         wdt = torch.bfloat16 if dw_bf16 else torch.float32
         r = self.r
@@ -230,7 +242,8 @@ class Workload:
         else:
             t = [p[k] for k in ("X", "G", "A", "B", "W_gate", "W_up", "W_down")]
             q = (p["quota_down"], p["quota_gate"], p["quota_up"])
-            self.pb = L.swiglu_problem(self.pairs, t[0], "token", t[1], "token", *t[2:], *q, fl)
+            self.pb = L.swiglu_problem(self.pairs, t[0], "token", t[1], "token", *t[2:], *q, fl,
+                                       h_sumsq=self.htab)
             self.pb_full = L.swiglu_problem(self.pairs, t[0], "token", t[1], "token", *t[2:],
                                             None, None, None, L.LRM_KEEP_ALL | fl)
             H, I = p["H"], p["I"]
@@ -285,7 +298,8 @@ class Workload:
             }
         H, I = p["H"], p["I"]
         return {
-            "score_down": dict(bytes=T * H * b + 2 * N * I * b + N * 12),
+            "score_down": dict(bytes=T * H * b + (N * 8 if self.htab is not None else 2 * N * I * b)
+                               + N * 12),
             "select_down": dict(bytes=N * 8 + M * 4),
             "compact_down": dict(bytes=2 * M * H * b + 3 * M * I * b),
             "gemm_down": dict(bytes=act * H * I * b + E * H * I * wb + M * (H + I) * b
@@ -586,7 +600,7 @@ def main():
         log("bench: keep-ratio sweep")
         print(json.dumps(keep_sweep(L, synth, p, dev, a.steps, a.warmup, a.config)), flush=True)
         return
-    W = Workload(L, p, dev, a.dw_bf16)
+    W = Workload(L, p, dev, a.dw_bf16, a.h_table)
     r = p["routing"]
     log("bench: timing the pruned backward")
     wall, per = time_fused(W, a.steps, a.warmup)
@@ -649,6 +663,7 @@ def main():
         "dtype": p["dtype"],
         "data": "synthetic",
         "config": {"workload": workload, "dw_dtype": "bf16" if a.dw_bf16 else "f32",
+                   "h_table": bool(a.h_table and p["kind"] != "linear"),
                    "pairs": r.N, "kept_pairs": M, "active_experts": int(np.count_nonzero(Me))},
         "roofline": roof,
         "gemm_kernels": ({k: {"ms": round(v["ms"], 4), "bytes": v["bytes"], "flops": v["flops"],

@@ -298,6 +298,12 @@ typedef struct lrm_problem {
   const int32_t* quota_down;
   const int32_t* quota_gate;
   const int32_t* quota_up;
+  /* SWIGLU, optional (NULL = computed from A and B): device [N] fp64, the
+   * squared norm |silu(a_p) * b_p|^2 of every pair's down-projection input,
+   * saved by the forward pass.  The down score then reads this one number per
+   * pair instead of the rows of A and B; compaction and the SwiGLU backward
+   * still read A and B, for the kept rows only.  8-byte aligned. */
+  const double* h_sumsq;
 } lrm_problem;
 
 typedef struct lrm_outputs {

@@ -117,13 +117,21 @@ hipError_t run_score(const lrm_pairs* p, const lrm_mat* X, const lrm_mat* G, flo
   return launch_pair_score(op, s);
 }
 
+// h_tab (optional): |silu(a) * b|^2 of every pair, saved by the forward; the
+// pair kernel then reads it instead of the A and B rows.
 hipError_t run_score_glu(const lrm_pairs* p, const lrm_mat* A, const lrm_mat* B,
-                         const lrm_mat* G, float* score, const ScoreWs& w, hipStream_t s) {
+                         const lrm_mat* G, float* score, const ScoreWs& w, hipStream_t s,
+                         const double* h_tab = nullptr) {
   const int bf16 = A->dtype == LRM_BF16;
   ScoreOperands op{};
   op.N = p->N; op.T = p->T; op.bf16 = bf16; op.token = p->token; op.weight = p->weight;
   op.G = G->ptr; op.ldg = G->ld; op.gcols = G->cols; op.g_pair = G->rows == LRM_ROWS_PAIR;
-  op.glu = 1; op.A = A->ptr; op.B = B->ptr; op.lda = A->ld; op.ldb = B->ld; op.icols = A->cols;
+  if (h_tab) {
+    op.xtab = h_tab;
+  } else {
+    op.glu = 1; op.A = A->ptr; op.B = B->ptr; op.lda = A->ld; op.ldb = B->ld;
+    op.icols = A->cols;
+  }
   op.x_pair = 1;
   op.score = score;
   if (!op.g_pair) {
@@ -576,6 +584,7 @@ lrm_status check_problem(const lrm_problem* pb, const lrm_outputs* out) {
     if (!pb->W_gate || !pb->W_up || !pb->W_down) return LRM_ERR_NULL;
     if (!aligned16(pb->W_gate) || !aligned16(pb->W_up) || !aligned16(pb->W_down))
       return LRM_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(pb->h_sumsq) & 7u) != 0) return LRM_ERR_ALIGN;
     if (!keep_all) {
       LRM_TRY(check_quota(pb->quota_down, p->E, nullptr));
       LRM_TRY(check_quota(pb->quota_gate, p->E, nullptr));
@@ -693,7 +702,8 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   const int dx_rows = gemm_dx_tile_rows(gd);
   LRM_TRY_HIP(mark(0));
   // ---- down projection: input h = silu(a) * b, gradient g = G row
-  if (!keep_all) LRM_TRY_HIP(run_score_glu(p, &pb->A, &pb->B, &pb->G, L.score, L.sc, s));
+  if (!keep_all)
+    LRM_TRY_HIP(run_score_glu(p, &pb->A, &pb->B, &pb->G, L.score, L.sc, s, pb->h_sumsq));
   LRM_TRY_HIP(mark(1));
   // (the token offsets of the unpermute step come out of the bucketing pass)
   const bool tok_out = pb->X.rows != LRM_ROWS_PAIR;

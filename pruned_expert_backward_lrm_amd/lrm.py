@@ -61,7 +61,7 @@ class lrm_problem(C.Structure):
                 ("d_out", C.c_int32), ("quota", C.c_void_p), ("A", lrm_mat), ("B", lrm_mat),
                 ("W_gate", C.c_void_p), ("W_up", C.c_void_p), ("W_down", C.c_void_p),
                 ("H", C.c_int32), ("I", C.c_int32), ("quota_down", C.c_void_p),
-                ("quota_gate", C.c_void_p), ("quota_up", C.c_void_p)]
+                ("quota_gate", C.c_void_p), ("quota_up", C.c_void_p), ("h_sumsq", C.c_void_p)]
 
 
 class lrm_outputs(C.Structure):
@@ -314,10 +314,11 @@ def linear_problem(pairs: Pairs, X, x_rows, G, g_rows, W, quota, flags=0) -> Pro
 
 
 def swiglu_problem(pairs: Pairs, X, x_rows, G, g_rows, A, B, W_gate, W_up, W_down,
-                   quota_down, quota_gate, quota_up, flags=0) -> Problem:
+                   quota_down, quota_gate, quota_up, flags=0, h_sumsq=None) -> Problem:
     pb = Problem(LRM_SWIGLU, pairs, dtype_code(X), flags)
     qs = [(_quota_arr(q) if q is not None else None) for q in (quota_down, quota_gate, quota_up)]
-    pb.hold(X, G, A, B, W_gate, W_up, W_down, *qs)
+    pb.hold(X, G, A, B, W_gate, W_up, W_down, *qs, h_sumsq)
+    pb.c.h_sumsq = _ptr(h_sumsq)
     c = pb.c
     c.X, c.G = mat(X, x_rows), mat(G, g_rows)
     c.A, c.B = mat(A, "pair"), mat(B, "pair")

@@ -96,7 +96,7 @@ def run_linear(L, p: dict, device: str, flags: int = 0, ws=None):
     return res
 
 
-def run_swiglu(L, p: dict, device: str, flags: int = 0, ws=None):
+def run_swiglu(L, p: dict, device: str, flags: int = 0, ws=None, h_sumsq=None):
     """The fused SwiGLU backward through the C ABI, with every optional output
     requested.  Returns host tensors."""
     r = p["routing"]
@@ -104,8 +104,9 @@ def run_swiglu(L, p: dict, device: str, flags: int = 0, ws=None):
     pairs = L.Pairs.from_routing(r, device)
     t = {k: p[k].to(device) for k in ("X", "G", "A", "B", "W_gate", "W_up", "W_down")}
     q = (None, None, None) if keep_all else (p["quota_down"], p["quota_gate"], p["quota_up"])
+    hs = None if h_sumsq is None else h_sumsq.to(device=device, dtype=torch.float64)
     pb = L.swiglu_problem(pairs, t["X"], "token", t["G"], "token", t["A"], t["B"], t["W_gate"],
-                          t["W_up"], t["W_down"], *q, flags)
+                          t["W_up"], t["W_down"], *q, flags, h_sumsq=hs)
     H, I, E, N = p["H"], p["I"], r.E, r.N
     Md = N if keep_all else max(L.lrm_max_kept(N, p["quota_down"]), 1)
     f32, i32 = dict(dtype=torch.float32, device=device), dict(dtype=torch.int32, device=device)

@@ -34,7 +34,7 @@ def test_struct_layouts_match_header():
     assert C.sizeof(L.lrm_mat) == 32
     assert C.sizeof(L.lrm_outputs) == 15 * 8
     assert L.lrm_problem.X.offset == 56 and L.lrm_problem.quota.offset == 144
-    assert C.sizeof(L.lrm_problem) == 272
+    assert C.sizeof(L.lrm_problem) == 280 and L.lrm_problem.h_sumsq.offset == 272
 
 
 def test_status_strings_and_version():

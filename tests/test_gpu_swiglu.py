@@ -88,6 +88,29 @@ def test_fused_swiglu_dw_bf16_is_rounded_fp32(L, variant):
         assert torch.equal(got[k], ref[k]), k
 
 
+@pytest.mark.parametrize("variant", ["same", "second"])
+def test_fused_swiglu_h_sumsq_table(L, variant):
+    """The down score from a per-pair |silu(a) b|^2 saved by the forward (here
+    computed in fp64 on the host): the down scores are w^2 |g|^2 times the
+    table, rounded once to fp32, and the whole call meets the parity bar."""
+    say("swiglu with a saved |h|^2 table", variant)
+    p = synth.make_swiglu(700, 6, 2, 200, 136, dtype="bf16", seed=17, zipf=1.2,
+                          quotas=QUOTAS[variant], g_std=1e-2)
+    a, b = p["A"].double(), p["B"].double()
+    h = a * torch.sigmoid(a) * b
+    tab = (h * h).sum(dim=1)
+    res = run_swiglu(L, p, DEV, h_sumsq=tab)
+    r = p["routing"]
+    g2 = (p["G"].double() ** 2).sum(dim=1)
+    w = torch.as_tensor(r.weight, dtype=torch.float64)
+    tok = torch.as_tensor(r.token, dtype=torch.int64)
+    expect = (w * w * g2[tok] * tab).float()
+    got = res["score"][: r.N]
+    assert torch.allclose(got, expect, rtol=1e-6, atol=0), (got - expect).abs().max()
+    s = judge_swiglu(p, res)
+    say("  ", s)
+
+
 def test_fused_swiglu_deterministic(L):
     p = synth.make_swiglu(500, 8, 2, 256, 128, dtype="bf16", seed=8, zipf=1.1,
                           quotas=QUOTAS["second"])
