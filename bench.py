@@ -97,10 +97,19 @@ TRAFFIC_PATH = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 GEMM_SRC = os.path.join(ROOT, "pruned_expert_backward_lrm_amd", "csrc", "k_gemm.hip")
 
 
+def normalized_source(text):
+    """C++ source without comments and whitespace: edits of comments or layout
+    do not change what the counters were taken on."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return "".join(text.split())
+
+
 def gemm_source_sha():
     import hashlib
-    with open(GEMM_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    with open(GEMM_SRC, encoding="utf-8") as f:
+        return hashlib.sha256(normalized_source(f.read()).encode()).hexdigest()
 
 
 def workload_name(spec, T, E, k, shape, variant=None):
@@ -178,8 +187,8 @@ def record_traffic(fetch_dir, write_dir, cfg):
                  "passes (FETCH_SIZE, WRITE_SIZE, KiB per dispatch) scaled by what the same "
                  f"counters read for a 512 MiB device copy (FETCH_SIZE reads "
                  f"{scale['FETCH_SIZE']:.4f}, WRITE_SIZE {scale['WRITE_SIZE']:.4f} of the true "
-                 "bytes). source_sha256 is the hash of csrc/k_gemm.hip the counters were "
-                 "taken on."),
+                 "bytes). source_sha256 is the SHA-256 of csrc/k_gemm.hip, comments and "
+                 "whitespace removed, that the counters were taken on."),
         "commands": [
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d " + fetch_dir
             + f" -o run -- python bench.py --config {cfg} --no-cpu --copy-probe --steps 5 --warmup 2",

@@ -3,24 +3,26 @@
 // For each expert e with M_e packed rows (device-side sizes, no host sync):
 //   dW[e] = Gp_e^T Xp_e   [d_out][d_in], K = M_e (zero tile when M_e = 0)
 //   dXp_e = Gp_e W_e (+ Gp2_e W2_e)  [M_e][d_in], K = d_out (+ d_out2)
-// Both products run in one launch over a combined tile list: E * (d_out/BM) *
-// (d_in/BN) fixed-size dW tiles, then dX tiles (ceil(M_e/BM) row tiles per
-// expert, located by a binary search of a device-built prefix).  Block ids are
-// remapped so that consecutive tiles (the same expert) land on the same XCD
-// and share its L2.
 //
-// bf16: v_mfma_f32_16x16x32_bf16 with fp32 accumulation, BK 64, tile shapes
-// 128x128 (4 waves of 64x64), 256x128 (8 waves of 64x64) and 256x256 (8 waves
-// of 128x64).  Operands are staged in LDS as [row][k] (k contiguous, 128-byte
-// rows with a bank-aware granule swizzle) so that each lane's fragment (8
-// consecutive k) is one 16-byte LDS read.  Sources whose k runs along rows (Gp
-// and Xp in dW, W in dX) are loaded as 4x8 blocks with 16-byte buffer loads
-// and transposed in registers (v_perm) before the LDS store.  Two LDS stages;
-// global loads run two k-tiles ahead of the MFMAs.
-// The MFMA is issued with the N-side fragment first, so each lane's four
-// accumulators are four consecutive output columns (one 16-byte store).
+// bf16: two launches of k_gemm_stream, one over the dW tiles (E x d_out/BM x
+// d_in/BN, fixed size) and one over the dX tiles (ceil(M_e/BM) row tiles per
+// expert, located by a binary search of a device-built prefix).  Each launch
+// cuts its tile list into 8 shares of equal cost, one per XCD (block b runs on
+// XCD b mod 8); inside a share, persistent blocks run their tiles' k-tiles as
+// one stream (or, for MFMA-bound launches of few rounds, one block per tile).
+// v_mfma_f32_16x16x32_bf16 with fp32 accumulation, BK 64, tiles of 256x256,
+// 256x128, 128x128 and 64x256.  Operands are staged in LDS as [row][k] (k
+// contiguous, 128-byte rows with a bank-aware granule swizzle) so that each
+// lane's fragment (8 consecutive k) is one 16-byte LDS read.  Sources whose k
+// runs along rows (Gp and Xp in dW, W in dX) are loaded as 4x8 blocks with
+// 16-byte buffer loads and transposed in registers (v_perm) before the LDS
+// store.  Two LDS stages; global loads run up to two k-tiles ahead of the
+// MFMAs.  The MFMA is issued with the N-side fragment first, so each lane's
+// four accumulators are four consecutive output columns (one 16-byte store,
+// or 8 bytes when dW is stored as bf16).
 //
-// fp32: plain LDS-tiled fp32 FMA (64x64 tile) for fp32 inputs.
+// fp32: plain LDS-tiled fp32 FMA (64x64 tile), one launch over the combined
+// dW and dX tile list.
 #include <stdlib.h>
 
 #include <algorithm>

@@ -24,6 +24,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "launch.h"
 #include "lrm.h"
 
 namespace lrm {
@@ -340,13 +341,13 @@ lrm_status lrm_receiver_layout(int32_t E, int32_t G, const int32_t* offsets,
   hipStream_t s = as_stream(stream);
   uint32_t* err = static_cast<uint32_t*>(ws);
   int32_t* rep_off = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + kAlign);
-  hipLaunchKernelGGL(k_layout_plan, dim3(1), dim3(kPlanThreads), 0, s, E, G, offsets, assign,
-                     rep_off, send_off, blk_off, err);
+  LRM_LAUNCH(1, kPlanThreads, 0, s, k_layout_plan)(E, G, offsets, assign, rep_off, send_off,
+                                                   blk_off, err);
   if (hipGetLastError() != hipSuccess) return LRM_ERR_HIP;
   if (max_rows > 0) {
     const int blocks = std::min(4096, (max_rows + 255) / 256);
-    hipLaunchKernelGGL(k_layout_rows, dim3(blocks), dim3(256), 0, s, E, G, max_rows, offsets,
-                       rep_off, send_off, blk_off, dst);
+    LRM_LAUNCH(blocks, 256, 0, s, k_layout_rows)(E, G, max_rows, offsets, rep_off, send_off,
+                                                 blk_off, dst);
     if (hipGetLastError() != hipSuccess) return LRM_ERR_HIP;
   }
   return LRM_OK;
