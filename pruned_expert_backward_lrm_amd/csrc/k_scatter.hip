@@ -53,6 +53,7 @@ __global__ __launch_bounds__(256) void k_unpermute_token(ScatterArgs a) {
   f32x4 acc[kUnpChunks];
 #pragma unroll
   for (int u = 0; u < kUnpChunks; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bool two = a.src[1] != nullptr;  // a second source (wave-uniform)
   for (int pb = p0; pb < p1; pb += kWave) {
     const int pi = pb + l;
     int r0 = -1, r1 = -1;
@@ -62,21 +63,28 @@ __global__ __launch_bounds__(256) void k_unpermute_token(ScatterArgs a) {
       r0 = src_row(a, 0, pi);
       r1 = src_row(a, 1, pi);
     }
-    const int np = min(kWave, p1 - pb);
-    for (int j0 = 0; j0 < np; j0 += kUnpBatch) {
+    // only the kept pairs, in pair order (a dropped pair adds exact zeros)
+    uint64_t kept = __ballot(r0 >= 0 || r1 >= 0);
+    while (kept) {
       f32x4 v[kUnpBatch][2][kUnpChunks];
       float wj[kUnpBatch];
 #pragma unroll
       for (int jj = 0; jj < kUnpBatch; ++jj) {
-        const int j = min(j0 + jj, kWave - 1);
-        const bool in = j0 + jj < np;
-        wj[jj] = __shfl(w, j, kWave);
+        const bool in = kept != 0;
+        const int j = in ? __builtin_ctzll(kept) : 0;
+        kept &= kept - 1;  // (a no-op once empty)
+        wj[jj] = in ? __shfl(w, j, kWave) : 0.f;
         // one buffer resource per source row (wave-uniform): the row itself,
-        // or an empty one for a pair whose row is not kept
+        // or an empty one (loads return zeros) for a missing row
         const int rj[2] = {__builtin_amdgcn_readfirstlane(in ? __shfl(r0, j, kWave) : -1),
                            __builtin_amdgcn_readfirstlane(in ? __shfl(r1, j, kWave) : -1)};
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
+          if (k == 1 && !two) {
+#pragma unroll
+            for (int u = 0; u < kUnpChunks; ++u) v[jj][k][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            continue;
+          }
           const __amdgpu_buffer_rsrc_t rs =
               rows_rsrc(a.src[k] + (int64_t)max(rj[k], 0) * a.d, rj[k] >= 0 ? (int64_t)a.d * 4 : 0);
 #pragma unroll
