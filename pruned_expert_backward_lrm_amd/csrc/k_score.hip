@@ -92,38 +92,101 @@ struct PairScoreArgs {
   float* score;
 };
 
+// A wave scores kPairsPerWave consecutive pairs.  Rows of up to 128 16-byte
+// chunks (1024 bf16 or 512 fp32 columns) are loaded two chunks per lane for
+// all of the wave's pairs before any is reduced, and the pairs' token,
+// weight and table entries are requested alongside, so a wave waits for
+// memory about once rather than once per pair.  Longer rows fall back to a
+// chunk loop per pair.
+constexpr int kPairsPerWave = 4;
+
+template <bool BF16>
+__device__ __forceinline__ double chunk_sumsq(u32x4 v, double acc) {
+  return BF16 ? chunk_sumsq_bf16(v, acc) : chunk_sumsq_f32(v, acc);
+}
+
+// |row|^2 partial sums of kPairsPerWave rows (lane-local; reduce afterwards).
+template <bool BF16>
+__device__ __forceinline__ void rows_sumsq_lane(const char* base, int64_t ld_bytes, int cols,
+                                                int64_t p0, int npairs, double (&acc)[kPairsPerWave]) {
+  constexpr int kEpc = BF16 ? 8 : 4;
+  const int nchunks = cols / kEpc;
+  const int l = lane_id();
+  if (nchunks <= 2 * kWave) {
+    u32x4 v[kPairsPerWave][2];
+#pragma unroll
+    for (int u = 0; u < kPairsPerWave; ++u) {
+      const u32x4* r = reinterpret_cast<const u32x4*>(base + (p0 + u) * ld_bytes);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = l + h * kWave;
+        v[u][h] = (u < npairs && c < nchunks) ? __builtin_nontemporal_load(r + c)
+                                              : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPairsPerWave; ++u)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) acc[u] = chunk_sumsq<BF16>(v[u][h], acc[u]);
+  } else {
+#pragma unroll
+    for (int u = 0; u < kPairsPerWave; ++u) {
+      if (u >= npairs) break;
+      const u32x4* r = reinterpret_cast<const u32x4*>(base + (p0 + u) * ld_bytes);
+      for (int c = l; c < nchunks; c += kWave)
+        acc[u] = chunk_sumsq<BF16>(__builtin_nontemporal_load(r + c), acc[u]);
+    }
+  }
+}
+
 // XMODE: 0 = table, 1 = inline row, 2 = inline GLU.  GINL: g inline.
 template <bool BF16, bool GINL, int XMODE>
 __global__ __launch_bounds__(256) void k_pair_score_wave(PairScoreArgs a) {
-  const int64_t p = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (p >= a.N) return;
-  const int t = a.token[p];
-  const bool tok_ok = (t >= 0 && t < a.T);
-  double g2, x2;
-  if constexpr (GINL) {
-    g2 = row_sumsq_wave<BF16>(a.G + p * a.ldg_bytes, a.gcols);
-  } else {
-    g2 = a.g_pair ? a.gtab[p] : (tok_ok ? a.gtab[t] : 0.0);
+  const int64_t p0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kPairsPerWave;
+  if (p0 >= a.N) return;
+  const int np = (int)min<int64_t>(kPairsPerWave, a.N - p0);
+  const int l = lane_id();
+  // lane u < np: pair p0 + u's token, weight and table factors
+  int t = -1;
+  double w = 0.0, gt = 0.0, xt = 0.0;
+  if (l < np) {
+    const int64_t p = p0 + l;
+    t = a.token[p];
+    w = a.weight[p];
+    const bool tok_ok = t >= 0 && t < a.T;
+    if constexpr (!GINL) gt = a.g_pair ? a.gtab[p] : (tok_ok ? a.gtab[t] : 0.0);
+    if constexpr (XMODE == 0) xt = a.x_pair ? a.xtab[p] : (tok_ok ? a.xtab[t] : 0.0);
   }
-  if constexpr (XMODE == 1) {
-    x2 = row_sumsq_wave<BF16>(a.X + p * a.ldx_bytes, a.xcols);
-  } else if constexpr (XMODE == 2) {
+  double g2[kPairsPerWave], x2[kPairsPerWave];
+#pragma unroll
+  for (int u = 0; u < kPairsPerWave; ++u) g2[u] = x2[u] = 0.0;
+  if constexpr (GINL) rows_sumsq_lane<BF16>(a.G, a.ldg_bytes, a.gcols, p0, np, g2);
+  if constexpr (XMODE == 1) rows_sumsq_lane<BF16>(a.X, a.ldx_bytes, a.xcols, p0, np, x2);
+  if constexpr (XMODE == 2) {
+    // A and B rows pair by pair (batching them across pairs costs occupancy)
     constexpr int kEpc = BF16 ? 8 : 4;
-    const u32x4* ra = reinterpret_cast<const u32x4*>(a.A + p * a.lda_bytes);
-    const u32x4* rb = reinterpret_cast<const u32x4*>(a.B + p * a.ldb_bytes);
-    double acc = 0.0;
-    for (int c = lane_id(); c < a.icols / kEpc; c += kWave) {
-      u32x4 va = __builtin_nontemporal_load(ra + c);
-      u32x4 vb = __builtin_nontemporal_load(rb + c);
-      acc = BF16 ? glu_chunk_sumsq_bf16(va, vb, acc) : glu_chunk_sumsq_f32(va, vb, acc);
+#pragma unroll
+    for (int u = 0; u < kPairsPerWave; ++u) {
+      if (u >= np) break;
+      const u32x4* ra = reinterpret_cast<const u32x4*>(a.A + (p0 + u) * a.lda_bytes);
+      const u32x4* rb = reinterpret_cast<const u32x4*>(a.B + (p0 + u) * a.ldb_bytes);
+      for (int c = l; c < a.icols / kEpc; c += kWave) {
+        u32x4 va = __builtin_nontemporal_load(ra + c);
+        u32x4 vb = __builtin_nontemporal_load(rb + c);
+        x2[u] = BF16 ? glu_chunk_sumsq_bf16(va, vb, x2[u]) : glu_chunk_sumsq_f32(va, vb, x2[u]);
+      }
     }
-    x2 = wave_sum(acc);
-  } else {
-    x2 = a.x_pair ? a.xtab[p] : (tok_ok ? a.xtab[t] : 0.0);
   }
-  if (lane_id() == 0) {
-    const double w = a.weight[p];
-    a.score[p] = (float)(w * w * g2 * x2);  // an out-of-range token gave a zero factor
+#pragma unroll
+  for (int u = 0; u < kPairsPerWave; ++u) {
+    if (u >= np) break;
+    const double gu = GINL ? wave_sum(g2[u]) : __shfl(gt, u, kWave);
+    const double xu = XMODE != 0 ? wave_sum(x2[u]) : __shfl(xt, u, kWave);
+    const double wu = __shfl(w, u, kWave);
+    const int tu = __shfl(t, u, kWave);
+    // an out-of-range token gives a zero factor, as in the table path
+    const bool tok_ok = tu >= 0 && tu < a.T;
+    if (l == 0) a.score[p0 + u] = (float)(wu * wu * gu * (tok_ok || XMODE != 0 ? xu : 0.0));
   }
 }
 
@@ -154,7 +217,7 @@ hipError_t launch_row_sumsq(const void* M, int bf16, int64_t ld, int cols, int r
 
 template <bool BF16>
 static void dispatch_pair_score(const PairScoreArgs& a, int g_inline, int x_mode, hipStream_t s) {
-  dim3 wgrid((a.N + 3) / 4);
+  dim3 wgrid((unsigned)((a.N + 4 * kPairsPerWave - 1) / (4 * kPairsPerWave)));
   if (!g_inline && x_mode == 0) {
     LRM_LAUNCH((a.N + 255) / 256, 256, 0, s, k_pair_score_table)(a);
   } else if (g_inline && x_mode == 0) {
