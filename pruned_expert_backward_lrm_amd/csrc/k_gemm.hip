@@ -36,6 +36,21 @@ namespace lrm {
 
 constexpr int NT = 256;  // threads of an fp32 block
 
+// Read of the per-expert tables (kept offsets, dX row-tile prefix) that no
+// GEMM kernel writes.  Through the constant address space a wave-uniform index
+// becomes a scalar load, which waits on its own counter; a vector load would
+// also wait for every store the wave issued before it (one counter covers
+// vector loads and stores, retired in order), so the first table read after a
+// tile's stores would hold the wave until those stores reach the cache.
+#ifdef LRM_CPU_EMU
+__device__ __forceinline__ int ld_table(const int32_t* p, int i) { return p[i]; }
+#else
+typedef const __attribute__((address_space(4))) int32_t* table_ptr;
+__device__ __forceinline__ int ld_table(const int32_t* p, int i) {
+  return ((table_ptr)(uintptr_t)p)[i];
+}
+#endif
+
 __device__ __forceinline__ int xcd_remap(int b, int G) {
   // hardware places block b on XCD b % 8; give each XCD a contiguous range
   return (b & 7) * (G >> 3) + (b >> 3);
@@ -46,7 +61,7 @@ __device__ __forceinline__ int find_expert(const int32_t* mt_off, int E, int mt)
   int lo = 0, hi = E;  // invariant: mt_off[lo] <= mt < mt_off[hi]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (mt_off[mid] <= mt) lo = mid; else hi = mid;
+    if (ld_table(mt_off, mid) <= mt) lo = mid; else hi = mid;
   }
   return lo;
 }
@@ -298,8 +313,8 @@ __device__ __forceinline__ Job make_job(const GemmPlan& P, int t) {
     int ti, tj;
     raster(t - e * per, P.ntm_w, P.ntn, &ti, &tj);
     const int i0 = ti * C::BM, j0 = tj * C::BN;
-    const int kb = a.offsets[e];
-    const int Me = max(0, min(a.offsets[e + 1], a.max_rows) - kb);
+    const int kb = ld_table(a.offsets, e);
+    const int Me = max(0, min(ld_table(a.offsets, e + 1), a.max_rows) - kb);
     j.s0.a = (const char*)a.Gp + (int64_t)kb * a.d_out * 2;
     j.s0.b = (const char*)a.Xp + (int64_t)kb * a.d_in * 2;
     j.s0.a_rows_valid = 0; j.s0.a_n0 = i0; j.s0.b_n0 = j0;
@@ -311,10 +326,10 @@ __device__ __forceinline__ Job make_job(const GemmPlan& P, int t) {
     j.cols = min(C::BN, a.d_in - j0);
   } else {
     int mt, tn;
-    raster(t, a.mt_off[a.E], P.ntn_x, &mt, &tn);
+    raster(t, ld_table(a.mt_off, a.E), P.ntn_x, &mt, &tn);
     const int e = find_expert(a.mt_off, a.E, mt);
-    const int m0 = a.offsets[e] + (mt - a.mt_off[e]) * C::BM;
-    const int rows = min(C::BM, min(a.offsets[e + 1], a.max_rows) - m0);
+    const int m0 = ld_table(a.offsets, e) + (mt - ld_table(a.mt_off, e)) * C::BM;
+    const int rows = min(C::BM, min(ld_table(a.offsets, e + 1), a.max_rows) - m0);
     const int j0 = tn * C::BN;
     j.s0.a = (const char*)a.Gp + (int64_t)m0 * a.d_out * 2;
     j.s0.b = (const char*)a.W + (int64_t)e * a.w_stride * 2;
@@ -486,7 +501,7 @@ __device__ __forceinline__ void gemm_stream(const GemmPlan& P) {
   int lo, hi;
   if constexpr (DX) {
     // every dX tile runs K = d_out: equal shares of the tile count
-    const int n = a.mt_off[a.E] * P.ntn_x;
+    const int n = ld_table(a.mt_off, a.E) * P.ntn_x;
     lo = (int)((int64_t)n * x / 8);
     hi = (int)((int64_t)n * (x + 1) / 8);
   } else {
@@ -662,8 +677,8 @@ __global__ __launch_bounds__(NT) void k_grouped_gemm_f32(GemmPlan P) {
     const int per = P.ntm_w * P.ntn;
     const int e = idx / per, rem = idx % per;
     const int i0 = (rem / P.ntn) * FBM, j0 = (rem % P.ntn) * FBN;
-    const int kb = a.offsets[e];
-    const int Me = max(0, min(a.offsets[e + 1], a.max_rows) - kb);
+    const int kb = ld_table(a.offsets, e);
+    const int Me = max(0, min(ld_table(a.offsets, e + 1), a.max_rows) - kb);
     F32Seg s;
     s.a = (const float*)a.Gp + (int64_t)kb * a.d_out; s.lda = a.d_out; s.a_trans = 1;
     s.b = (const float*)a.Xp + (int64_t)kb * a.d_in; s.ldb = a.d_in;
