@@ -715,7 +715,7 @@ __global__ __launch_bounds__(NT) void k_grouped_gemm_f32(GemmPlan P) {
 // Tile configurations of the bf16 kernel.
 using CfgS = TileCfg<128, 128, 2, 2, 2>;  // 4 waves of 64x64
 using CfgM = TileCfg<256, 128, 4, 2>;   // 8 waves of 64x64
-using CfgL = TileCfg<256, 256, 2, 4>;   // 8 waves of 128x64
+using CfgL = TileCfg<256, 256, 4, 2>;   // 8 waves of 64x128
 using CfgXS = TileCfg<64, 256, 1, 8, 2>;  // 8 waves of 64x32 (dX of small experts)
 
 // Plan the combined tile list (dW tiles tmw x tn, dX tiles tmx x tn) and build
