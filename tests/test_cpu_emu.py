@@ -1,0 +1,202 @@
+"""The unchanged library sources on the CPU: every kernel compiled as host C++
+against tests/cpu_emu/cpu_emu.h (lanes as threads, wave collectives, buffer
+range checks, an MFMA model) with AddressSanitizer, driven through the fused
+C-ABI call by tests/cpu_emu/emu_driver.cpp.  Any out-of-bounds global-memory
+access of a kernel or of the host code aborts the run; the outputs must pass
+the same oracle checks as the GPU parity tests.  Runs without a GPU.
+
+Every lane is an OS thread and every wave collective two 64-thread barriers,
+so a case takes 30-130 s.  The default run keeps two: the tiny fp32 workload
+(every step, the fp32 GEMM) and the bf16 grouped GEMM in its 256x256 tiles;
+LRM_EMU_FULL=1 runs all of them (about 20 minutes on 8 cores).
+"""
+
+from __future__ import annotations
+
+import concurrent.futures as cf
+import hashlib
+import os
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+from pruned_expert_backward_lrm_amd import synth
+from parity import judge_linear, judge_swiglu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "pruned_expert_backward_lrm_amd", "csrc")
+EMU = os.path.join(ROOT, "tests", "cpu_emu")
+CLANG = "/opt/rocm/llvm/bin/clang++"
+FLAGS = ["-std=c++20", "-O1", "-g", "-fsanitize=address", "-fno-omit-frame-pointer"]
+
+LINEAR, SWIGLU = 0, 1
+F32, BF16 = 0, 1
+KEEP_ALL = 1
+ROWS = {"token": 0, "pair": 1}
+
+extended = pytest.mark.skipif(not os.environ.get("LRM_EMU_FULL"),
+                              reason="extended emulation case (set LRM_EMU_FULL=1)")
+
+
+def _sources():
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+
+
+@pytest.fixture(scope="module")
+def driver(tmp_path_factory):
+    if not os.path.exists(CLANG):
+        pytest.skip("clang++ of the ROCm toolchain not found")
+    srcs = _sources() + [os.path.join(EMU, "emu_driver.cpp")]
+    h = hashlib.sha256()
+    for s in srcs + [os.path.join(EMU, "cpu_emu.h")] + \
+            [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC)) if f.endswith(".h")]:
+        with open(s, "rb") as f:
+            h.update(f.read())
+    out = tmp_path_factory.mktemp("emu_" + h.hexdigest()[:12])
+
+    def compile_one(src):
+        obj = os.path.join(out, os.path.basename(src) + ".o")
+        cmd = [CLANG, *FLAGS, "-DLRM_CPU_EMU", "-x", "c++", "-I", EMU, "-I",
+               os.path.join(ROOT, "include"), "-I", CSRC, "-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"{src}:\n{r.stderr[-4000:]}")
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 2)) as ex:
+        objs = list(ex.map(compile_one, srcs))
+    exe = os.path.join(out, "emu_driver")
+    r = subprocess.run([CLANG, "-fsanitize=address", "-o", exe, *objs, "-lpthread"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-4000:]
+    return exe
+
+
+def _raw(t: torch.Tensor) -> bytes:
+    t = t.contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().tobytes()
+    return t.numpy().tobytes()
+
+
+def run_emu(exe, tmp_path, p: dict, flags: int = 0, env_extra=None) -> dict:
+    """One fused call of the emulated library.  Returns the outputs as CPU
+    tensors under the keys the GPU parity helpers use."""
+    r = p["routing"]
+    N, E, T = r.N, r.E, r.T
+    Nr = max(N, 1)
+    dt = BF16 if p["dtype"] == "bf16" else F32
+    kind = LINEAR if p["kind"] == "linear" else SWIGLU
+    d_in = p.get("d_in", 0)
+    d_out = p.get("d_out", 0)
+    H, I = p.get("H", 0), p.get("I", 0)
+    xr = ROWS[p.get("X_rows", "token")]
+    gr = ROWS[p.get("G_rows", "token")]
+    if kind == SWIGLU:
+        Md = N if flags & KEEP_ALL else int(np.minimum(p["quota_down"], r.counts).sum())
+        Md = max(Md, 1)
+    else:
+        Md = 0
+    hdr = np.array([kind, dt, flags, T, N, E, d_in, d_out, H, I, xr, gr, Md, 0, 0, 0], np.int32)
+    pad = lambda a, dtype: np.ascontiguousarray(  # noqa: E731
+        np.concatenate([np.asarray(a, dtype), np.zeros(Nr - len(a), dtype)]))
+    parts = [hdr.tobytes(), pad(r.token, np.int32).tobytes(), pad(r.expert, np.int32).tobytes(),
+             pad(r.weight, np.float32).tobytes()]
+    if kind == LINEAR:
+        parts += [_raw(p["X"]), _raw(p["G"]), _raw(p["W"]),
+                  np.asarray(p["quota"], np.int32).tobytes()]
+    else:
+        parts += [_raw(p[k]) for k in ("X", "G", "A", "B", "W_gate", "W_up", "W_down")]
+        parts += [np.asarray(p[k], np.int32).tobytes()
+                  for k in ("quota_down", "quota_gate", "quota_up")]
+    fin, fout = tmp_path / "in.bin", tmp_path / "out.bin"
+    fin.write_bytes(b"".join(parts))
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1")
+    env.pop("LRM_GEMM_TILE", None)
+    env.update(env_extra or {})
+    res = subprocess.run([exe, str(fin), str(fout)], capture_output=True, text=True,
+                         timeout=600, env=env)
+    assert res.returncode == 0, f"emulated run failed ({res.returncode}):\n{res.stderr[-6000:]}"
+    buf = fout.read_bytes()
+    off = 0
+
+    def take(n, dtype, shape=None):
+        nonlocal off
+        a = np.frombuffer(buf, dtype=dtype, count=n, offset=off).copy()
+        off += n * np.dtype(dtype).itemsize
+        return torch.from_numpy(a.reshape(shape) if shape else a)
+
+    status, dev_status = (int(v) for v in take(2, np.int32))
+    assert status == 0, f"lrm_expert_backward returned {status}"
+    assert dev_status == 0, f"lrm_check_device_errors returned {dev_status}"
+    out = {}
+    if kind == LINEAR:
+        out["dW"] = take(E * d_out * d_in, np.float32, (E, d_out, d_in))
+        rows = T if xr == 0 else N
+        out["dX"] = take(rows * d_in, np.float32, (rows, d_in))
+    else:
+        for k in ("dW_gate", "dW_up"):
+            out[k] = take(E * I * H, np.float32, (E, I, H))
+        out["dW_down"] = take(E * H * I, np.float32, (E, H, I))
+        out["dX"] = take(T * H, np.float32, (T, H))
+    out["score"] = take(Nr, np.float32)
+    out["pos"] = take(Nr, np.int32)
+    out["offsets"] = take(E + 1, np.int32)
+    if kind == SWIGLU:
+        out["score_gate"] = take(Md, np.float32)
+        out["score_up"] = take(Md, np.float32)
+        out["pos_gate"] = take(Md, np.int32)
+        out["pos_up"] = take(Md, np.int32)
+        out["offsets_gate"] = take(E + 1, np.int32)
+        out["offsets_up"] = take(E + 1, np.int32)
+        out["dH"] = take(Md * I, np.float32, (Md, I))
+    assert off == len(buf)
+    return out
+
+
+def test_emu_linear_config1(driver, tmp_path):
+    p = synth.make_config(1)
+    judge_linear(p, run_emu(driver, tmp_path, p))
+
+
+@extended
+@pytest.mark.parametrize("x_rows,g_rows", [("token", "pair"), ("pair", "token")])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_emu_linear_ragged(driver, tmp_path, dtype, x_rows, g_rows):
+    # ragged feature sizes (not multiples of the tiles), skewed experts,
+    # quotas that keep 0..all of an expert
+    p = synth.make_linear(300, 10, 4, 136, 200, dtype=dtype, x_rows=x_rows, g_rows=g_rows,
+                          seed=8, zipf=1.4, quota=lambda c: (c * 5) // 8 + (c % 3 == 0))
+    judge_linear(p, run_emu(driver, tmp_path, p))
+
+
+@pytest.mark.parametrize("tile", [pytest.param("S", marks=extended),
+                                  pytest.param("M", marks=extended), "L",
+                                  pytest.param("X", marks=extended)])
+def test_emu_linear_tile_configs(driver, tmp_path, tile):
+    # every bf16 tile configuration of the grouped GEMM, over an expert with
+    # more rows than one 256-row tile and experts that keep nothing
+    p = synth.make_linear(400, 4, 2, 72, 264, dtype="bf16", seed=3, zipf=1.6,
+                          quota=lambda c: np.where(np.arange(c.size) == 3, 0, c))
+    judge_linear(p, run_emu(driver, tmp_path, p, env_extra={"LRM_GEMM_TILE": tile}))
+
+
+@extended
+def test_emu_linear_keep_all(driver, tmp_path):
+    p = synth.make_linear(200, 6, 2, 64, 96, dtype="bf16", seed=4, zipf=0.8)
+    judge_linear(p, run_emu(driver, tmp_path, p, flags=KEEP_ALL), keep_all=True)
+
+
+@extended
+@pytest.mark.parametrize("variant", ["same", "second"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_emu_swiglu(driver, tmp_path, dtype, variant):
+    quotas = {
+        "same": (lambda c: c // 2, lambda c: c // 2, lambda c: c // 2),
+        "second": (lambda c: (3 * c) // 4, lambda c: (3 * c) // 8 + 1, lambda c: c // 3),
+    }[variant]
+    p = synth.make_swiglu(160, 6, 2, 136, 72, dtype=dtype, seed=5, zipf=1.2, quotas=quotas,
+                          g_std=1e-2)
+    judge_swiglu(p, run_emu(driver, tmp_path, p))
