@@ -200,3 +200,36 @@ def test_emu_swiglu(driver, tmp_path, dtype, variant):
     p = synth.make_swiglu(160, 6, 2, 136, 72, dtype=dtype, seed=5, zipf=1.2, quotas=quotas,
                           g_std=1e-2)
     judge_swiglu(p, run_emu(driver, tmp_path, p))
+
+
+def _no_pairs(kind, dtype, T=48, E=4):
+    r = synth.Routing(T, E, 2, np.zeros(0, np.int32), np.zeros(0, np.int32),
+                      np.zeros(0, np.float32), np.zeros(E, np.int64))
+    dt = synth.torch_dtype(dtype)
+    g = torch.Generator().manual_seed(13)
+    q = np.full(E, 2, np.int32)
+    if kind == "linear":
+        return dict(kind="linear", dtype=dtype, routing=r, T=T, N=0, E=E, k=2, d_in=64,
+                    d_out=32, X_rows="token", G_rows="token", quota=q,
+                    X=torch.randn(T, 64, generator=g).to(dt),
+                    G=torch.randn(T, 32, generator=g).to(dt),
+                    W=torch.randn(E, 32, 64, generator=g).to(dt))
+    H, I = 64, 32
+    return dict(kind="swiglu", dtype=dtype, routing=r, T=T, N=0, E=E, k=2, H=H, I=I,
+                quota_down=q, quota_gate=q.copy(), quota_up=q.copy(),
+                X=torch.randn(T, H, generator=g).to(dt), G=torch.randn(T, H, generator=g).to(dt),
+                A=torch.zeros(0, I).to(dt), B=torch.zeros(0, I).to(dt),
+                W_gate=torch.randn(E, I, H, generator=g).to(dt),
+                W_up=torch.randn(E, I, H, generator=g).to(dt),
+                W_down=torch.randn(E, H, I, generator=g).to(dt))
+
+
+@pytest.mark.parametrize("kind", ["linear", "swiglu"])
+def test_emu_no_pairs(driver, tmp_path, kind):
+    # no pair on this GPU: every output written, exactly zero
+    p = _no_pairs(kind, "bf16")
+    out = run_emu(driver, tmp_path, p)
+    keys = ("dW", "dX") if kind == "linear" else ("dW_gate", "dW_up", "dW_down", "dX")
+    for k in keys:
+        assert not torch.any(out[k] != 0), f"{k} must be exactly zero"
+    assert torch.equal(out["offsets"], torch.zeros(p["E"] + 1, dtype=torch.int32))

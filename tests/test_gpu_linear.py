@@ -370,3 +370,37 @@ def test_fused_linear_config2(L):
     s = judge_linear(host, res)
     say("config2", s)
     assert s["kept"] == int(np.minimum(p["quota"], p["routing"].counts).sum())
+
+
+def _no_pairs_linear(dtype, T=96, E=5, d_in=64, d_out=48):
+    r = synth.Routing(T, E, 2, np.zeros(0, np.int32), np.zeros(0, np.int32),
+                      np.zeros(0, np.float32), np.zeros(E, np.int64))
+    dt = synth.torch_dtype(dtype)
+    g = torch.Generator().manual_seed(11)
+    return dict(kind="linear", dtype=dtype, routing=r, T=T, N=0, E=E, k=2, d_in=d_in,
+                d_out=d_out, X_rows="token", G_rows="token", quota=np.full(E, 3, np.int32),
+                X=torch.randn(T, d_in, generator=g).to(dt),
+                G=torch.randn(T, d_out, generator=g).to(dt),
+                W=torch.randn(E, d_out, d_in, generator=g).to(dt))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fused_linear_no_pairs(L, dtype):
+    # a GPU whose experts received no pair in this layer call: every output
+    # is written, and is exactly zero
+    say("fused linear, no pairs", dtype)
+    p = _no_pairs_linear(dtype)
+    res = run_linear(L, p, DEV)
+    assert not torch.any(res["dW"] != 0), "dW must be exactly zero"
+    assert not torch.any(res["dX"] != 0), "dX must be exactly zero"
+    assert torch.equal(res["offsets"], torch.zeros(p["E"] + 1, dtype=torch.int32))
+
+
+def test_fused_linear_max_experts(L):
+    # the largest expert count the ABI takes: most of the 4096 experts get no
+    # pair or one pair, a few get several (Zipf skew)
+    say("fused linear, 4096 experts")
+    p = synth.make_linear(2048, 4096, 2, 64, 32, dtype="bf16", seed=21, zipf=1.0,
+                          quota=lambda c: (2 * c + 1) // 3)
+    s = judge_linear(p, run_linear(L, p, DEV))
+    say("  ", s)

@@ -140,3 +140,26 @@ def test_swiglu_configs(L, cfg):
     say(f"config {cfg}: oracle on experts {ex}")
     s = judge_swiglu(host, res, experts=ex, tokens=toks)
     say(f"config {cfg}", s)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fused_swiglu_no_pairs(L, dtype):
+    # no pair on this GPU: every weight gradient and every dX row is exactly 0
+    say("swiglu, no pairs", dtype)
+    T, E, H, I = 80, 4, 64, 32
+    r = synth.Routing(T, E, 2, np.zeros(0, np.int32), np.zeros(0, np.int32),
+                      np.zeros(0, np.float32), np.zeros(E, np.int64))
+    dt = synth.torch_dtype(dtype)
+    g = torch.Generator().manual_seed(12)
+    q = np.full(E, 2, np.int32)
+    p = dict(kind="swiglu", dtype=dtype, routing=r, T=T, N=0, E=E, k=2, H=H, I=I,
+             quota_down=q, quota_gate=q.copy(), quota_up=q.copy(),
+             X=torch.randn(T, H, generator=g).to(dt), G=torch.randn(T, H, generator=g).to(dt),
+             A=torch.zeros(0, I).to(dt), B=torch.zeros(0, I).to(dt),
+             W_gate=torch.randn(E, I, H, generator=g).to(dt),
+             W_up=torch.randn(E, I, H, generator=g).to(dt),
+             W_down=torch.randn(E, H, I, generator=g).to(dt))
+    res = run_swiglu(L, p, DEV)
+    for k in ("dW_gate", "dW_up", "dW_down", "dX"):
+        assert not torch.any(res[k] != 0), f"{k} must be exactly zero"
+    assert torch.equal(res["offsets"], torch.zeros(E + 1, dtype=torch.int32))
