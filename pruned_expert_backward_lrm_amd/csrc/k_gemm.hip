@@ -26,6 +26,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include <type_traits>
 
@@ -738,26 +739,31 @@ static hipError_t plan_tiles(const GemmArgs& a, int tmw, int tnw, int tmx, int t
   return hipSuccess;
 }
 
-// Resident blocks of one stream kernel on the current device (cached).
+// Resident blocks of one stream kernel on the current device, cached for the
+// first 16 devices (concurrent callers may both compute it; they store the
+// same value).
 template <class C, bool DX, bool DWB = false>
 static int stream_grid_cap() {
-  static int cap[16];
+  static std::atomic<int> cap[16];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
-  if (cap[dev] == 0) {
-    int cus = 0, occ = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
-    hipError_t e;
-    if constexpr (DWB)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemm_stream_dwbf16<C>, C::NT, 0);
-    else
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemm_stream<C, DX>, C::NT, 0);
-    if (e != hipSuccess || occ <= 0) occ = 1;
-    cap[dev] = cus * occ;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev < 16) {
+    const int c = cap[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
   }
-  return cap[dev];
+  int cus = 0, occ = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  hipError_t e;
+  if constexpr (DWB)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemm_stream_dwbf16<C>, C::NT, 0);
+  else
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemm_stream<C, DX>, C::NT, 0);
+  if (e != hipSuccess || occ <= 0) occ = 1;
+  const int c = cus * occ;
+  if (dev < 16) cap[dev].store(c, std::memory_order_relaxed);
+  return c;
 }
 
 // per_tile: one block per tile (a multiple of 8 blocks), the hardware handing
