@@ -92,6 +92,21 @@ typedef enum lrm_kind { LRM_LINEAR = 0, LRM_SWIGLU = 1 } lrm_kind;
  * Halves the dW bytes, which are fixed per expert and dominate when few pairs
  * are kept.  bf16 inputs only (LRM_ERR_UNSUPPORTED otherwise). */
 #define LRM_DW_BF16 2u
+/* Quotas in device memory: quota (lrm_select, the LINEAR problem) and
+ * quota_down, quota_gate, quota_up (SWIGLU) are device pointers to int32[E],
+ * read by the kernels in stream order, never by the host (a controller on the
+ * GPU can write them just before the call).  The host then cannot size the
+ * packed blocks from the quotas: lrm_workspace_size assumes every pair kept,
+ * and a SWIGLU call always runs its gate/up selections (the one-packing path
+ * for gate/up quotas at least the down quotas needs the host to compare them).
+ * Negative quotas cannot be checked on the host and keep nothing.  Results are
+ * the same as with the same quotas on the host. */
+#define LRM_QUOTA_ON_DEVICE 4u
+/* Debug checks: lrm_expert_backward synchronises its stream at the end and
+ * returns LRM_ERR_INDEX if a kernel of the call found an expert id or token
+ * out of range, or tokens out of order (what lrm_check_device_errors reports,
+ * and clears, without the extra call). */
+#define LRM_DEBUG_CHECKS 8u
 
 /* The routed pairs of one layer call (the page's "pair": one token -> expert
  * choice; page 1 introduction). */
@@ -271,7 +286,7 @@ size_t lrm_receiver_layout_workspace_size(int32_t E, int32_t G);
 
 typedef struct lrm_problem {
   int32_t kind;    /* lrm_kind */
-  uint32_t flags;  /* LRM_KEEP_ALL or 0 */
+  uint32_t flags;  /* LRM_KEEP_ALL, LRM_DW_BF16, LRM_QUOTA_ON_DEVICE, LRM_DEBUG_CHECKS */
   int32_t dtype;   /* lrm_dtype of every dense input */
   int32_t _pad;
   lrm_pairs pairs;

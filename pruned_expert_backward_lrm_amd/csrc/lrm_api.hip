@@ -168,22 +168,23 @@ SelectWs carve_select(Carve& c, int N, int E) {
 
 // Bucket the pairs by expert and select the top quota of each expert.
 // quota_host == nullptr keeps everything (then kept is filled by the bucket
-// scatter and no keys are gathered).
+// scatter and no keys are gathered); with quota_on_device it is a device
+// pointer, used as it is.
 // tok_off (optional, [T+1]): the first pair of each token, computed on the way
 // when there is at least one pair.  mt_off (optional, [E+1]): the prefix of
 // ceil(M_e / mt_bm), the dX row tiles of the grouped GEMM.
 lrm_status run_select(const lrm_pairs* p, const float* score, const int32_t* quota_host,
                       int32_t* pos, int32_t* offsets, int32_t* kept, const SelectWs& w,
                       hipStream_t s, int32_t* tok_off = nullptr, int32_t* mt_off = nullptr,
-                      int mt_bm = 0) {
+                      int mt_bm = 0, bool quota_on_device = false) {
   const bool keep_all = quota_host == nullptr;
-  if (!keep_all) {
+  if (!keep_all && !quota_on_device) {
     LRM_TRY_HIP(hipMemcpyAsync(w.quota, quota_host, sizeof(int32_t) * p->E,
                                hipMemcpyHostToDevice, s));
   }
   BucketArgs b{};
   b.N = p->N; b.T = p->T; b.E = p->E; b.token = p->token; b.expert = p->expert;
-  b.quota = keep_all ? nullptr : w.quota;
+  b.quota = keep_all ? nullptr : (quota_on_device ? quota_host : w.quota);
   b.score = keep_all ? nullptr : score;
   b.blkcnt = w.blkcnt; b.cand_off = w.cand_off; b.offsets = offsets;
   b.cand = keep_all ? kept : w.cand;
@@ -281,12 +282,17 @@ lrm_status lrm_select(const lrm_pairs* pairs, const float* score, const int32_t*
                       size_t ws_bytes, void* stream) {
   LRM_TRY(check_pairs(pairs));
   const bool keep_all = (flags & LRM_KEEP_ALL) != 0;
-  if (flags & ~LRM_KEEP_ALL) return LRM_ERR_UNSUPPORTED;
+  const bool qdev = (flags & LRM_QUOTA_ON_DEVICE) != 0;
+  if (flags & ~(LRM_KEEP_ALL | LRM_QUOTA_ON_DEVICE)) return LRM_ERR_UNSUPPORTED;
   if (!offsets) return LRM_ERR_NULL;
   if (pairs->N > 0 && (!pos || !kept)) return LRM_ERR_NULL;
   if (!keep_all) {
     if (pairs->N > 0 && !score) return LRM_ERR_NULL;
-    LRM_TRY(check_quota(quota, pairs->E, nullptr));
+    if (qdev) {
+      if (!quota) return LRM_ERR_NULL;
+    } else {
+      LRM_TRY(check_quota(quota, pairs->E, nullptr));
+    }
   }
   Carve c(nullptr);
   carve_select(c, pairs->N, pairs->E);
@@ -294,7 +300,8 @@ lrm_status lrm_select(const lrm_pairs* pairs, const float* score, const int32_t*
   Carve r(ws);
   SelectWs w = carve_select(r, pairs->N, pairs->E);
   hipStream_t s = as_stream(stream);
-  return run_select(pairs, score, keep_all ? nullptr : quota, pos, offsets, kept, w, s);
+  return run_select(pairs, score, keep_all ? nullptr : quota, pos, offsets, kept, w, s, nullptr,
+                    nullptr, 0, qdev);
 }
 
 lrm_status lrm_compact(const lrm_pairs* pairs, const int32_t* kept, const int32_t* offsets,
@@ -544,6 +551,11 @@ GluSizes glu_sizes(const lrm_problem* pb) {
     z.pass_through = true;
     return z;
   }
+  if (pb->flags & LRM_QUOTA_ON_DEVICE) {  // quotas the host cannot read
+    z.Md = z.Mg = z.Mu = N;
+    z.pass_through = false;
+    return z;
+  }
   z.Md = lrm_max_kept(N, E, pb->quota_down);
   z.Mg = lrm_max_kept((int32_t)z.Md, E, pb->quota_gate);
   z.Mu = lrm_max_kept((int32_t)z.Md, E, pb->quota_up);
@@ -559,11 +571,17 @@ GluSizes glu_sizes(const lrm_problem* pb) {
 lrm_status check_problem(const lrm_problem* pb, const lrm_outputs* out) {
   if (!pb) return LRM_ERR_NULL;
   LRM_TRY(check_pairs(&pb->pairs));
-  if (pb->flags & ~(LRM_KEEP_ALL | LRM_DW_BF16)) return LRM_ERR_UNSUPPORTED;
+  if (pb->flags & ~(LRM_KEEP_ALL | LRM_DW_BF16 | LRM_QUOTA_ON_DEVICE | LRM_DEBUG_CHECKS))
+    return LRM_ERR_UNSUPPORTED;
   if (pb->dtype != LRM_F32 && pb->dtype != LRM_BF16) return LRM_ERR_DTYPE;
   if ((pb->flags & LRM_DW_BF16) && pb->dtype != LRM_BF16) return LRM_ERR_UNSUPPORTED;
   const lrm_pairs* p = &pb->pairs;
   const bool keep_all = (pb->flags & LRM_KEEP_ALL) != 0;
+  const bool qdev = (pb->flags & LRM_QUOTA_ON_DEVICE) != 0;
+  // host quotas are checked (non-negative); device quotas only for presence
+  auto check_q = [&](const int32_t* q) {
+    return qdev ? (q ? LRM_OK : LRM_ERR_NULL) : check_quota(q, p->E, nullptr);
+  };
   const int q = 16 / esize(pb->dtype);
   if (pb->kind == LRM_LINEAR) {
     if (pb->d_in <= 0 || pb->d_out <= 0) return LRM_ERR_SHAPE;
@@ -573,7 +591,7 @@ lrm_status check_problem(const lrm_problem* pb, const lrm_outputs* out) {
     if (!aligned16(pb->W)) return LRM_ERR_ALIGN;
     if (pb->w_stride < (int64_t)pb->d_in * pb->d_out) return LRM_ERR_SHAPE;
     if ((pb->w_stride * esize(pb->dtype)) % 16) return LRM_ERR_ALIGN;
-    if (!keep_all) LRM_TRY(check_quota(pb->quota, p->E, nullptr));
+    if (!keep_all) LRM_TRY(check_q(pb->quota));
   } else if (pb->kind == LRM_SWIGLU) {
     if (pb->H <= 0 || pb->I <= 0) return LRM_ERR_SHAPE;
     if (pb->H % q || pb->I % q) return LRM_ERR_UNSUPPORTED;
@@ -586,9 +604,9 @@ lrm_status check_problem(const lrm_problem* pb, const lrm_outputs* out) {
       return LRM_ERR_ALIGN;
     if ((reinterpret_cast<uintptr_t>(pb->h_sumsq) & 7u) != 0) return LRM_ERR_ALIGN;
     if (!keep_all) {
-      LRM_TRY(check_quota(pb->quota_down, p->E, nullptr));
-      LRM_TRY(check_quota(pb->quota_gate, p->E, nullptr));
-      LRM_TRY(check_quota(pb->quota_up, p->E, nullptr));
+      LRM_TRY(check_q(pb->quota_down));
+      LRM_TRY(check_q(pb->quota_gate));
+      LRM_TRY(check_q(pb->quota_up));
     }
   } else {
     return LRM_ERR_UNSUPPORTED;
@@ -612,7 +630,7 @@ lrm_status check_problem(const lrm_problem* pb, const lrm_outputs* out) {
 size_t plan_size(const lrm_problem* pb, const lrm_outputs* out) {
   Carve c(nullptr);
   if (pb->kind == LRM_LINEAR) {
-    const int64_t Mcap = (pb->flags & LRM_KEEP_ALL)
+    const int64_t Mcap = (pb->flags & (LRM_KEEP_ALL | LRM_QUOTA_ON_DEVICE))
                              ? pb->pairs.N
                              : lrm_max_kept(pb->pairs.N, pb->pairs.E, pb->quota);
     carve_linear(c, pb, out, Mcap);
@@ -638,7 +656,8 @@ lrm_status run_linear(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
                       const Marks& mark) {
   const lrm_pairs* p = &pb->pairs;
   const bool keep_all = (pb->flags & LRM_KEEP_ALL) != 0;
-  const int64_t Mcap = keep_all ? p->N : lrm_max_kept(p->N, p->E, pb->quota);
+  const bool qdev = (pb->flags & LRM_QUOTA_ON_DEVICE) != 0;
+  const int64_t Mcap = keep_all || qdev ? p->N : lrm_max_kept(p->N, p->E, pb->quota);
   Carve c(ws);
   LinearPlan L = carve_linear(c, pb, out, Mcap);
   const int bf16 = pb->dtype == LRM_BF16;
@@ -655,7 +674,8 @@ lrm_status run_linear(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   // (the token offsets of the unpermute step come out of the bucketing pass)
   const bool tok_out = pb->X.rows != LRM_ROWS_PAIR;
   LRM_TRY(run_select(p, L.score, keep_all ? nullptr : pb->quota, L.pos, L.offsets, L.kept,
-                     L.sel, s, tok_out && p->N > 0 ? L.tok_off : nullptr, L.mt_off, dx_rows));
+                     L.sel, s, tok_out && p->N > 0 ? L.tok_off : nullptr, L.mt_off, dx_rows,
+                     qdev));
   LRM_TRY_HIP(mark(2));
   // 3. compaction: Xp = w x, Gp = g
   CompactArgs ca{};
@@ -707,8 +727,10 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   LRM_TRY_HIP(mark(1));
   // (the token offsets of the unpermute step come out of the bucketing pass)
   const bool tok_out = pb->X.rows != LRM_ROWS_PAIR;
+  const bool qdev = (pb->flags & LRM_QUOTA_ON_DEVICE) != 0;
   LRM_TRY(run_select(p, L.score, keep_all ? nullptr : pb->quota_down, L.pos, L.offsets, L.kept,
-                     L.sel, s, tok_out && p->N > 0 ? L.tok_off : nullptr, L.mt_off, dx_rows));
+                     L.sel, s, tok_out && p->N > 0 ? L.tok_off : nullptr, L.mt_off, dx_rows,
+                     qdev));
   LRM_TRY_HIP(mark(2));
   CompactArgs cd{};
   cd.T = p->T; cd.bf16 = bf16; cd.max_rows = (int)z.Md; cd.E = E;
@@ -741,15 +763,21 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   LRM_TRY_HIP(mark(5));
   // ---- gate/up selections among the down-kept rows (candidate ids = rows)
   if (!keep_all) {
-    LRM_TRY_HIP(hipMemcpyAsync(L.qgate, pb->quota_gate, sizeof(int32_t) * E,
-                               hipMemcpyHostToDevice, s));
-    LRM_TRY_HIP(hipMemcpyAsync(L.qup, pb->quota_up, sizeof(int32_t) * E, hipMemcpyHostToDevice,
-                               s));
-    LRM_TRY_HIP(launch_kept_offsets(E, L.offsets, L.qgate, L.off_g, s));
+    const int32_t* qg = pb->quota_gate;
+    const int32_t* qu = pb->quota_up;
+    if (!qdev) {
+      LRM_TRY_HIP(hipMemcpyAsync(L.qgate, pb->quota_gate, sizeof(int32_t) * E,
+                                 hipMemcpyHostToDevice, s));
+      LRM_TRY_HIP(hipMemcpyAsync(L.qup, pb->quota_up, sizeof(int32_t) * E,
+                                 hipMemcpyHostToDevice, s));
+      qg = L.qgate;
+      qu = L.qup;
+    }
+    LRM_TRY_HIP(launch_kept_offsets(E, L.offsets, qg, L.off_g, s));
     LRM_TRY_HIP(launch_select(E, L.offsets, L.off_g,
                               reinterpret_cast<const uint32_t*>(L.s_gate), nullptr, L.pos_g,
                               L.kept_g, s));
-    LRM_TRY_HIP(launch_kept_offsets(E, L.offsets, L.qup, L.off_u, s));
+    LRM_TRY_HIP(launch_kept_offsets(E, L.offsets, qu, L.off_u, s));
     LRM_TRY_HIP(launch_select(E, L.offsets, L.off_u, reinterpret_cast<const uint32_t*>(L.s_up),
                               nullptr, L.pos_u, L.kept_u, s));
   }
@@ -843,8 +871,10 @@ lrm_status lrm_expert_backward_events(const lrm_problem* prob, const lrm_outputs
   if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return LRM_ERR_ALIGN;
   hipStream_t s = as_stream(stream);
   const Marks mark{events, n_events, s};
-  if (prob->kind == LRM_LINEAR) return run_linear(prob, out, ws, s, mark);
-  return run_swiglu(prob, out, ws, s, mark);
+  LRM_TRY(prob->kind == LRM_LINEAR ? run_linear(prob, out, ws, s, mark)
+                                   : run_swiglu(prob, out, ws, s, mark));
+  if (prob->flags & LRM_DEBUG_CHECKS) return lrm_check_device_errors(ws, stream);
+  return LRM_OK;
 }
 
 lrm_status lrm_expert_backward(const lrm_problem* prob, const lrm_outputs* out, void* ws,

@@ -32,6 +32,8 @@ LRM_ROWS_TOKEN, LRM_ROWS_PAIR = 0, 1
 LRM_LINEAR, LRM_SWIGLU = 0, 1
 LRM_KEEP_ALL = 1
 LRM_DW_BF16 = 2
+LRM_QUOTA_ON_DEVICE = 4
+LRM_DEBUG_CHECKS = 8
 ROWS = {"token": LRM_ROWS_TOKEN, "pair": LRM_ROWS_PAIR}
 
 
@@ -173,7 +175,13 @@ def _ws(nbytes: int, device, ws):
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
-def _quota_arr(q) -> np.ndarray:
+def _quota_arr(q):
+    """Quotas as the C ABI takes them: a host int32 array, or (with
+    LRM_QUOTA_ON_DEVICE) a contiguous int32 device tensor passed as it is."""
+    if isinstance(q, torch.Tensor) and q.is_cuda:
+        if q.dtype != torch.int32 or not q.is_contiguous():
+            raise ValueError("device quotas must be a contiguous int32 tensor")
+        return q
     return np.ascontiguousarray(np.asarray(q, dtype=np.int32))
 
 

@@ -108,7 +108,9 @@ def run_swiglu(L, p: dict, device: str, flags: int = 0, ws=None, h_sumsq=None):
     pb = L.swiglu_problem(pairs, t["X"], "token", t["G"], "token", t["A"], t["B"], t["W_gate"],
                           t["W_up"], t["W_down"], *q, flags, h_sumsq=hs)
     H, I, E, N = p["H"], p["I"], r.E, r.N
-    Md = N if keep_all else max(L.lrm_max_kept(N, p["quota_down"]), 1)
+    qd = p["quota_down"]
+    qd_host = qd.cpu().numpy() if isinstance(qd, torch.Tensor) else qd
+    Md = N if keep_all else max(L.lrm_max_kept(N, qd_host), 1)
     f32, i32 = dict(dtype=torch.float32, device=device), dict(dtype=torch.int32, device=device)
     nan = float("nan")
     wd = dict(dtype=torch.bfloat16 if flags & L.LRM_DW_BF16 else torch.float32, device=device)

@@ -91,7 +91,7 @@ def test_select_validation():
     assert lib.lrm_select(*args) == 6
     assert lib.lrm_select(C.byref(p), d, None, 0, d, d, d, d, 1 << 24, None) == 1
     q = np.array([1, 2, 3], np.int32)
-    assert lib.lrm_select(C.byref(p), d, q.ctypes.data, 4, d, d, d, d, 1 << 24, None) == 10
+    assert lib.lrm_select(C.byref(p), d, q.ctypes.data, 16, d, d, d, d, 1 << 24, None) == 10
     assert lib.lrm_select(C.byref(p), d, q.ctypes.data, 0, d, d, d, d, 16, None) == 7
 
 
@@ -175,3 +175,33 @@ def test_receiver_layout_validation_returns_before_launch():
     assert lib.lrm_receiver_layout(4, 2, d, d, 8, d, d, d, d, n - 1, None) == 7
     assert lib.lrm_receiver_layout(4, 2, d, d, -1, d, d, d, d, n, None) == 2
 
+
+
+def test_quota_on_device_and_debug_flags():
+    # LRM_QUOTA_ON_DEVICE: the host never reads the quota arrays (a pointer that
+    # is not host memory is fine) and sizes the packed blocks for every pair
+    lib = L._lib
+    pb = L.lrm_problem()
+    pb.kind, pb.dtype = L.LRM_LINEAR, L.LRM_BF16
+    pb.pairs = _pairs(T=16, N=32, E=4)
+    pb.X = _m(cols=64, ld=64)
+    pb.G = _m(rows=L.LRM_ROWS_PAIR, cols=32, ld=32)
+    pb.W, pb.w_stride, pb.d_in, pb.d_out = 0x8000, 64 * 32, 64, 32
+    q_all = np.array([100, 100, 100, 100], np.int32)
+    pb.quota = q_all.ctypes.data
+    n_all = lib.lrm_workspace_size(C.byref(pb))
+    pb.flags = L.LRM_QUOTA_ON_DEVICE
+    pb.quota = 0x10  # a device address: must not be dereferenced on the host
+    assert lib.lrm_workspace_size(C.byref(pb)) == n_all
+    pb.flags = L.LRM_QUOTA_ON_DEVICE | L.LRM_DEBUG_CHECKS | L.LRM_DW_BF16
+    assert lib.lrm_workspace_size(C.byref(pb)) == n_all
+    pb.quota = None
+    assert lib.lrm_workspace_size(C.byref(pb)) == 0
+    pb.quota, pb.flags = 0x10, 16  # not a flag of the ABI
+    assert lib.lrm_workspace_size(C.byref(pb)) == 0
+    # lrm_select: device quotas must be present; the workspace is still checked
+    p = _pairs(E=3)
+    d = C.c_void_p(0x4000)
+    qdev = L.LRM_QUOTA_ON_DEVICE
+    assert lib.lrm_select(C.byref(p), d, None, qdev, d, d, d, d, 1 << 24, None) == 1
+    assert lib.lrm_select(C.byref(p), d, C.c_void_p(0x10), qdev, d, d, d, d, 16, None) == 7

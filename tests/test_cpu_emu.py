@@ -81,9 +81,10 @@ def _raw(t: torch.Tensor) -> bytes:
     return t.numpy().tobytes()
 
 
-def run_emu(exe, tmp_path, p: dict, flags: int = 0, env_extra=None) -> dict:
+def run_emu(exe, tmp_path, p: dict, flags: int = 0, env_extra=None, expect=(0, 0)) -> dict:
     """One fused call of the emulated library.  Returns the outputs as CPU
-    tensors under the keys the GPU parity helpers use."""
+    tensors under the keys the GPU parity helpers use.  `expect`: the status
+    of the call and of lrm_check_device_errors after it (-1: not run)."""
     r = p["routing"]
     N, E, T = r.N, r.E, r.T
     Nr = max(N, 1)
@@ -129,8 +130,8 @@ def run_emu(exe, tmp_path, p: dict, flags: int = 0, env_extra=None) -> dict:
         return torch.from_numpy(a.reshape(shape) if shape else a)
 
     status, dev_status = (int(v) for v in take(2, np.int32))
-    assert status == 0, f"lrm_expert_backward returned {status}"
-    assert dev_status == 0, f"lrm_check_device_errors returned {dev_status}"
+    assert (status, dev_status) == tuple(expect), \
+        f"lrm_expert_backward returned {status}, lrm_check_device_errors {dev_status}"
     out = {}
     if kind == LINEAR:
         out["dW"] = take(E * d_out * d_in, np.float32, (E, d_out, d_in))
@@ -233,3 +234,15 @@ def test_emu_no_pairs(driver, tmp_path, kind):
     for k in keys:
         assert not torch.any(out[k] != 0), f"{k} must be exactly zero"
     assert torch.equal(out["offsets"], torch.zeros(p["E"] + 1, dtype=torch.int32))
+
+
+def test_emu_bad_expert_id(driver, tmp_path):
+    # an expert id out of range: the pair is left out of every step, the call
+    # returns LRM_OK and the device error word reports it (LRM_ERR_INDEX = 8);
+    # with LRM_DEBUG_CHECKS (8) the call itself returns LRM_ERR_INDEX
+    p = synth.make_linear(64, 4, 2, 32, 32, dtype="bf16", seed=9)
+    r = p["routing"]
+    r.expert = r.expert.copy()
+    r.expert[5] = r.E + 3
+    run_emu(driver, tmp_path, p, expect=(0, 8))
+    run_emu(driver, tmp_path, p, flags=8, expect=(8, -1))

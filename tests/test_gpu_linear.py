@@ -404,3 +404,39 @@ def test_fused_linear_max_experts(L):
                           quota=lambda c: (2 * c + 1) // 3)
     s = judge_linear(p, run_linear(L, p, DEV))
     say("  ", s)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fused_linear_quota_on_device(L, dtype):
+    # the same quotas read from device memory (LRM_QUOTA_ON_DEVICE): the same
+    # kept sets and bit-identical gradients (the packed blocks are sized for
+    # every pair, which may pick other tile shapes; each output element is the
+    # same sum in the same order)
+    say("fused linear, device quotas", dtype)
+    p = synth.make_linear(600, 10, 4, 136, 200, dtype=dtype, seed=8, zipf=1.4,
+                          quota=lambda c: (c * 5) // 8 + (c % 3 == 0))
+    host = run_linear(L, p, DEV)
+    pd = dict(p, quota=torch.tensor(p["quota"], dtype=torch.int32, device=DEV))
+    dev = run_linear(L, pd, DEV, flags=L.LRM_QUOTA_ON_DEVICE)
+    for k in ("pos", "offsets", "dW", "dX", "score"):
+        assert torch.equal(torch.nan_to_num(host[k].float()), torch.nan_to_num(dev[k].float())), k
+    judge_linear(p, dev)
+
+
+def test_fused_linear_debug_checks(L):
+    # an expert id out of range: without LRM_DEBUG_CHECKS the call succeeds and
+    # lrm_check_device_errors reports it; with the flag the call itself does
+    say("fused linear, debug checks")
+    p = synth.make_linear(64, 4, 2, 32, 32, dtype="bf16", seed=9)
+    r = p["routing"]
+    r.expert = r.expert.copy()
+    r.expert[5] = r.E + 3
+    res = run_linear(L, p, DEV)
+    assert L.lrm_check_device_errors(res["ws"]) == L.LRM_ERR_INDEX
+    with pytest.raises(L.LrmError) as ex:
+        run_linear(L, p, DEV, flags=L.LRM_DEBUG_CHECKS)
+    assert ex.value.status == L.LRM_ERR_INDEX
+    # a clean call after it reports no error
+    p2 = synth.make_linear(64, 4, 2, 32, 32, dtype="bf16", seed=9)
+    res = run_linear(L, p2, DEV, flags=L.LRM_DEBUG_CHECKS)
+    judge_linear(p2, res)

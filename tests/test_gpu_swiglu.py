@@ -163,3 +163,22 @@ def test_fused_swiglu_no_pairs(L, dtype):
     for k in ("dW_gate", "dW_up", "dW_down", "dX"):
         assert not torch.any(res[k] != 0), f"{k} must be exactly zero"
     assert torch.equal(res["offsets"], torch.zeros(E + 1, dtype=torch.int32))
+
+
+@pytest.mark.parametrize("variant", ["same", "second"])
+def test_fused_swiglu_quota_on_device(L, variant):
+    # quotas in device memory: the call always runs the gate/up selections
+    # (the host cannot compare the quotas), so the result must meet the oracle;
+    # with a real second selection both runs take that path and agree bit for bit
+    say("swiglu, device quotas", variant)
+    p = synth.make_swiglu(400, 6, 2, 136, 72, dtype="bf16", seed=5, zipf=1.2,
+                          quotas=QUOTAS[variant], g_std=1e-2)
+    t = lambda q: torch.tensor(q, dtype=torch.int32, device=DEV)  # noqa: E731
+    pd = dict(p, quota_down=t(p["quota_down"]), quota_gate=t(p["quota_gate"]),
+              quota_up=t(p["quota_up"]))
+    dev = run_swiglu(L, pd, DEV, flags=L.LRM_QUOTA_ON_DEVICE)
+    judge_swiglu(p, dev)
+    if variant == "second":
+        host = run_swiglu(L, p, DEV)
+        for k in ("dW_gate", "dW_up", "dW_down", "dX", "pos", "offsets"):
+            assert torch.equal(torch.nan_to_num(host[k].float()), torch.nan_to_num(dev[k].float())), k
