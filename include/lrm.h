@@ -164,8 +164,11 @@ lrm_status lrm_score_glu(const lrm_pairs* pairs, const lrm_mat* A, const lrm_mat
  *                          the first offsets[E] entries are written)
  *   pos      device [N]:   packed row of p, or -1 if p is dropped
  * quota: HOST [E] int32 (fixed by a controller for the call), copied
- * stream-ordered into ws; negative quotas are rejected (LRM_ERR_QUOTA).
- * flags: LRM_KEEP_ALL ignores score and quota and keeps every pair.
+ * stream-ordered into ws; negative quotas are rejected (LRM_ERR_QUOTA).  With
+ * LRM_QUOTA_ON_DEVICE it is a device [E] int32 array read by the kernels
+ * (negative entries keep nothing).
+ * flags: LRM_KEEP_ALL ignores score and quota and keeps every pair;
+ * LRM_QUOTA_ON_DEVICE as above; other bits: LRM_ERR_UNSUPPORTED.
  * ws: device scratch of lrm_select_workspace_size(pairs) bytes; its first word
  * receives device-detected index errors (see lrm_check_device_errors). */
 lrm_status lrm_select(const lrm_pairs* pairs, const float* score, const int32_t* quota,
@@ -353,7 +356,12 @@ typedef struct lrm_outputs {
  *           the down-kept pairs -> compact -> grouped GEMMs (dW_gate, dW_up,
  *           dX rows) -> unpermute.
  * With LRM_KEEP_ALL every pair is kept and no score or select runs (the
- * unpruned baseline on the same kernels).
+ * unpruned baseline on the same kernels).  With LRM_DEBUG_CHECKS the call
+ * synchronises its stream at the end and returns LRM_ERR_INDEX when a kernel
+ * found an index error (the only flag that makes the call synchronous).
+ * "max down rows" is min(N, sum of quota_down), or N with LRM_KEEP_ALL; with
+ * LRM_QUOTA_ON_DEVICE the caller, which knows its quotas, sizes those outputs
+ * by the same rule (only rows of kept pairs are written).
  * ws: device scratch of lrm_workspace_size(prob) bytes, 256-byte aligned. */
 lrm_status lrm_expert_backward(const lrm_problem* prob, const lrm_outputs* out, void* ws,
                                size_t ws_bytes, void* stream);
