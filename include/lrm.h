@@ -163,8 +163,9 @@ lrm_status lrm_score_glu(const lrm_pairs* pairs, const lrm_mat* A, const lrm_mat
  *   kept     device [N]:   kept[offsets[e] + i] = i-th kept pair of e (only
  *                          the first offsets[E] entries are written)
  *   pos      device [N]:   packed row of p, or -1 if p is dropped
- * quota: HOST [E] int32 (fixed by a controller for the call), copied
- * stream-ordered into ws; negative quotas are rejected (LRM_ERR_QUOTA).  With
+ * quota: HOST [E] int32 (fixed by a controller for the call), read during the
+ * call (passed with the kernel arguments for E <= 512, else copied
+ * stream-ordered into ws); negative quotas are rejected (LRM_ERR_QUOTA).  With
  * LRM_QUOTA_ON_DEVICE it is a device [E] int32 array read by the kernels
  * (negative entries keep nothing).
  * flags: LRM_KEEP_ALL ignores score and quota and keeps every pair;
@@ -295,7 +296,8 @@ typedef struct lrm_problem {
   lrm_pairs pairs;
   /* LINEAR: one projection y = W_e x per pair.  X: saved input (d_in cols,
    * TOKEN or PAIR), G: incoming gradient at the output (d_out cols, TOKEN or
-   * PAIR), W: device [E][d_out][d_in] at stride w_stride, quota: HOST [E]. */
+   * PAIR), W: device [E][d_out][d_in] at stride w_stride, quota: HOST [E]
+   * (device [E] with LRM_QUOTA_ON_DEVICE). */
   lrm_mat X;
   lrm_mat G;
   const void* W;
@@ -306,7 +308,8 @@ typedef struct lrm_problem {
    * (H cols, TOKEN), G: incoming gradient at the layer output (H cols,
    * TOKEN), A, B: saved gate/up pre-activations (I cols, PAIR), weights
    * W_gate, W_up device [E][I][H], W_down device [E][H][I] (dense, stride
-   * I*H), quotas HOST [E] per projection. */
+   * I*H), quotas HOST [E] per projection (device [E] with
+   * LRM_QUOTA_ON_DEVICE).  Host quotas are read during the call. */
   lrm_mat A;
   lrm_mat B;
   const void* W_gate;

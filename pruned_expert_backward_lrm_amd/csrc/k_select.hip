@@ -84,7 +84,8 @@ __global__ __launch_bounds__(kSelThreads) void k_bucket_scan(int nblk, int E,
                                                              const uint32_t* __restrict__ blkerr,
                                                              uint32_t* __restrict__ err,
                                                              int32_t* __restrict__ mt_off,
-                                                             int mt_bm) {
+                                                             int mt_bm, QuotaPack qp,
+                                                             int use_qp) {
   LRM_DYN_SHARED(int, counts);  // [2E]: counts, then kept counts min(quota, count)
   __shared__ int lds[kSelThreads / kWave + 1];
   __shared__ uint32_t eor;
@@ -94,7 +95,10 @@ __global__ __launch_bounds__(kSelThreads) void k_bucket_scan(int nblk, int E,
   uint32_t bad = 0u;
   for (int b = threadIdx.x; b < nblk; b += kSelThreads) bad |= blkerr[b];
   int* mcount = counts + E;
-  auto quota_of = [&](int e) { return quota ? max(quota[e], 0) : 0x7fffffff; };
+  // quotas: device array, or by value (E <= kQuotaPackMax), or keep all
+  auto quota_of = [&](int e) {
+    return quota ? max(quota[e], 0) : (use_qp ? max(qp.q[e], 0) : 0x7fffffff);
+  };
   const int q0 = threadIdx.x < E ? quota_of(threadIdx.x) : 0;
   const int w = threadIdx.x >> 6, l = lane_id();
   constexpr int NW = kSelThreads / kWave;
@@ -157,13 +161,15 @@ __global__ __launch_bounds__(kSelThreads) void k_bucket_scan(int nblk, int E,
 __global__ __launch_bounds__(kSelThreads) void k_kept_offsets(int E,
                                                               const int32_t* __restrict__ cand_off,
                                                               const int32_t* __restrict__ quota,
-                                                              int32_t* __restrict__ offsets) {
+                                                              int32_t* __restrict__ offsets,
+                                                              QuotaPack qp, int use_qp) {
   __shared__ int lds[kSelThreads / kWave + 1];
   block_scan_array<kSelThreads>(
       E,
       [&](int e) {
         const int n = cand_off[e + 1] - cand_off[e];
-        return quota ? min(max(quota[e], 0), n) : n;
+        if (quota) return min(max(quota[e], 0), n);
+        return use_qp ? min(max(qp.q[e], 0), n) : n;
       },
       offsets, lds);
 }
@@ -414,9 +420,11 @@ hipError_t launch_bucket(const BucketArgs& a, hipStream_t s) {
                                                         a.expert, a.blkcnt, a.blkerr, a.tok_off);
   }
   if (a.mt_off && a.mt_bm < 1) return hipErrorInvalidValue;
-  LRM_LAUNCH(1, kSelThreads, 2 * a.E * sizeof(int), s, k_bucket_scan)(nblk, a.E, a.blkcnt, a.quota,
-                                                          a.cand_off, a.offsets, a.blkerr,
-                                                          a.err, a.mt_off, a.mt_bm);
+  const bool use_qp = !a.quota && a.qpack;
+  if (use_qp && a.E > kQuotaPackMax) return hipErrorInvalidValue;
+  LRM_LAUNCH(1, kSelThreads, 2 * a.E * sizeof(int), s, k_bucket_scan)(
+      nblk, a.E, a.blkcnt, a.quota, a.cand_off, a.offsets, a.blkerr, a.err, a.mt_off, a.mt_bm,
+      use_qp ? *a.qpack : QuotaPack{}, use_qp ? 1 : 0);
   if (a.N > 0) {
     LRM_LAUNCH(nblk, 64, a.E * sizeof(int), s, k_bucket_scatter)(a.N, a.T, a.E, chunk, a.token,
                                                          a.expert, a.blkcnt, a.cand_off, a.score,
@@ -433,8 +441,11 @@ hipError_t launch_select(int E, const int32_t* cand_off, const int32_t* offsets,
 }
 
 hipError_t launch_kept_offsets(int E, const int32_t* cand_off, const int32_t* quota,
-                               int32_t* offsets, hipStream_t s) {
-  LRM_LAUNCH(1, kSelThreads, 0, s, k_kept_offsets)(E, cand_off, quota, offsets);
+                               const QuotaPack* qpack, int32_t* offsets, hipStream_t s) {
+  const bool use_qp = !quota && qpack;
+  if (use_qp && E > kQuotaPackMax) return hipErrorInvalidValue;
+  LRM_LAUNCH(1, kSelThreads, 0, s, k_kept_offsets)(E, cand_off, quota, offsets,
+                                                   use_qp ? *qpack : QuotaPack{}, use_qp ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -33,11 +33,20 @@ struct ScoreOperands {
 hipError_t launch_pair_score(const ScoreOperands& op, hipStream_t s);
 
 // -------------------------------------------------------------- select
+// Quotas of at most kQuotaPackMax experts, passed by value in the kernel
+// arguments (2 KB): the host array is read at the call, and no copy
+// operation is enqueued on the stream.
+constexpr int kQuotaPackMax = 512;
+struct QuotaPack {
+  int32_t q[kQuotaPackMax];
+};
+
 struct BucketArgs {
   int N, T, E;
   const int32_t* token;
   const int32_t* expert;
-  const int32_t* quota;  // device [E] or nullptr (keep all)
+  const int32_t* quota;  // device [E], or nullptr: qpack, or keep all
+  const QuotaPack* qpack;  // host: quotas by value (E <= kQuotaPackMax), or nullptr
   const float* score;    // nullptr: no keys gathered
   int32_t* blkcnt;       // [E][bucket_blocks(N)]
   int32_t* cand_off;     // [E+1]
@@ -56,7 +65,10 @@ hipError_t launch_bucket(const BucketArgs& a, hipStream_t s);
 hipError_t launch_select(int E, const int32_t* cand_off, const int32_t* offsets,
                          const uint32_t* keys, const int32_t* cand, int32_t* pos, int32_t* kept,
                          hipStream_t s);
+// quota: device [E]; or qpack (host, by value, E <= kQuotaPackMax) when quota
+// is nullptr; both nullptr: keep all.
 hipError_t launch_kept_offsets(int E, const int32_t* cand_off, const int32_t* quota,
+                               const QuotaPack* qpack,
                                int32_t* offsets, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
 hipError_t launch_token_offsets(int N, int T, const int32_t* token, int32_t* tok_off,

@@ -178,13 +178,19 @@ lrm_status run_select(const lrm_pairs* p, const float* score, const int32_t* quo
                       hipStream_t s, int32_t* tok_off = nullptr, int32_t* mt_off = nullptr,
                       int mt_bm = 0, bool quota_on_device = false) {
   const bool keep_all = quota_host == nullptr;
-  if (!keep_all && !quota_on_device) {
+  // host quotas of up to kQuotaPackMax experts go by value with the scan's
+  // launch; more are copied stream-ordered into the workspace
+  const bool by_value = !keep_all && !quota_on_device && p->E <= kQuotaPackMax;
+  QuotaPack pack;
+  if (by_value) std::memcpy(pack.q, quota_host, sizeof(int32_t) * p->E);
+  if (!keep_all && !quota_on_device && !by_value) {
     LRM_TRY_HIP(hipMemcpyAsync(w.quota, quota_host, sizeof(int32_t) * p->E,
                                hipMemcpyHostToDevice, s));
   }
   BucketArgs b{};
   b.N = p->N; b.T = p->T; b.E = p->E; b.token = p->token; b.expert = p->expert;
-  b.quota = keep_all ? nullptr : (quota_on_device ? quota_host : w.quota);
+  b.quota = keep_all || by_value ? nullptr : (quota_on_device ? quota_host : w.quota);
+  b.qpack = by_value ? &pack : nullptr;
   b.score = keep_all ? nullptr : score;
   b.blkcnt = w.blkcnt; b.cand_off = w.cand_off; b.offsets = offsets;
   b.cand = keep_all ? kept : w.cand;
@@ -763,9 +769,16 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   LRM_TRY_HIP(mark(5));
   // ---- gate/up selections among the down-kept rows (candidate ids = rows)
   if (!keep_all) {
+    // quotas: device arrays, by value (host, E <= kQuotaPackMax), or copied
     const int32_t* qg = pb->quota_gate;
     const int32_t* qu = pb->quota_up;
-    if (!qdev) {
+    QuotaPack pg, pu;
+    const bool by_value = !qdev && E <= kQuotaPackMax;
+    if (by_value) {
+      std::memcpy(pg.q, pb->quota_gate, sizeof(int32_t) * E);
+      std::memcpy(pu.q, pb->quota_up, sizeof(int32_t) * E);
+      qg = qu = nullptr;
+    } else if (!qdev) {
       LRM_TRY_HIP(hipMemcpyAsync(L.qgate, pb->quota_gate, sizeof(int32_t) * E,
                                  hipMemcpyHostToDevice, s));
       LRM_TRY_HIP(hipMemcpyAsync(L.qup, pb->quota_up, sizeof(int32_t) * E,
@@ -773,11 +786,11 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
       qg = L.qgate;
       qu = L.qup;
     }
-    LRM_TRY_HIP(launch_kept_offsets(E, L.offsets, qg, L.off_g, s));
+    LRM_TRY_HIP(launch_kept_offsets(E, L.offsets, qg, by_value ? &pg : nullptr, L.off_g, s));
     LRM_TRY_HIP(launch_select(E, L.offsets, L.off_g,
                               reinterpret_cast<const uint32_t*>(L.s_gate), nullptr, L.pos_g,
                               L.kept_g, s));
-    LRM_TRY_HIP(launch_kept_offsets(E, L.offsets, qu, L.off_u, s));
+    LRM_TRY_HIP(launch_kept_offsets(E, L.offsets, qu, by_value ? &pu : nullptr, L.off_u, s));
     LRM_TRY_HIP(launch_select(E, L.offsets, L.off_u, reinterpret_cast<const uint32_t*>(L.s_up),
                               nullptr, L.pos_u, L.kept_u, s));
   }
