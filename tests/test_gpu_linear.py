@@ -440,3 +440,47 @@ def test_fused_linear_debug_checks(L):
     p2 = synth.make_linear(64, 4, 2, 32, 32, dtype="bf16", seed=9)
     res = run_linear(L, p2, DEV, flags=L.LRM_DEBUG_CHECKS)
     judge_linear(p2, res)
+
+
+def _graph_replays(L, pb, out, ws, n=3):
+    """Capture one fused call in a HIP graph, replay it n times with eager work
+    in between (the outputs overwritten), and return the outputs of each replay."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        L.lrm_expert_backward(pb, out, ws=ws)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        L.lrm_expert_backward(pb, out, ws=ws)
+    got = []
+    for _ in range(n):
+        for v in out.values():  # eager work between the replays
+            v.fill_(-7) if v.dtype == torch.int32 else v.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got.append({k: v.cpu().clone() for k, v in out.items()})
+    return got
+
+
+def test_fused_linear_graph_replay(L):
+    # the fused call is only kernel launches (host quotas go in the kernel
+    # arguments), so it can be captured in a HIP graph and replayed
+    say("fused linear, graph replay")
+    p = synth.make_linear(600, 10, 4, 136, 200, dtype="bf16", seed=8, zipf=1.4,
+                          quota=lambda c: (c * 5) // 8 + (c % 3 == 0))
+    eager = run_linear(L, p, DEV)
+    r = p["routing"]
+    pairs = L.Pairs.from_routing(r, DEV)
+    X, G, W = (p[k].to(DEV) for k in ("X", "G", "W"))
+    pb = L.linear_problem(pairs, X, "token", G, "pair", W, p["quota"])
+    out = dict(dW=torch.empty(r.E, p["d_out"], p["d_in"], device=DEV),
+               dX=torch.empty(r.T, p["d_in"], device=DEV),
+               pos=torch.empty(r.N, dtype=torch.int32, device=DEV),
+               offsets=torch.empty(r.E + 1, dtype=torch.int32, device=DEV))
+    ws = torch.empty(L.lrm_workspace_size(pb), dtype=torch.uint8, device=DEV)
+    for got in _graph_replays(L, pb, out, ws):
+        for k in out:
+            assert torch.equal(got[k], eager[k]), k

@@ -182,3 +182,25 @@ def test_fused_swiglu_quota_on_device(L, variant):
         host = run_swiglu(L, p, DEV)
         for k in ("dW_gate", "dW_up", "dW_down", "dX", "pos", "offsets"):
             assert torch.equal(torch.nan_to_num(host[k].float()), torch.nan_to_num(dev[k].float())), k
+
+
+@pytest.mark.parametrize("variant", ["same", "second"])
+def test_fused_swiglu_graph_replay(L, variant):
+    say("swiglu, graph replay", variant)
+    from test_gpu_linear import _graph_replays
+    p = synth.make_swiglu(400, 6, 2, 136, 72, dtype="bf16", seed=5, zipf=1.2,
+                          quotas=QUOTAS[variant], g_std=1e-2)
+    eager = run_swiglu(L, p, DEV)
+    r = p["routing"]
+    pairs = L.Pairs.from_routing(r, DEV)
+    t = {k: p[k].to(DEV) for k in ("X", "G", "A", "B", "W_gate", "W_up", "W_down")}
+    pb = L.swiglu_problem(pairs, t["X"], "token", t["G"], "token", t["A"], t["B"], t["W_gate"],
+                          t["W_up"], t["W_down"], p["quota_down"], p["quota_gate"], p["quota_up"])
+    E, H, I = r.E, p["H"], p["I"]
+    out = dict(dW_gate=torch.empty(E, I, H, device=DEV), dW_up=torch.empty(E, I, H, device=DEV),
+               dW_down=torch.empty(E, H, I, device=DEV), dX=torch.empty(r.T, H, device=DEV),
+               pos=torch.empty(r.N, dtype=torch.int32, device=DEV))
+    ws = torch.empty(L.lrm_workspace_size(pb), dtype=torch.uint8, device=DEV)
+    for got in _graph_replays(L, pb, out, ws):
+        for k in out:
+            assert torch.equal(got[k], eager[k]), k
