@@ -644,7 +644,9 @@ def main():
         kernels = gemm_kernels(W, a.steps, a.warmup)
         name = max(kernels, key=lambda k: kernels[k]["ms"])
         kd = kernels[name]
-        kname = {"dW": "k_gemm_stream<dW>", "dX": "k_gemm_stream<dX>"}[name]
+        # bf16 runs the two stream kernels; fp32 one tiled FMA kernel over either tile kind
+        kname = (f"k_gemm_stream<{name}>" if p["dtype"] == "bf16"
+                 else f"k_grouped_gemm_f32 ({name} tiles)")
         k_ai, k_t = kd["flops"] / kd["bytes"], kd["ms"] * 1e-3
         k_gbs, k_tf = kd["bytes"] / k_t / 1e9, kd["flops"] / k_t / 1e12
         traffic = traffic_of(kname, workload)
