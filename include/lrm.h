@@ -197,7 +197,8 @@ lrm_status lrm_compact(const lrm_pairs* pairs, const int32_t* kept, const int32_
  * W: device, expert e at W + e*w_stride elements, [d_out][d_in] row-major.
  * dtype applies to Gp, Xp, W; bf16 runs on MFMA with fp32 accumulation, fp32
  * with fp32 FMA.  dW or dXp may be NULL to skip that product (W may then be
- * NULL).  Rows of dXp at or beyond offsets[E] are not written.
+ * NULL).  Rows of dXp at or beyond offsets[E] are not written.  d_in and d_out
+ * are each 1..2^20-1 (LRM_ERR_SHAPE otherwise).
  * ws: device scratch of lrm_grouped_bwd_workspace_size(E) bytes. */
 lrm_status lrm_grouped_bwd(int32_t E, const int32_t* offsets, int32_t max_rows, int32_t dtype,
                            const void* Gp, const void* Xp, const void* W, int64_t w_stride,
@@ -302,7 +303,7 @@ typedef struct lrm_problem {
   lrm_mat G;
   const void* W;
   int64_t w_stride;
-  int32_t d_in, d_out;
+  int32_t d_in, d_out;   /* each 1..2^20-1 */
   const int32_t* quota;
   /* SWIGLU: expert MLP W_down (silu(W_gate x) * (W_up x)).  X: saved input
    * (H cols, TOKEN), G: incoming gradient at the layer output (H cols,
@@ -315,7 +316,7 @@ typedef struct lrm_problem {
   const void* W_gate;
   const void* W_up;
   const void* W_down;
-  int32_t H, I;
+  int32_t H, I;          /* each 1..2^20-1 */
   const int32_t* quota_down;
   const int32_t* quota_gate;
   const int32_t* quota_up;

@@ -351,45 +351,63 @@ __device__ __forceinline__ Job make_job(const GemmPlan& P, int t) {
   return j;
 }
 
-// Writes a tile's accumulators (or zeros) within its valid rows and columns.
-// Lane l holds C[row = .. + (l & 15)][col = .. + (l >> 4) * 4 + 0..3].
-template <class C>
-__device__ __forceinline__ void write_tile(const f32x4 (&acc)[C::FM][C::FN], bool zero,
-                                           float* out, int64_t ldc, int rows, int cols) {
-  const int l = lane_id(), w = threadIdx.x >> 6;
-  const int wm = w / C::WGN, wn = w % C::WGN;
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
-    const int row = wm * C::TM + i * 16 + (l & 15);
-    if (row >= rows) continue;
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      const int col = wn * C::TN + j * 16 + (l >> 4) * 4;
-      if (col < cols)
-        *reinterpret_cast<f32x4*>(out + (int64_t)row * ldc + col) =
-            zero ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[i][j];
-    }
-  }
+// Tile stores are raw buffer stores through one resource per tile, bounded
+// by the tile's last valid element.  Lanes outside the valid rows and columns
+// take an offset past the bound, and the hardware drops their stores, so the
+// stores need no per-lane branches, and each takes one offset register where
+// a global store takes a 64-bit address (the 256x256 kernels: 242-245 VGPRs
+// instead of 256).
+constexpr int kOobOff = 0x7fff0000;  // past every tile's bound (tiles span < 1 GiB)
+
+__device__ __forceinline__ void bstore16(rsrc_t r, int off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void bstore8(rsrc_t r, int off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
 }
 
-// The same tile rounded to bf16 (nearest even): 4 columns per lane as 8 bytes.
-template <class C>
-__device__ __forceinline__ void write_tile_bf16(const f32x4 (&acc)[C::FM][C::FN], bool zero,
-                                                uint16_t* out, int64_t ldc, int rows, int cols) {
+// A wave-uniform value the compiler cannot see through: offsets built from it
+// are computed where the stores are, not hoisted out of the tile loop (where
+// the 32 per-store offsets would take 32 live registers).
+#ifdef LRM_CPU_EMU
+__device__ __forceinline__ int opaque_uniform(int x) { return x; }
+#else
+__device__ __forceinline__ int opaque_uniform(int x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+#endif
+
+// Writes a tile's accumulators (or zeros) within its valid rows and columns
+// (rows <= 0: nothing is written, but every store is still issued).  Elements
+// of ES bytes; lane l holds C[row = .. + (l & 15)][col = .. + (l >> 4) * 4 + 0..3].
+// ldc < 2^20 (checked by the launcher), so a tile spans less than 1 GiB.
+template <class C, bool BF16>
+__device__ __forceinline__ void write_tile(const f32x4 (&acc)[C::FM][C::FN], bool zero,
+                                           void* out, int64_t ldc, int rows, int cols) {
+  constexpr int ES = BF16 ? 2 : 4;
   const int l = lane_id(), w = threadIdx.x >> 6;
   const int wm = w / C::WGN, wn = w % C::WGN;
+  const int64_t extent = (rows > 0 && cols > 0) ? ((int64_t)(rows - 1) * ldc + cols) * ES : 0;
+  const rsrc_t rs = make_rsrc((const char*)out, extent);
+  const int ld = opaque_uniform((int)ldc);
+  const int row0 = wm * C::TM + (l & 15), col0 = wn * C::TN + (l >> 4) * 4;
+  const int base = (row0 * ld + col0) * ES;
+  const int rr = rows - row0, cc = cols - col0;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
-    const int row = wm * C::TM + i * 16 + (l & 15);
-    if (row >= rows) continue;
+    const int bi = base + i * 16 * ld * ES;
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
-      const int col = wn * C::TN + j * 16 + (l >> 4) * 4;
-      if (col < cols) {
+      const bool ok = i * 16 < rr && j * 16 < cc;
+      const int off = (ok ? bi : kOobOff) + j * 16 * ES;
+      if constexpr (BF16) {
         u32x2 v;
         v[0] = zero ? 0u : pack_bf16x2(acc[i][j][0], acc[i][j][1]);
         v[1] = zero ? 0u : pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-        *reinterpret_cast<u32x2*>(out + (int64_t)row * ldc + col) = v;
+        bstore8(rs, off, v);
+      } else {
+        bstore16(rs, off, zero ? u32x4{0u, 0u, 0u, 0u} : __builtin_bit_cast(u32x4, acc[i][j]));
       }
     }
   }
@@ -401,10 +419,10 @@ template <class C, bool DWB>
 __device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x4 (&acc)[C::FM][C::FN],
                                            bool zero, float* out, int rows, int cols) {
   if constexpr (DWB)
-    write_tile_bf16<C>(acc, zero, reinterpret_cast<uint16_t*>(a.dW) + (out - a.dW), a.d_in,
-                       rows, cols);
+    write_tile<C, true>(acc, zero, reinterpret_cast<uint16_t*>(a.dW) + (out - a.dW), a.d_in,
+                        rows, cols);
   else
-    write_tile<C>(acc, zero, out, a.d_in, rows, cols);
+    write_tile<C, false>(acc, zero, out, a.d_in, rows, cols);
 }
 
 // MFMAs of k-granules kk..kk+3 (lane group l >> 4 takes granule kk + (l >> 4))
@@ -554,24 +572,29 @@ __device__ __forceinline__ void gemm_stream(const GemmPlan& P) {
   st.store(As, Bs);
   LRM_ISSUE_LOAD();
   __syncthreads();
+  int it = 0;
+  // One k-tile: MFMAs on the current stage, the next k-tile's registers into
+  // the idle stage, the load two k-tiles ahead.
+#define LRM_KSTEP()                                                             \
+  {                                                                             \
+    const int cur = C::STAGES == 2 ? (it & 1) : 0;                              \
+    const uint16_t* Ac = As + cur * (C::BM * BK);                               \
+    const uint16_t* Bc = Bs + cur * (C::BN * BK);                               \
+    mma_k32<C>(acc, Ac, Bc, 0);                                                 \
+    if constexpr (C::STAGES == 2)                                               \
+      st.store(As + (cur ^ 1) * (C::BM * BK), Bs + (cur ^ 1) * (C::BN * BK));   \
+    if constexpr (kEarlyLoad) LRM_ISSUE_LOAD();                                 \
+    mma_k32<C>(acc, Ac, Bc, 4);                                                 \
+    if constexpr (C::STAGES == 1) {                                             \
+      __syncthreads();                                                          \
+      st.store(As, Bs);                                                         \
+    }                                                                           \
+    if constexpr (!kEarlyLoad) LRM_ISSUE_LOAD();                                \
+    ++it;                                                                       \
+  }
   int kc = 0;
-  for (int it = 0;; ++it) {
-    const int cur = C::STAGES == 2 ? (it & 1) : 0;
-    const uint16_t* Ac = As + cur * (C::BM * BK);
-    const uint16_t* Bc = Bs + cur * (C::BN * BK);
-    mma_k32<C>(acc, Ac, Bc, 0);
-    if constexpr (C::STAGES == 2) {
-      // the next k-tile of the stream into the idle stage (stale registers
-      // past the stream's end: the stage they fill is then never read)
-      st.store(As + (cur ^ 1) * (C::BM * BK), Bs + (cur ^ 1) * (C::BN * BK));
-    }
-    if constexpr (kEarlyLoad) LRM_ISSUE_LOAD();
-    mma_k32<C>(acc, Ac, Bc, 4);
-    if constexpr (C::STAGES == 1) {
-      __syncthreads();  // every wave is done with the stage
-      st.store(As, Bs);
-    }
-    if constexpr (!kEarlyLoad) LRM_ISSUE_LOAD();
+  for (;;) {
+    LRM_KSTEP();
     if (++kc == jc.nk) {
       store_tile<C, DWB>(a, acc, false, jc.C, jc.rows, jc.cols);
 #pragma unroll
@@ -588,6 +611,7 @@ __device__ __forceinline__ void gemm_stream(const GemmPlan& P) {
     }
     __syncthreads();
   }
+#undef LRM_KSTEP
 #undef LRM_ISSUE_LOAD
 }
 
@@ -839,6 +863,8 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s) {
       (a.dW && a.max_rows > 0 && !a.Xp) || (a.Gp2 && (!a.W2 || a.d_out2 != a.d_out)))
     return hipErrorInvalidValue;
   if (a.bf16) {
+    // 32-bit store offsets inside a tile (the public entry points check this)
+    if (a.d_in >= (1 << 20) || a.d_out >= (1 << 20)) return hipErrorInvalidValue;
     switch (gemm_tile_choice(a)) {
       case 3: return launch_bf16<CfgL, CfgXS>(a, s);
       case 2: return launch_bf16<CfgL, CfgL>(a, s);

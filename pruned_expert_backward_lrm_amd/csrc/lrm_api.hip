@@ -12,6 +12,9 @@ using namespace lrm;
 namespace {
 
 constexpr int kMaxE = 4096;
+// GEMM leading dimensions: a 256-row output tile spans less than 1 GiB, so
+// its stores take 32-bit offsets
+constexpr int kMaxDim = (1 << 20) - 1;
 constexpr size_t kAlign = 256;
 
 // Bump allocator over a caller workspace.  With base == nullptr it only
@@ -340,7 +343,9 @@ lrm_status lrm_grouped_bwd(int32_t E, const int32_t* offsets, int32_t max_rows, 
                            const void* Gp, const void* Xp, const void* W, int64_t w_stride,
                            int32_t d_in, int32_t d_out, float* dW, float* dXp, void* ws,
                            size_t ws_bytes, void* stream) {
-  if (E < 1 || E > kMaxE || max_rows < 0 || d_in <= 0 || d_out <= 0) return LRM_ERR_SHAPE;
+  if (E < 1 || E > kMaxE || max_rows < 0 || d_in <= 0 || d_out <= 0 || d_in > kMaxDim ||
+      d_out > kMaxDim)
+    return LRM_ERR_SHAPE;
   if (dtype != LRM_F32 && dtype != LRM_BF16) return LRM_ERR_DTYPE;
   const int q = 16 / esize(dtype);
   if (d_in % q || d_out % q) return LRM_ERR_UNSUPPORTED;
@@ -590,7 +595,8 @@ lrm_status check_problem(const lrm_problem* pb, const lrm_outputs* out) {
   };
   const int q = 16 / esize(pb->dtype);
   if (pb->kind == LRM_LINEAR) {
-    if (pb->d_in <= 0 || pb->d_out <= 0) return LRM_ERR_SHAPE;
+    if (pb->d_in <= 0 || pb->d_out <= 0 || pb->d_in > kMaxDim || pb->d_out > kMaxDim)
+      return LRM_ERR_SHAPE;
     LRM_TRY(check_mat(&pb->X, p, pb->dtype, pb->d_in, -1));
     LRM_TRY(check_mat(&pb->G, p, pb->dtype, pb->d_out, -1));
     if (p->E > 0 && !pb->W) return LRM_ERR_NULL;
@@ -599,7 +605,7 @@ lrm_status check_problem(const lrm_problem* pb, const lrm_outputs* out) {
     if ((pb->w_stride * esize(pb->dtype)) % 16) return LRM_ERR_ALIGN;
     if (!keep_all) LRM_TRY(check_q(pb->quota));
   } else if (pb->kind == LRM_SWIGLU) {
-    if (pb->H <= 0 || pb->I <= 0) return LRM_ERR_SHAPE;
+    if (pb->H <= 0 || pb->I <= 0 || pb->H > kMaxDim || pb->I > kMaxDim) return LRM_ERR_SHAPE;
     if (pb->H % q || pb->I % q) return LRM_ERR_UNSUPPORTED;
     LRM_TRY(check_mat(&pb->X, p, pb->dtype, pb->H, LRM_ROWS_TOKEN));
     LRM_TRY(check_mat(&pb->G, p, pb->dtype, pb->H, LRM_ROWS_TOKEN));

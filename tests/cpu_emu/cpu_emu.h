@@ -212,6 +212,18 @@ inline u32x4_emu buffer_load16(BufRsrc r, int voff, int soff) {
   if (off >= 0 && off + 16 <= r.n) std::memcpy(&v, r.base + off, 16);
   return v;
 }
+// A store whose bytes are not all below the bound is dropped, as the hardware
+// range check drops the kernels' out-of-range lanes (offsets far past the
+// bound); stores inside the bound reach real memory, checked by ASan.
+typedef unsigned int u32x2_emu __attribute__((ext_vector_type(2)));
+inline void buffer_store16(u32x4_emu v, BufRsrc r, int voff, int soff) {
+  const long long off = (long long)voff + soff;
+  if (off >= 0 && off + 16 <= r.n) std::memcpy(const_cast<char*>(r.base) + off, &v, 16);
+}
+inline void buffer_store8(u32x2_emu v, BufRsrc r, int voff, int soff) {
+  const long long off = (long long)voff + soff;
+  if (off >= 0 && off + 8 <= r.n) std::memcpy(const_cast<char*>(r.base) + off, &v, 8);
+}
 // v_perm_b32: result byte i = byte sel_i of the 8-byte value {s0 (bytes 4..7), s1 (bytes 0..3)}
 inline unsigned perm(unsigned s0, unsigned s1, unsigned sel) {
   const unsigned long long v = ((unsigned long long)s0 << 32) | s1;
@@ -229,6 +241,10 @@ inline unsigned perm(unsigned s0, unsigned s1, unsigned sel) {
 typedef ::emu::BufRsrc __amdgpu_buffer_rsrc_t;
 #define __builtin_amdgcn_make_buffer_rsrc(p, stride, n, flags) ::emu::make_rsrc((p), (n))
 #define __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, aux) ::emu::buffer_load16((r), (voff), (soff))
+#define __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, aux) \
+  ::emu::buffer_store16((v), (r), (voff), (soff))
+#define __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, aux) \
+  ::emu::buffer_store8((v), (r), (voff), (soff))
 #define __builtin_amdgcn_perm(s0, s1, sel) ::emu::perm((s0), (s1), (sel))
 
 namespace emu {
