@@ -104,6 +104,10 @@ def test_grouped_bwd_and_unpermute_validation():
     assert lib.lrm_grouped_bwd(4, None, 4, 1, d, d, d, 64 * 64, 64, 64, d, d, d, 1 << 20,
                                None) == 1
     assert lib.lrm_grouped_bwd(4, d, 4, 1, d, d, d, 64 * 64, 64, 64, d, d, d, 4, None) == 7
+    # leading dimensions up to 2^20 - 1 (32-bit offsets inside a 256-row tile)
+    big = (1 << 20) * 64
+    assert lib.lrm_grouped_bwd(4, d, 4, 1, d, d, d, big, 1 << 20, 64, d, d, d, 1 << 20, None) == 2
+    assert lib.lrm_grouped_bwd(4, d, 4, 1, d, d, d, big, 64, 1 << 20, d, d, d, 1 << 20, None) == 2
     p = _pairs()
     assert lib.lrm_unpermute(C.byref(p), d, d, 64, 5, d, d, 1 << 20, None) == 4
     assert lib.lrm_unpermute(C.byref(p), d, d, 62, 0, d, d, 1 << 20, None) == 10
@@ -136,6 +140,14 @@ def test_expert_backward_validation_and_workspace_size():
     assert lib.lrm_expert_backward(C.byref(pb), C.byref(out), C.c_void_p(0x10000), 16, None) == 7
     pb.quota = np.array([1, -1, 1, 1], np.int32).ctypes.data
     assert lib.lrm_workspace_size(C.byref(pb)) == 0
+    pb.quota = q.ctypes.data
+    # d_in and d_out up to 2^20 - 1
+    pb.X = _m(cols=1 << 20, ld=1 << 20)
+    pb.d_in, pb.w_stride = 1 << 20, (1 << 20) * 32
+    assert lib.lrm_workspace_size(C.byref(pb)) == 0
+    pb.X = _m(cols=(1 << 20) - 8, ld=(1 << 20) - 8)  # bf16 rows stay 16-byte aligned
+    pb.d_in, pb.w_stride = (1 << 20) - 8, ((1 << 20) - 8) * 32
+    assert lib.lrm_workspace_size(C.byref(pb)) > 0
     pb.kind = 5
     assert lib.lrm_workspace_size(C.byref(pb)) == 0
 
@@ -159,6 +171,11 @@ def test_swiglu_workspace_sizes_from_quotas():
     second = lib.lrm_workspace_size(C.byref(pb))
     assert same > 0 and second > 0 and same != second
     pb.A = _m(rows=L.LRM_ROWS_TOKEN, cols=32, ld=32)
+    assert lib.lrm_workspace_size(C.byref(pb)) == 0
+    # H and I up to 2^20 - 1
+    pb.A = _m(rows=L.LRM_ROWS_PAIR, cols=1 << 20, ld=1 << 20)
+    pb.B = _m(rows=L.LRM_ROWS_PAIR, cols=1 << 20, ld=1 << 20)
+    pb.I = 1 << 20
     assert lib.lrm_workspace_size(C.byref(pb)) == 0
 
 
