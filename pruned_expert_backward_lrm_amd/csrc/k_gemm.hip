@@ -561,13 +561,11 @@ __device__ __forceinline__ void gemm_stream(const GemmPlan& P) {
       }                                                                         \
     }                                                                           \
   }
-  // Where the registers allow, the loads of k-tile i+2 are issued as soon as
-  // k-tile i+1 has left the registers for LDS, in the middle of k-tile i's
-  // MFMAs, which gives them a whole k-tile of MFMAs to arrive (issued after
-  // the MFMAs, they get half of one).  256x256 dX tiles keep the late issue:
-  // their larger job state leaves no room for loads in flight across the
-  // second half of the MFMAs.
-  constexpr bool kEarlyLoad = C::STAGES == 2 && (!DX || C::FM * C::FN < 32);
+  // With two LDS stages the loads of k-tile i+2 are issued as soon as k-tile
+  // i+1 has left the registers for LDS, in the middle of k-tile i's MFMAs,
+  // which gives them a whole k-tile of MFMAs to arrive (issued after the
+  // MFMAs, they get half of one).
+  constexpr bool kEarlyLoad = C::STAGES == 2;
   LRM_ISSUE_LOAD();
   st.store(As, Bs);
   LRM_ISSUE_LOAD();
