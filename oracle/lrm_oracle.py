@@ -417,17 +417,3 @@ def swiglu_pair_dx(p: dict, pairs, in_gate, in_up) -> np.ndarray:
             dx += (u * silu(a)) @ f64(p["W_up"][e])
         out[i] = float(r.weight[q]) * dx
     return out
-
-
-def swiglu_dx_tokens(p: dict, ref: dict, tokens: np.ndarray) -> np.ndarray:
-    """dX rows of the listed tokens from a reference whose dx_pairs cover every
-    expert those tokens route to."""
-    r = p["routing"]
-    want = {int(t): i for i, t in enumerate(tokens)}
-    out = np.zeros((len(tokens), p["H"]))
-    for e, (kd, dx) in ref["dx_pairs"].items():
-        for j, pp in enumerate(kd.tolist()):
-            i = want.get(int(r.token[pp]))
-            if i is not None:
-                out[i] += dx[j]
-    return out

@@ -30,6 +30,16 @@ MUTATIONS = {
                            'u = g @ f64(p["W_down"][e]) * 1.0001'),
     "pack_offsets_shifted": ("np.cumsum(sizes, out=offsets[1:])",
                              "np.cumsum(sizes, out=offsets[1:]); offsets[1:] += 1"),
+    # the threshold is the smallest kept score, not the largest
+    "threshold_max_not_min": ("return float(np.min(np.asarray(score, np.float64)[kept_e]))",
+                              "return float(np.max(np.asarray(score, np.float64)[kept_e]))"),
+    # off by one in the kept count: the (M_e - 1)-th largest score, and None
+    # for one kept pair instead of for all kept
+    "threshold_count_off_by_one": ("    m = kept_e.shape[0]\n    if m == 0 or m == n_e:",
+                                   "    m = kept_e.shape[0] - 1\n    if m == 0 or m == n_e:"),
+    # the (M_e + 1)-th largest: the best dropped score instead of the worst kept
+    "threshold_next_below": ("return float(np.min(np.asarray(score, np.float64)[kept_e]))",
+                             "return float(np.sort(np.asarray(score, np.float64))[::-1][m])"),
 }
 
 

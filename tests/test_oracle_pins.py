@@ -446,3 +446,48 @@ def test_swiglu_pair_dx_and_given_kept_sets():
         for k in ("dW_down", "dW_gate", "dW_up"):
             assert np.array_equal(again[k][e], ref[k][e])
     assert np.array_equal(again["dX"], ref["dX"])
+
+
+# ------------------------------------------------------------- threshold
+
+def _bruteforce_threshold(score, expert, quota, e):
+    """The M_e-th largest score of expert e by a Python sort (None when the
+    selection keeps nothing or everything, so there is nothing to decide)."""
+    c = sorted((float(score[q]) for q in range(len(score)) if expert[q] == e), reverse=True)
+    m = min(int(quota[e]), len(c))
+    return None if m in (0, len(c)) else c[m - 1]
+
+
+def test_threshold_hand_cases():
+    # one expert, scores 9 7 4 2 (pair order scrambled), quota 2: the second
+    # largest (7) decides, not the third (4) nor the largest (9)
+    score = np.array([4.0, 9.0, 2.0, 7.0])
+    kept = O.select_top_quota(np.zeros(4, np.int32), score, np.array([2]), 1)[0]
+    assert kept.tolist() == [1, 3]
+    assert O.threshold(score, kept, 4) == 7.0
+    # nothing kept, everything kept: no threshold
+    assert O.threshold(score, np.zeros(0, np.int64), 4) is None
+    assert O.threshold(score, np.arange(4), 4) is None
+    # a single kept pair among several: its own score
+    assert O.threshold(score, np.array([1]), 4) == 9.0
+    # ties straddling the boundary: scores 5 3 3 3 1, quota 2 keeps 5 and the
+    # lowest-index 3; the threshold is 3, equal to the dropped tied pairs
+    score = np.array([5.0, 3.0, 3.0, 3.0, 1.0])
+    kept = O.select_top_quota(np.zeros(5, np.int32), score, np.array([2]), 1)[0]
+    assert kept.tolist() == [0, 1]
+    assert O.threshold(score, kept, 5) == 3.0
+
+
+def test_threshold_against_sorted_scores():
+    rng = np.random.default_rng(21)
+    for trial in range(20):
+        N, E = int(rng.integers(1, 200)), int(rng.integers(1, 6))
+        expert = rng.integers(0, E, N).astype(np.int32)
+        # few distinct values on odd trials: ties at the boundary
+        score = (rng.integers(0, 5, N) if trial % 2 else rng.random(N)).astype(np.float64)
+        quota = rng.integers(0, 60, E)
+        kept = O.select_top_quota(expert, score, quota, E)
+        counts = np.bincount(expert, minlength=E)
+        for e in range(E):
+            assert O.threshold(score, kept[e], int(counts[e])) == \
+                _bruteforce_threshold(score, expert, quota, e)
