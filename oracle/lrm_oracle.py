@@ -316,7 +316,8 @@ def swiglu_gate_up_grads(p: dict, kd: np.ndarray, u: np.ndarray):
 
 
 def swiglu_reference(p: dict, experts=None, keep_all: bool = False,
-                     u_override: dict | None = None, kept: dict | None = None) -> dict:
+                     u_override: dict | None = None, kept: dict | None = None,
+                     grads: bool = True) -> dict:
     """The SwiGLU expert backward (reading R-glu), expert by expert.
 
     ``experts`` limits which experts' weight gradients and pair gradients are
@@ -327,6 +328,7 @@ def swiglu_reference(p: dict, experts=None, keep_all: bool = False,
     expert), "gate" and "up" (dicts by expert): given kept sets replace the
     corresponding selections (the same arithmetic re-run on another
     implementation's choices; when "down" is given no down scores are formed).
+    ``grads=False`` stops after the selections (scores and kept sets only).
     Returns kept sets, scores, dW per expert and, when every expert is
     formed, dX [T, H]."""
     r = p["routing"]
@@ -349,9 +351,11 @@ def swiglu_reference(p: dict, experts=None, keep_all: bool = False,
     H = p["H"]
     for e in experts:
         kd = K_down[e]
-        dWd, u = swiglu_expert_down(p, e, kd)
         if u_override is not None and e in u_override:
             u = np.asarray(u_override[e], dtype=np.float64)
+            dWd = swiglu_expert_down(p, e, kd)[0] if grads else None
+        else:
+            dWd, u = swiglu_expert_down(p, e, kd)
         ga, gb = swiglu_gate_up_grads(p, kd, u)
         w = r.weight[kd].astype(np.float64)
         sg = lrm_score(w, (ga * ga).sum(axis=1), x2[r.token[kd]])
@@ -369,6 +373,10 @@ def swiglu_reference(p: dict, experts=None, keep_all: bool = False,
             Ku = np.sort(np.asarray(kept["up"][e], dtype=np.int64))
         else:
             Ku = select_top_quota(r.expert, s_full_u, qu, E, candidates=kd)[e]
+        out["K_gate"][e], out["K_up"][e] = Kg, Ku
+        out["s_gate"][e], out["s_up"][e] = sg, su
+        if not grads:
+            continue
         row = {pp: i for i, pp in enumerate(kd.tolist())}
         ig = np.array([row[pp] for pp in Kg.tolist()], dtype=np.int64)
         iu = np.array([row[pp] for pp in Ku.tolist()], dtype=np.int64)
@@ -384,10 +392,8 @@ def swiglu_reference(p: dict, experts=None, keep_all: bool = False,
             dx[ig] += wg[:, None] * (ga[ig] @ f64(p["W_gate"][e]))
         if Ku.size:
             dx[iu] += wu[:, None] * (gb[iu] @ f64(p["W_up"][e]))
-        out["K_gate"][e], out["K_up"][e] = Kg, Ku
-        out["s_gate"][e], out["s_up"][e] = sg, su
         out["dx_pairs"][e] = (kd, dx)
-    if len(experts) == E:
+    if grads and len(experts) == E:
         dX = np.zeros((r.T, H))
         for e in range(E):
             kd, dx = out["dx_pairs"][e]
@@ -400,20 +406,24 @@ def swiglu_reference(p: dict, experts=None, keep_all: bool = False,
 def swiglu_pair_dx(p: dict, pairs, in_gate, in_up) -> np.ndarray:
     """Input-gradient row of each listed down-kept pair q (token t, expert e):
     w_q (1[q kept by gate] ga_q W_gate_e + 1[q kept by up] gb_q W_up_e), with
-    u = W_down_e^T g_t, ga = u * b * silu'(a), gb = u * silu(a)."""
+    u = W_down_e^T g_t, ga = u * b * silu'(a), gb = u * silu(a).  The pairs of
+    one expert are formed together (each row is independent of the others)."""
     r = p["routing"]
-    out = np.zeros((len(pairs), p["H"]))
-    for i, q in enumerate(pairs):
-        q = int(q)
-        e, t = int(r.expert[q]), int(r.token[q])
-        g = f64(p["G"][t])
-        a = f64(p["A"][q])
-        b = f64(p["B"][q])
+    pairs = np.asarray(pairs, dtype=np.int64)
+    in_gate = np.asarray(in_gate, dtype=bool)
+    in_up = np.asarray(in_up, dtype=bool)
+    out = np.zeros((pairs.shape[0], p["H"]))
+    for e in np.unique(r.expert[pairs]) if pairs.size else []:
+        sel = np.nonzero(r.expert[pairs] == e)[0]
+        q = pairs[sel]
+        g = pair_rows(p["G"], TOKEN, r.token, q)
         u = g @ f64(p["W_down"][e])
-        dx = np.zeros(p["H"])
-        if in_gate[i]:
-            dx += (u * b * dsilu(a)) @ f64(p["W_gate"][e])
-        if in_up[i]:
-            dx += (u * silu(a)) @ f64(p["W_up"][e])
-        out[i] = float(r.weight[q]) * dx
+        ga, gb = swiglu_gate_up_grads(p, q, u)
+        dx = np.zeros((q.shape[0], p["H"]))
+        mg, mu = in_gate[sel], in_up[sel]
+        if mg.any():
+            dx[mg] += ga[mg] @ f64(p["W_gate"][e])
+        if mu.any():
+            dx[mu] += gb[mu] @ f64(p["W_up"][e])
+        out[sel] = r.weight[q].astype(np.float64)[:, None] * dx
     return out
