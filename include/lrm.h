@@ -170,6 +170,10 @@ lrm_status lrm_score_glu(const lrm_pairs* pairs, const lrm_mat* A, const lrm_mat
  * (negative entries keep nothing).
  * flags: LRM_KEEP_ALL ignores score and quota and keeps every pair;
  * LRM_QUOTA_ON_DEVICE as above; other bits: LRM_ERR_UNSUPPORTED.
+ * Under HIP graph capture, host quotas of up to 512 experts are frozen into
+ * the graph at capture; host quotas of more than 512 experts would be re-read
+ * by a stream copy at every replay, so such a call returns
+ * LRM_ERR_UNSUPPORTED on a capturing stream (use LRM_QUOTA_ON_DEVICE).
  * ws: device scratch of lrm_select_workspace_size(pairs) bytes; its first word
  * receives device-detected index errors (see lrm_check_device_errors). */
 lrm_status lrm_select(const lrm_pairs* pairs, const float* score, const int32_t* quota,
@@ -366,6 +370,15 @@ typedef struct lrm_outputs {
  * "max down rows" is min(N, sum of quota_down), or N with LRM_KEEP_ALL; with
  * LRM_QUOTA_ON_DEVICE the caller, which knows its quotas, sizes those outputs
  * by the same rule (only rows of kept pairs are written).
+ * HIP graph capture: a captured call freezes the packed sizes the host
+ * computed from the quotas at capture, and host quotas of up to 512 experts
+ * (passed by value).  Host quotas of more than 512 experts are copied by a
+ * stream copy that a replay would repeat from the host array, so the call
+ * returns LRM_ERR_UNSUPPORTED on a capturing stream; device quotas
+ * (LRM_QUOTA_ON_DEVICE) are read at every replay and sized for every pair.
+ * Should a selection ever keep more rows than its packed buffers hold, the
+ * later experts keep fewer, every access stays inside the workspace and the
+ * outputs, and lrm_check_device_errors reports LRM_ERR_WORKSPACE.
  * ws: device scratch of lrm_workspace_size(prob) bytes, 256-byte aligned. */
 lrm_status lrm_expert_backward(const lrm_problem* prob, const lrm_outputs* out, void* ws,
                                size_t ws_bytes, void* stream);
@@ -398,7 +411,10 @@ int64_t lrm_max_kept(int32_t N, int32_t E, const int32_t* quota);
  * a workspace used by lrm_select, lrm_expert_backward or lrm_receiver_layout:
  * LRM_OK, or LRM_ERR_INDEX if an expert index was out of range or token[]
  * was out of range or decreasing (such pairs are treated as absent), or a
- * replica assignment did not match the kept counts, and clears it. */
+ * replica assignment did not match the kept counts; otherwise
+ * LRM_ERR_WORKSPACE if a selection kept more rows than the packed buffers of
+ * the call were sized for (a captured call replayed with other quotas); and
+ * clears it. */
 lrm_status lrm_check_device_errors(void* ws, void* stream);
 
 /* Static description of a status code. */

@@ -76,6 +76,9 @@ enum : uint32_t {
   kErrExpertRange = 1u,
   kErrTokenRange = 2u,
   kErrTokenOrder = 4u,
+  // more kept rows than the packed buffers were sized for (only a captured
+  // call replayed with host quotas other than those it was sized with)
+  kErrCapacity = 8u,
 };
 
 // Exclusive scan of one int per thread over an NT-thread block.  lds must hold

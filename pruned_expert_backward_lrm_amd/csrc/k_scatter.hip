@@ -11,11 +11,14 @@
 
 namespace lrm {
 
+// Row of pair p in source k, or -1.  Rows past what the packed buffers hold
+// (possible only when a captured call is replayed with other host quotas,
+// which the selection flags as an error) are taken as missing.
 __device__ __forceinline__ int src_row(const ScatterArgs& a, int k, int p) {
   if (!a.src[k]) return -1;
   int r = a.pos[k][p];
-  if (r >= 0 && a.pos2[k]) r = a.pos2[k][r];
-  return r;
+  if (r >= 0 && a.pos2[k]) r = r < a.pos2_rows[k] ? a.pos2[k][r] : -1;
+  return r < a.src_rows[k] ? r : -1;
 }
 
 __device__ __forceinline__ f32x4 ld4(const float* p) {

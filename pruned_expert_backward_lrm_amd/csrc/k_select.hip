@@ -27,6 +27,39 @@ constexpr int kSelRegKeys = 4;  // keys per thread held in registers by k_select
 constexpr int kScanTile = 8192;  // block counts staged in LDS per round by k_bucket_scan
 constexpr int kScatBatch = 8;   // 64-pair groups per wave loaded ahead by k_bucket_scatter
 
+// Kept offsets out[e] = min(M_0 + ... + M_{e-1}, cap) for e in [0, E] (cap < 0:
+// no cap), with M_e in mcount (LDS, E <= 4 * kSelThreads).  When the total
+// passes cap (only a captured call replayed with other host quotas than it
+// was sized with), every later expert keeps fewer rows, so all kernels after
+// it see at most cap packed rows; mcount then holds the capped counts.
+// Returns true (in every thread) if the total passed cap.
+__device__ bool scan_kept_capped(int E, int* mcount, int32_t* out, int64_t cap, int* lds) {
+  constexpr int per = 4;
+  const int i0 = threadIdx.x * per;
+  int v[per];
+  int local = 0;
+#pragma unroll
+  for (int j = 0; j < per; ++j) {
+    v[j] = (i0 + j < E) ? mcount[i0 + j] : 0;
+    local += v[j];
+  }
+  int total;
+  int run = block_excl_scan<kSelThreads>(local, lds, &total);
+  const int c = cap < 0 ? 0x7fffffff : (int)min<int64_t>(cap, 0x7fffffff);
+#pragma unroll
+  for (int j = 0; j < per; ++j) {
+    if (i0 + j < E) {
+      const int lo = min(run, c);
+      out[i0 + j] = lo;
+      if (total > c) mcount[i0 + j] = min(run + v[j], c) - lo;
+    }
+    run += v[j];
+  }
+  if (threadIdx.x == 0) out[E] = min(total, c);
+  __syncthreads();  // capped counts visible to the whole block
+  return total > c;
+}
+
 // tok_off[t] for the tokens t that start at pair p (p in [0, N]): the first
 // pair whose token is >= t.
 __device__ __forceinline__ void token_offsets_at(int64_t p, int N, int T,
@@ -85,7 +118,7 @@ __global__ __launch_bounds__(kSelThreads) void k_bucket_scan(int nblk, int E,
                                                              uint32_t* __restrict__ err,
                                                              int32_t* __restrict__ mt_off,
                                                              int mt_bm, QuotaPack qp,
-                                                             int use_qp) {
+                                                             int use_qp, int64_t max_kept) {
   LRM_DYN_SHARED(int, counts);  // [2E]: counts, then kept counts min(quota, count)
   __shared__ int lds[kSelThreads / kWave + 1];
   __shared__ uint32_t eor;
@@ -149,12 +182,12 @@ __global__ __launch_bounds__(kSelThreads) void k_bucket_scan(int nblk, int E,
   }
   __syncthreads();
   block_scan_array<kSelThreads>(E, [&](int e) { return counts[e]; }, cand_off, lds);
-  block_scan_array<kSelThreads>(E, [&](int e) { return mcount[e]; }, offsets, lds);
+  const bool over = scan_kept_capped(E, mcount, offsets, max_kept, lds);
   if (mt_off) {
     block_scan_array<kSelThreads>(
         E, [&](int e) { return (mcount[e] + mt_bm - 1) / mt_bm; }, mt_off, lds);
   }
-  if (threadIdx.x == 0) err[0] = eor;
+  if (threadIdx.x == 0) err[0] = eor | (over ? kErrCapacity : 0u);
 }
 
 // Stage-two offsets: candidates of e are cand_off[e]..cand_off[e+1].
@@ -162,16 +195,19 @@ __global__ __launch_bounds__(kSelThreads) void k_kept_offsets(int E,
                                                               const int32_t* __restrict__ cand_off,
                                                               const int32_t* __restrict__ quota,
                                                               int32_t* __restrict__ offsets,
-                                                              QuotaPack qp, int use_qp) {
+                                                              QuotaPack qp, int use_qp,
+                                                              uint32_t* __restrict__ err,
+                                                              int64_t cap) {
   __shared__ int lds[kSelThreads / kWave + 1];
-  block_scan_array<kSelThreads>(
-      E,
-      [&](int e) {
-        const int n = cand_off[e + 1] - cand_off[e];
-        if (quota) return min(max(quota[e], 0), n);
-        return use_qp ? min(max(qp.q[e], 0), n) : n;
-      },
-      offsets, lds);
+  LRM_DYN_SHARED(int, mcount);  // [E]
+  for (int e = threadIdx.x; e < E; e += kSelThreads) {
+    const int n = cand_off[e + 1] - cand_off[e];
+    mcount[e] = quota ? min(max(quota[e], 0), n) : (use_qp ? min(max(qp.q[e], 0), n) : n);
+  }
+  __syncthreads();
+  const bool over = scan_kept_capped(E, mcount, offsets, cap, lds);
+  // (the call's error word was written by an earlier kernel of the stream)
+  if (threadIdx.x == 0 && over) err[0] |= kErrCapacity;
 }
 
 // One wave per chunk; stable scatter in pair order.  Lanes with the same
@@ -245,17 +281,20 @@ __global__ __launch_bounds__(64) void k_bucket_scatter(int N, int T, int E, int 
 
 // One workgroup per expert.  keys[c] and ids cand[c] (or c itself when cand is
 // null) for candidates c in [cand_off[e], cand_off[e+1]), ascending id.
+// Candidates and packed slots are clipped to [0, limit), the extent of keys,
+// cand, pos and kept (offsets beyond it arise only when a captured call is
+// replayed with other host quotas, flagged by the offsets kernels).
 __global__ __launch_bounds__(kSelThreads) void k_select(const int32_t* __restrict__ cand_off,
                                                         const int32_t* __restrict__ offsets,
                                                         const uint32_t* __restrict__ keys,
                                                         const int32_t* __restrict__ cand,
                                                         int32_t* __restrict__ pos,
-                                                        int32_t* __restrict__ kept) {
+                                                        int32_t* __restrict__ kept, int limit) {
   const int e = blockIdx.x;
-  const int c0 = cand_off[e];
-  const int n = cand_off[e + 1] - c0;
-  const int o = offsets[e];
-  const int m = offsets[e + 1] - o;
+  const int c0 = min(cand_off[e], limit);
+  const int n = min(cand_off[e + 1], limit) - c0;
+  const int o = min(offsets[e], limit);
+  const int m = min(offsets[e + 1], limit) - o;
   const int tid = threadIdx.x;
   // two histograms and two result slots, alternating between radix passes,
   // so that a pass needs two barriers (after the counts, after the search)
@@ -424,7 +463,7 @@ hipError_t launch_bucket(const BucketArgs& a, hipStream_t s) {
   if (use_qp && a.E > kQuotaPackMax) return hipErrorInvalidValue;
   LRM_LAUNCH(1, kSelThreads, 2 * a.E * sizeof(int), s, k_bucket_scan)(
       nblk, a.E, a.blkcnt, a.quota, a.cand_off, a.offsets, a.blkerr, a.err, a.mt_off, a.mt_bm,
-      use_qp ? *a.qpack : QuotaPack{}, use_qp ? 1 : 0);
+      use_qp ? *a.qpack : QuotaPack{}, use_qp ? 1 : 0, a.max_kept);
   if (a.N > 0) {
     LRM_LAUNCH(nblk, 64, a.E * sizeof(int), s, k_bucket_scatter)(a.N, a.T, a.E, chunk, a.token,
                                                          a.expert, a.blkcnt, a.cand_off, a.score,
@@ -435,17 +474,21 @@ hipError_t launch_bucket(const BucketArgs& a, hipStream_t s) {
 
 hipError_t launch_select(int E, const int32_t* cand_off, const int32_t* offsets,
                          const uint32_t* keys, const int32_t* cand, int32_t* pos, int32_t* kept,
-                         hipStream_t s) {
-  LRM_LAUNCH(E, kSelThreads, 0, s, k_select)(cand_off, offsets, keys, cand, pos, kept);
+                         int limit, hipStream_t s) {
+  LRM_LAUNCH(E, kSelThreads, 0, s, k_select)(cand_off, offsets, keys, cand, pos, kept,
+                                             limit < 0 ? 0 : limit);
   return hipGetLastError();
 }
 
 hipError_t launch_kept_offsets(int E, const int32_t* cand_off, const int32_t* quota,
-                               const QuotaPack* qpack, int32_t* offsets, hipStream_t s) {
+                               const QuotaPack* qpack, int32_t* offsets, uint32_t* err,
+                               int64_t cap, hipStream_t s) {
   const bool use_qp = !quota && qpack;
   if (use_qp && E > kQuotaPackMax) return hipErrorInvalidValue;
-  LRM_LAUNCH(1, kSelThreads, 0, s, k_kept_offsets)(E, cand_off, quota, offsets,
-                                                   use_qp ? *qpack : QuotaPack{}, use_qp ? 1 : 0);
+  if (cap >= 0 && !err) return hipErrorInvalidValue;
+  LRM_LAUNCH(1, kSelThreads, E * sizeof(int), s, k_kept_offsets)(E, cand_off, quota, offsets,
+                                                   use_qp ? *qpack : QuotaPack{}, use_qp ? 1 : 0,
+                                                   err, cap);
   return hipGetLastError();
 }
 

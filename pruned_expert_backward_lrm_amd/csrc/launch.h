@@ -36,7 +36,12 @@ hipError_t launch_pair_score(const ScoreOperands& op, hipStream_t s);
 // Quotas of at most kQuotaPackMax experts, passed by value in the kernel
 // arguments (2 KB): the host array is read at the call, and no copy
 // operation is enqueued on the stream.
-constexpr int kQuotaPackMax = 512;
+// (The CPU-emulation test build lowers it, so that its copy path runs on
+// problems small enough to emulate.)
+#ifndef LRM_QUOTA_PACK_MAX
+#define LRM_QUOTA_PACK_MAX 512
+#endif
+constexpr int kQuotaPackMax = LRM_QUOTA_PACK_MAX;
 struct QuotaPack {
   int32_t q[kQuotaPackMax];
 };
@@ -60,16 +65,21 @@ struct BucketArgs {
   int32_t* tok_off;      // [T+1] first pair of each token, or nullptr (not wanted)
   int32_t* mt_off;       // [E+1] row-tile prefix of the kept blocks for dX tiles
   int mt_bm;             //   of mt_bm rows (mt_off == nullptr: not wanted)
+  int64_t max_kept;      // rows the packed buffers hold (-1: no limit); more kept
+                         //   rows set kErrCapacity
 };
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s);
+// limit: candidate indices, packed slots and pos entries at or beyond it are
+// never touched (the extent of keys, cand, pos and kept).
 hipError_t launch_select(int E, const int32_t* cand_off, const int32_t* offsets,
                          const uint32_t* keys, const int32_t* cand, int32_t* pos, int32_t* kept,
-                         hipStream_t s);
+                         int limit, hipStream_t s);
 // quota: device [E]; or qpack (host, by value, E <= kQuotaPackMax) when quota
-// is nullptr; both nullptr: keep all.
+// is nullptr; both nullptr: keep all.  More than cap kept rows (cap >= 0) set
+// kErrCapacity in err[0].
 hipError_t launch_kept_offsets(int E, const int32_t* cand_off, const int32_t* quota,
-                               const QuotaPack* qpack,
-                               int32_t* offsets, hipStream_t s);
+                               const QuotaPack* qpack, int32_t* offsets, uint32_t* err,
+                               int64_t cap, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
 hipError_t launch_token_offsets(int N, int T, const int32_t* token, int32_t* tok_off,
                                 hipStream_t s);
@@ -120,6 +130,8 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s);
 // ------------------------------------------------------------ unpermute
 // Up to two sources; the row of pair p in source k is
 //   r = pos_k[p]; if (r >= 0 && pos2_k) r = pos2_k[r];
+// with r taken as missing when it reaches past pos2_rows[k] (before the
+// second lookup) or src_rows[k] (the rows source k holds).
 struct ScatterArgs {
   int N, T, d, out_pair;
   const int32_t* token;
@@ -128,6 +140,8 @@ struct ScatterArgs {
   const int32_t* pos[2];
   const int32_t* pos2[2];
   const float* src[2];
+  int pos2_rows[2];
+  int src_rows[2];
   float* dX;
 };
 hipError_t launch_unpermute(const ScatterArgs& a, hipStream_t s);

@@ -5,6 +5,7 @@
 #include <new>
 
 #include "lrm.h"
+#include "common.h"
 #include "launch.h"
 
 using namespace lrm;
@@ -83,6 +84,18 @@ lrm_status check_quota(const int32_t* q, int E, int64_t* sum) {
   } while (0)
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Host quotas of more than kQuotaPackMax experts are copied into the
+// workspace with a stream copy of the host array.  A captured graph would
+// re-read that array at every replay while keeping the packed sizes the host
+// computed from it at capture, so such a call is refused under capture
+// (device quotas, or at most kQuotaPackMax experts, are the capturable forms).
+lrm_status check_capturable(int E, bool host_quotas, hipStream_t s) {
+  if (!host_quotas || E <= kQuotaPackMax) return LRM_OK;
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &st) != hipSuccess) return LRM_ERR_HIP;
+  return st == hipStreamCaptureStatusNone ? LRM_OK : LRM_ERR_UNSUPPORTED;
+}
 
 // ---------------------------------------------------------------- scoring
 
@@ -175,11 +188,13 @@ SelectWs carve_select(Carve& c, int N, int E) {
 // pointer, used as it is.
 // tok_off (optional, [T+1]): the first pair of each token, computed on the way
 // when there is at least one pair.  mt_off (optional, [E+1]): the prefix of
-// ceil(M_e / mt_bm), the dX row tiles of the grouped GEMM.
+// ceil(M_e / mt_bm), the dX row tiles of the grouped GEMM.  max_kept: the rows
+// the packed buffers were sized for (-1: none); more kept rows are flagged in
+// the error word.
 lrm_status run_select(const lrm_pairs* p, const float* score, const int32_t* quota_host,
                       int32_t* pos, int32_t* offsets, int32_t* kept, const SelectWs& w,
                       hipStream_t s, int32_t* tok_off = nullptr, int32_t* mt_off = nullptr,
-                      int mt_bm = 0, bool quota_on_device = false) {
+                      int mt_bm = 0, bool quota_on_device = false, int64_t max_kept = -1) {
   const bool keep_all = quota_host == nullptr;
   // host quotas of up to kQuotaPackMax experts go by value with the scan's
   // launch; more are copied stream-ordered into the workspace
@@ -199,9 +214,10 @@ lrm_status run_select(const lrm_pairs* p, const float* score, const int32_t* quo
   b.cand = keep_all ? kept : w.cand;
   b.keys = keep_all ? nullptr : w.keys;
   b.pos = pos; b.keep_all = keep_all; b.err = w.err; b.blkerr = w.blkerr; b.tok_off = tok_off;
-  b.mt_off = mt_off; b.mt_bm = mt_bm;
+  b.mt_off = mt_off; b.mt_bm = mt_bm; b.max_kept = max_kept;
   LRM_TRY_HIP(launch_bucket(b, s));
-  if (!keep_all) LRM_TRY_HIP(launch_select(p->E, w.cand_off, offsets, w.keys, w.cand, pos, kept, s));
+  if (!keep_all)
+    LRM_TRY_HIP(launch_select(p->E, w.cand_off, offsets, w.keys, w.cand, pos, kept, p->N, s));
   return LRM_OK;
 }
 
@@ -306,9 +322,10 @@ lrm_status lrm_select(const lrm_pairs* pairs, const float* score, const int32_t*
   Carve c(nullptr);
   carve_select(c, pairs->N, pairs->E);
   if (!ws || ws_bytes < c.size()) return LRM_ERR_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  LRM_TRY(check_capturable(pairs->E, !keep_all && !qdev, s));
   Carve r(ws);
   SelectWs w = carve_select(r, pairs->N, pairs->E);
-  hipStream_t s = as_stream(stream);
   return run_select(pairs, score, keep_all ? nullptr : quota, pos, offsets, kept, w, s, nullptr,
                     nullptr, 0, qdev);
 }
@@ -392,6 +409,7 @@ lrm_status lrm_unpermute(const lrm_pairs* pairs, const int32_t* pos, const float
   a.N = pairs->N; a.T = pairs->T; a.d = d_in; a.out_pair = out_rows == LRM_ROWS_PAIR;
   a.token = pairs->token; a.weight = pairs->weight;
   a.pos[0] = pos; a.src[0] = dXp;
+  a.src_rows[0] = 0x7fffffff;  // the caller's dXp holds every row pos names
   a.dX = dX;
   if (!a.out_pair) {
     Carve r(ws);
@@ -412,7 +430,8 @@ lrm_status lrm_check_device_errors(void* ws, void* stream) {
   if (word) {
     LRM_TRY_HIP(launch_fill_u32(static_cast<uint32_t*>(ws), 0u, 1, s));
     LRM_TRY_HIP(hipStreamSynchronize(s));
-    return LRM_ERR_INDEX;
+    // index errors first; capacity alone: the packed buffers were too small
+    return (word & ~kErrCapacity) ? LRM_ERR_INDEX : LRM_ERR_WORKSPACE;
   }
   return LRM_OK;
 }
@@ -687,7 +706,7 @@ lrm_status run_linear(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   const bool tok_out = pb->X.rows != LRM_ROWS_PAIR;
   LRM_TRY(run_select(p, L.score, keep_all ? nullptr : pb->quota, L.pos, L.offsets, L.kept,
                      L.sel, s, tok_out && p->N > 0 ? L.tok_off : nullptr, L.mt_off, dx_rows,
-                     qdev));
+                     qdev, Mcap));
   LRM_TRY_HIP(mark(2));
   // 3. compaction: Xp = w x, Gp = g
   CompactArgs ca{};
@@ -710,6 +729,7 @@ lrm_status run_linear(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   ScatterArgs sa{};
   sa.N = p->N; sa.T = p->T; sa.d = pb->d_in; sa.out_pair = pb->X.rows == LRM_ROWS_PAIR;
   sa.token = p->token; sa.weight = p->weight; sa.pos[0] = L.pos; sa.src[0] = L.dXp;
+  sa.src_rows[0] = (int)Mcap;
   if (!sa.out_pair) {
     if (p->N == 0) LRM_TRY_HIP(launch_token_offsets(p->N, p->T, p->token, L.tok_off, s));
     sa.tok_off = L.tok_off;
@@ -742,7 +762,7 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   const bool qdev = (pb->flags & LRM_QUOTA_ON_DEVICE) != 0;
   LRM_TRY(run_select(p, L.score, keep_all ? nullptr : pb->quota_down, L.pos, L.offsets, L.kept,
                      L.sel, s, tok_out && p->N > 0 ? L.tok_off : nullptr, L.mt_off, dx_rows,
-                     qdev));
+                     qdev, z.Md));
   LRM_TRY_HIP(mark(2));
   CompactArgs cd{};
   cd.T = p->T; cd.bf16 = bf16; cd.max_rows = (int)z.Md; cd.E = E;
@@ -792,13 +812,16 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
       qg = L.qgate;
       qu = L.qup;
     }
-    LRM_TRY_HIP(launch_kept_offsets(E, L.offsets, qg, by_value ? &pg : nullptr, L.off_g, s));
+    // candidates are down rows: the per-row arrays hold Md of them
+    LRM_TRY_HIP(launch_kept_offsets(E, L.offsets, qg, by_value ? &pg : nullptr, L.off_g,
+                                    L.sel.err, z.Mg, s));
     LRM_TRY_HIP(launch_select(E, L.offsets, L.off_g,
                               reinterpret_cast<const uint32_t*>(L.s_gate), nullptr, L.pos_g,
-                              L.kept_g, s));
-    LRM_TRY_HIP(launch_kept_offsets(E, L.offsets, qu, by_value ? &pu : nullptr, L.off_u, s));
+                              L.kept_g, (int)z.Md, s));
+    LRM_TRY_HIP(launch_kept_offsets(E, L.offsets, qu, by_value ? &pu : nullptr, L.off_u,
+                                    L.sel.err, z.Mu, s));
     LRM_TRY_HIP(launch_select(E, L.offsets, L.off_u, reinterpret_cast<const uint32_t*>(L.s_up),
-                              nullptr, L.pos_u, L.kept_u, s));
+                              nullptr, L.pos_u, L.kept_u, (int)z.Md, s));
   }
   LRM_TRY_HIP(mark(6));
   const bool x_tok = !x_pair;
@@ -828,7 +851,7 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
     gu.dW = out->dW_up; gu.dXp = nullptr; gu.mt_off = L.mt_off;
     gu.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
     LRM_TRY_HIP(launch_grouped_gemm(gu, s));
-    sa.pos[0] = L.pos; sa.src[0] = L.dXp;
+    sa.pos[0] = L.pos; sa.src[0] = L.dXp; sa.src_rows[0] = (int)z.Md;
   } else {
     const void* GAsrc[2] = {L.GA, L.GB};
     int32_t* keptv[2] = {L.kept_g, L.kept_u};
@@ -859,6 +882,7 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
       gk.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
       LRM_TRY_HIP(launch_grouped_gemm(gk, s));
       sa.pos[k] = L.pos; sa.pos2[k] = posv[k]; sa.src[k] = dXv[k];
+      sa.pos2_rows[k] = (int)z.Md; sa.src_rows[k] = (int)cap[k];
     }
   }
   LRM_TRY_HIP(mark(8));
@@ -889,6 +913,8 @@ lrm_status lrm_expert_backward_events(const lrm_problem* prob, const lrm_outputs
   if (!ws || ws_bytes < plan_size(prob, out)) return LRM_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return LRM_ERR_ALIGN;
   hipStream_t s = as_stream(stream);
+  LRM_TRY(check_capturable(prob->pairs.E,
+                           !(prob->flags & (LRM_KEEP_ALL | LRM_QUOTA_ON_DEVICE)), s));
   const Marks mark{events, n_events, s};
   LRM_TRY(prob->kind == LRM_LINEAR ? run_linear(prob, out, ws, s, mark)
                                    : run_swiglu(prob, out, ws, s, mark));

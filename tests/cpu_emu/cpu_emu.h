@@ -44,8 +44,24 @@ enum hipMemcpyKind {
   hipMemcpyHostToHost, hipMemcpyHostToDevice, hipMemcpyDeviceToHost, hipMemcpyDeviceToDevice,
   hipMemcpyDefault
 };
-inline hipError_t hipMemcpyAsync(void* d, const void* s, size_t n, hipMemcpyKind, hipStream_t) {
+// LRM_EMU_H2D_INT_ADD=k adds k to every int32 of a host-to-device copy made
+// after the call's sizing: in the fused call the only such copies are host
+// quotas of more than LRM_QUOTA_PACK_MAX experts, so this stands for a captured call
+// replayed after its host quota arrays grew.
+inline hipError_t hipMemcpyAsync(void* d, const void* s, size_t n, hipMemcpyKind k, hipStream_t) {
   std::memcpy(d, s, n);
+  if (k == hipMemcpyHostToDevice && std::getenv("LRM_EMU_H2D_INT_ADD") && n % 4 == 0) {
+    const int add = std::atoi(std::getenv("LRM_EMU_H2D_INT_ADD"));
+    int32_t* q = static_cast<int32_t*>(d);
+    for (size_t i = 0; i < n / 4; ++i) q[i] += add;
+  }
+  return hipSuccess;
+}
+enum hipStreamCaptureStatus {
+  hipStreamCaptureStatusNone, hipStreamCaptureStatusActive, hipStreamCaptureStatusInvalidated
+};
+inline hipError_t hipStreamIsCapturing(hipStream_t, hipStreamCaptureStatus* st) {
+  *st = hipStreamCaptureStatusNone;
   return hipSuccess;
 }
 inline hipError_t hipMemcpy(void* d, const void* s, size_t n, hipMemcpyKind) {

@@ -29,7 +29,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "pruned_expert_backward_lrm_amd", "csrc")
 EMU = os.path.join(ROOT, "tests", "cpu_emu")
 CLANG = "/opt/rocm/llvm/bin/clang++"
-FLAGS = ["-std=c++20", "-O1", "-g", "-fsanitize=address", "-fno-omit-frame-pointer"]
+# host quotas of more than QUOTA_PACK_MAX experts take the library's stream-copy
+# path (512 in the product build; lowered here so that path runs on small E)
+QUOTA_PACK_MAX = 8
+FLAGS = ["-std=c++20", "-O1", "-g", "-fsanitize=address", "-fno-omit-frame-pointer",
+         f"-DLRM_QUOTA_PACK_MAX={QUOTA_PACK_MAX}"]
 
 LINEAR, SWIGLU = 0, 1
 F32, BF16 = 0, 1
@@ -246,3 +250,31 @@ def test_emu_bad_expert_id(driver, tmp_path):
     r.expert[5] = r.E + 3
     run_emu(driver, tmp_path, p, expect=(0, 8))
     run_emu(driver, tmp_path, p, flags=8, expect=(8, -1))
+
+
+@pytest.mark.parametrize("kind", ["linear", "swiglu"])
+def test_emu_selection_past_packed_capacity(driver, tmp_path, kind):
+    """Host quotas of more than QUOTA_PACK_MAX experts are copied into the
+    workspace on the stream.  The emulation adds 50 to every quota of that
+    copy, as a captured call replayed after its host quota arrays grew would
+    see: the selections then keep more rows than the host sized the packed
+    buffers for.  Every access must stay in bounds (AddressSanitizer), the
+    call must return LRM_OK and the device error word LRM_ERR_WORKSPACE (7);
+    the kept counts are capped at the packed capacity."""
+    E = 2 * QUOTA_PACK_MAX
+    if kind == "linear":
+        p = synth.make_linear(96, E, 2, 8, 8, dtype="f32", seed=21, zipf=2.0,
+                              quota=lambda c: c // 4)
+        cap = int(np.minimum(p["quota"], p["routing"].counts).sum())
+    else:
+        q = lambda c: c // 4  # noqa: E731
+        p = synth.make_swiglu(96, E, 2, 8, 8, dtype="f32", seed=21, zipf=2.0,
+                              quotas=(q, q, q), g_std=1e-2)
+        cap = int(np.minimum(p["quota_down"], p["routing"].counts).sum())
+    assert 0 < cap < p["routing"].N // 2
+    out = run_emu(driver, tmp_path, p, env_extra={"LRM_EMU_H2D_INT_ADD": "50"}, expect=(0, 7))
+    offs = out["offsets"].numpy().astype(np.int64)
+    assert offs[-1] == cap and np.all(np.diff(offs) >= 0)
+    if kind == "swiglu":
+        for k in ("offsets_gate", "offsets_up"):
+            assert out[k].numpy()[-1] <= cap

@@ -484,3 +484,39 @@ def test_fused_linear_graph_replay(L):
     for got in _graph_replays(L, pb, out, ws):
         for k in out:
             assert torch.equal(got[k], eager[k]), k
+
+
+def test_capture_refused_for_copied_host_quotas(L):
+    """Host quotas of more than 512 experts travel by a stream copy of the
+    host array, which a replay would repeat while the packed sizes stay those
+    of the capture: on a capturing stream the call is refused before any
+    launch (LRM_ERR_UNSUPPORTED = 10).  Device quotas of the same problem
+    capture and replay bit-exactly against the eager call."""
+    say("capture with 600 experts' host quotas")
+    p = synth.make_linear(900, 600, 2, 64, 64, dtype="bf16", seed=31, zipf=1.1,
+                          quota=lambda c: (c + 1) // 2)
+    r = p["routing"]
+    pairs = L.Pairs.from_routing(r, DEV)
+    X, G, W = (p[k].to(DEV) for k in ("X", "G", "W"))
+    pb = L.linear_problem(pairs, X, "token", G, "pair", W, p["quota"])
+    out = dict(dW=torch.empty(r.E, 64, 64, device=DEV), dX=torch.empty(r.T, 64, device=DEV))
+    ws = torch.empty(L.lrm_workspace_size(pb), dtype=torch.uint8, device=DEV)
+    L.lrm_expert_backward(pb, out, ws=ws)  # eager: fine
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with pytest.raises(L.LrmError) as ei:
+        with torch.cuda.graph(graph):
+            L.lrm_expert_backward(pb, out, ws=ws)
+    assert ei.value.status == 10, str(ei.value)
+    torch.cuda.synchronize()
+    qd = torch.tensor(p["quota"], dtype=torch.int32, device=DEV)
+    pbd = L.linear_problem(pairs, X, "token", G, "pair", W, qd, L.LRM_QUOTA_ON_DEVICE)
+    outd = dict(dW=torch.empty(r.E, 64, 64, device=DEV), dX=torch.empty(r.T, 64, device=DEV),
+                pos=torch.empty(r.N, dtype=torch.int32, device=DEV))
+    wsd = torch.empty(L.lrm_workspace_size(pbd), dtype=torch.uint8, device=DEV)
+    L.lrm_expert_backward(pbd, outd, ws=wsd)
+    torch.cuda.synchronize()
+    eager = {k: v.cpu().clone() for k, v in outd.items()}
+    for got in _graph_replays(L, pbd, outd, wsd):
+        for k in outd:
+            assert torch.equal(got[k], eager[k]), k
