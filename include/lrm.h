@@ -239,6 +239,25 @@ size_t lrm_unpermute_workspace_size(const lrm_pairs* pairs);
  * LRM_ERR_QUOTA if a count or the budget is negative. */
 lrm_status lrm_quota_waterfill(int32_t E, const int32_t* counts, int64_t budget, int32_t* quota);
 
+/* The same controller on the GPU, in stream order (same section and rule as
+ * lrm_quota_waterfill; integer arithmetic, so the quotas are identical), so
+ * that controller and backward run on one stream with no host round trip and
+ * can be captured in one HIP graph at any E:
+ *   pairs:  the routed pairs of the layer call (E is taken from it).
+ *   counts: device [E] int32 pairs per expert (negative entries count as 0),
+ *           or NULL: the counts are those of the pairs, computed here (pairs
+ *           with an expert or token out of range are not counted, and the
+ *           workspace error word reports them, see lrm_check_device_errors).
+ *   budget: pairs this GPU may carry through the backward pass, >= 0 (host
+ *           value, fixed for the call).
+ *   quota:  device [E] int32 output, ready for LRM_QUOTA_ON_DEVICE.
+ * ws: device scratch of lrm_quota_waterfill_device_workspace_size(pairs)
+ * bytes.  LRM_ERR_QUOTA if budget < 0. */
+lrm_status lrm_quota_waterfill_device(const lrm_pairs* pairs, const int32_t* counts,
+                                      int64_t budget, int32_t* quota, void* ws, size_t ws_bytes,
+                                      void* stream);
+size_t lrm_quota_waterfill_device_workspace_size(const lrm_pairs* pairs);
+
 /* ----------------------------------------- redistribution onto replicas */
 
 /* Redistribution of the kept pairs over the copies of their expert (page 1,
@@ -384,15 +403,21 @@ lrm_status lrm_expert_backward(const lrm_problem* prob, const lrm_outputs* out, 
                                size_t ws_bytes, void* stream);
 
 /* lrm_expert_backward, additionally recording events[i] (a hipEvent_t created
- * by the caller, passed as void*) on the stream at stage boundary i, for each
- * i < n_events with events[i] != NULL.  Boundaries:
+ * by the caller, passed as void*) on the stream at boundary i, for each
+ * i < n_events with events[i] != NULL.  Every grouped-GEMM launch sits
+ * between two boundaries of its own:
  *   LINEAR: 0 start, 1 after score, 2 after select, 3 after compaction,
- *           4 after the grouped GEMM, 5 after unpermute (end);
+ *           4 after the dW launch, 5 after the dX launch, 6 after unpermute
+ *           (end).  fp32 runs both products in one launch: 4 and 5 are its end.
  *   SWIGLU: 0 start, 1 after the down score, 2 after the down select, 3 after
- *           the down compaction, 4 after the down grouped GEMM, 5 after the
- *           SwiGLU backward with the gate/up scores, 6 after the gate/up
- *           selects, 7 after the gate/up compaction, 8 after the gate/up
- *           grouped GEMMs, 9 after unpermute (end).
+ *           the down compaction, 4 after the down dW launch, 5 after the down
+ *           dX launch (u), 6 after the SwiGLU backward with the gate/up
+ *           scores, 7 after the gate/up selects, 8 after the gate/up
+ *           compaction, 9 after the gate dW launch, 10 after the gate dX
+ *           launch, 11 after the up dW launch, 12 after the up dX launch,
+ *           13 after unpermute (end).  When the gate/up selections keep every
+ *           down-kept row, one launch computes both input-gradient products
+ *           (between 9 and 10) and 12 coincides with 11.
  * The time between consecutive events is that stage's device time on the
  * stream (for profiling; the results are those of lrm_expert_backward). */
 lrm_status lrm_expert_backward_events(const lrm_problem* prob, const lrm_outputs* out, void* ws,

@@ -79,6 +79,8 @@ enum : uint32_t {
   // more kept rows than the packed buffers were sized for (only a captured
   // call replayed with host quotas other than those it was sized with)
   kErrCapacity = 8u,
+  // a replica assignment that does not match the kept counts
+  kErrAssign = 16u,
 };
 
 // Exclusive scan of one int per thread over an NT-thread block.  lds must hold

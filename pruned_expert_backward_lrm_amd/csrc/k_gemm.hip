@@ -829,6 +829,7 @@ static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
   const bool per_tile = gemm_tile_choice(a) == 2 && rounds <= 16;
   err = launch_stream<CW, false>(P, P.nW, s, per_tile);
   if (err != hipSuccess) return err;
+  if (a.mid_event && (err = hipEventRecord(a.mid_event, s)) != hipSuccess) return err;
   return launch_stream<CX, true>(P, P.nX, s, per_tile);
 }
 
@@ -875,6 +876,11 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s) {
   hipError_t err = plan_tiles(a, FBM, FBN, FBM, FBN, &P, s);
   if (err != hipSuccess || P.G == 0) return err;
   LRM_LAUNCH(P.G, NT, 0, s, k_grouped_gemm_f32)(P);
+  // one launch holds both tile kinds: the mid point is its end
+  if (a.mid_event) {
+    err = hipEventRecord(a.mid_event, s);
+    if (err != hipSuccess) return err;
+  }
   return hipGetLastError();
 }
 

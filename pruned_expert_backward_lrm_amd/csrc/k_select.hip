@@ -450,6 +450,17 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_bucket_count(int N, int T, int E, const int32_t* token, const int32_t* expert,
+                               int32_t* blkcnt, uint32_t* blkerr, int32_t* tok_off,
+                               hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  const int nblk = bucket_blocks(N);
+  if (nblk > kScanTile) return hipErrorInvalidValue;
+  LRM_LAUNCH(nblk, 256, E * sizeof(int), s, k_bucket_count)(N, T, E, bucket_chunk(N), token,
+                                                            expert, blkcnt, blkerr, tok_off);
+  return hipGetLastError();
+}
+
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s) {
   const int nblk = bucket_blocks(a.N);
   const int chunk = bucket_chunk(a.N);

@@ -69,6 +69,12 @@ struct BucketArgs {
                          //   rows set kErrCapacity
 };
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s);
+// Per-block expert histograms of the pairs (the first bucketing step):
+// blkcnt[e][b] pairs of expert e in block b of bucket_blocks(N), blkerr[b] the
+// block's index-error bits; tok_off as in BucketArgs, or nullptr.
+hipError_t launch_bucket_count(int N, int T, int E, const int32_t* token, const int32_t* expert,
+                               int32_t* blkcnt, uint32_t* blkerr, int32_t* tok_off,
+                               hipStream_t s);
 // limit: candidate indices, packed slots and pos entries at or beyond it are
 // never touched (the extent of keys, cand, pos and kept).
 hipError_t launch_select(int E, const int32_t* cand_off, const int32_t* offsets,
@@ -85,6 +91,24 @@ hipError_t launch_token_offsets(int N, int T, const int32_t* token, int32_t* tok
                                 hipStream_t s);
 hipError_t launch_tile_plan(int E, int bm, const int32_t* offsets, int32_t* mt_off,
                             hipStream_t s);
+
+// --------------------------------------------------------- quota control
+// Water-filling quotas on the device.  counts: device [E], or nullptr to
+// count the pairs (token, expert of N pairs, T tokens) with the bucketing
+// histogram (blkcnt [E][bucket_blocks(N)], blkerr [bucket_blocks(N)] scratch;
+// the pairs' index errors go to err[0]).
+struct QuotaArgs {
+  int N, T, E;
+  const int32_t* token;
+  const int32_t* expert;
+  const int32_t* counts;
+  int64_t budget;
+  int32_t* quota;
+  int32_t* blkcnt;
+  uint32_t* blkerr;
+  uint32_t* err;
+};
+hipError_t launch_quota_waterfill(const QuotaArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------- compact
 // Row j < min(offsets[E], max_rows) of the packed block:
@@ -121,6 +145,7 @@ struct GemmArgs {
   int32_t* mt_off;  // workspace [E+1]
   int mt_ready;     // mt_off already holds the prefix for gemm_dx_tile_rows(*this)
   int dw_bf16;      // dW is stored as bf16 (round to nearest even), bf16 kernels only
+  hipEvent_t mid_event;  // recorded after the dW launch, before the dX launch (or null)
 };
 int gemm_tile_choice(const GemmArgs& a);
 // Rows of a dX tile of the bf16 kernels (the prefix mt_off is built for it).

@@ -421,6 +421,34 @@ lrm_status lrm_unpermute(const lrm_pairs* pairs, const int32_t* pos, const float
   return LRM_OK;
 }
 
+size_t lrm_quota_waterfill_device_workspace_size(const lrm_pairs* pairs) {
+  if (check_pairs(pairs) != LRM_OK) return 0;
+  Carve c(nullptr);
+  carve_select(c, pairs->N, pairs->E);
+  return c.size();
+}
+
+lrm_status lrm_quota_waterfill_device(const lrm_pairs* pairs, const int32_t* counts,
+                                      int64_t budget, int32_t* quota, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  LRM_TRY(check_pairs(pairs));
+  if (!quota) return LRM_ERR_NULL;
+  if (budget < 0) return LRM_ERR_QUOTA;
+  Carve c(nullptr);
+  carve_select(c, pairs->N, pairs->E);
+  if (!ws || ws_bytes < c.size()) return LRM_ERR_WORKSPACE;
+  // the selection's layout: error word first, the histogram scratch as the
+  // bucketing pass uses it
+  Carve r(ws);
+  SelectWs w = carve_select(r, pairs->N, pairs->E);
+  QuotaArgs a{};
+  a.N = pairs->N; a.T = pairs->T; a.E = pairs->E; a.token = pairs->token;
+  a.expert = pairs->expert; a.counts = counts; a.budget = budget; a.quota = quota;
+  a.blkcnt = w.blkcnt; a.blkerr = w.blkerr; a.err = w.err;
+  LRM_TRY_HIP(launch_quota_waterfill(a, as_stream(stream)));
+  return LRM_OK;
+}
+
 lrm_status lrm_check_device_errors(void* ws, void* stream) {
   if (!ws) return LRM_ERR_NULL;
   hipStream_t s = as_stream(stream);
@@ -681,6 +709,10 @@ struct Marks {
     if (ev && i < n && ev[i]) return hipEventRecord(reinterpret_cast<hipEvent_t>(ev[i]), s);
     return hipSuccess;
   }
+  // the event of boundary i, for a launcher to record inside its sequence
+  hipEvent_t at(int i) const {
+    return ev && i < n ? reinterpret_cast<hipEvent_t>(ev[i]) : nullptr;
+  }
 };
 
 lrm_status run_linear(const lrm_problem* pb, const lrm_outputs* out, void* ws, hipStream_t s,
@@ -723,8 +755,9 @@ lrm_status run_linear(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   g.offsets = L.offsets; g.Gp = L.Gp; g.Xp = L.Xp; g.W = pb->W; g.w_stride = pb->w_stride;
   g.dW = out->dW; g.dXp = L.dXp; g.mt_off = L.mt_off; g.mt_ready = 1;
   g.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
+  g.mid_event = mark.at(4);
   LRM_TRY_HIP(launch_grouped_gemm(g, s));
-  LRM_TRY_HIP(mark(4));
+  LRM_TRY_HIP(mark(5));
   // 5. back to the layout of X, times the routing weight
   ScatterArgs sa{};
   sa.N = p->N; sa.T = p->T; sa.d = pb->d_in; sa.out_pair = pb->X.rows == LRM_ROWS_PAIR;
@@ -736,7 +769,7 @@ lrm_status run_linear(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   }
   sa.dX = out->dX;
   LRM_TRY_HIP(launch_unpermute(sa, s));
-  LRM_TRY_HIP(mark(5));
+  LRM_TRY_HIP(mark(6));
   return LRM_OK;
 }
 
@@ -778,8 +811,9 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   gd.W = pb->W_down; gd.w_stride = (int64_t)H * I;
   gd.dW = out->dW_down; gd.dXp = L.U; gd.mt_off = L.mt_off; gd.mt_ready = 1;
   gd.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
+  gd.mid_event = mark.at(4);
   LRM_TRY_HIP(launch_grouped_gemm(gd, s));
-  LRM_TRY_HIP(mark(4));
+  LRM_TRY_HIP(mark(5));
   // ---- SwiGLU backward and the gate/up scores
   const bool x_pair = pb->X.rows == LRM_ROWS_PAIR;
   if (!keep_all)
@@ -792,7 +826,7 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   gb.s_gate = keep_all ? nullptr : L.s_gate;
   gb.s_up = keep_all ? nullptr : L.s_up;
   LRM_TRY_HIP(launch_glu_bwd(gb, s));
-  LRM_TRY_HIP(mark(5));
+  LRM_TRY_HIP(mark(6));
   // ---- gate/up selections among the down-kept rows (candidate ids = rows)
   if (!keep_all) {
     // quotas: device arrays, by value (host, E <= kQuotaPackMax), or copied
@@ -823,7 +857,7 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
     LRM_TRY_HIP(launch_select(E, L.offsets, L.off_u, reinterpret_cast<const uint32_t*>(L.s_up),
                               nullptr, L.pos_u, L.kept_u, (int)z.Md, s));
   }
-  LRM_TRY_HIP(mark(6));
+  LRM_TRY_HIP(mark(7));
   const bool x_tok = !x_pair;
   ScatterArgs sa{};
   sa.N = p->N; sa.T = p->T; sa.d = H; sa.out_pair = x_pair;
@@ -836,7 +870,7 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
     cx.offsets = L.offsets; cx.kept = L.kept; cx.token = p->token; cx.weight = p->weight;
     cx.X = pb->X.ptr; cx.ldx = pb->X.ld; cx.xcols = H; cx.x_pair = x_pair; cx.Xp = L.Xgu;
     LRM_TRY_HIP(launch_compact(cx, s));
-    LRM_TRY_HIP(mark(7));
+    LRM_TRY_HIP(mark(8));
     GemmArgs gg{};
     gg.E = E; gg.bf16 = bf16; gg.max_rows = (int)z.Md; gg.d_in = H; gg.d_out = I;
     gg.offsets = L.offsets; gg.Gp = L.GA; gg.Xp = L.Xgu;
@@ -844,13 +878,17 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
     gg.Gp2 = L.GB; gg.W2 = pb->W_up; gg.w2_stride = (int64_t)I * H; gg.d_out2 = I;
     gg.dW = out->dW_gate; gg.dXp = L.dXp; gg.mt_off = L.mt_off;
     gg.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
+    gg.mid_event = mark.at(9);
     LRM_TRY_HIP(launch_grouped_gemm(gg, s));
+    LRM_TRY_HIP(mark(10));
     GemmArgs gu{};
     gu.E = E; gu.bf16 = bf16; gu.max_rows = (int)z.Md; gu.d_in = H; gu.d_out = I;
     gu.offsets = L.offsets; gu.Gp = L.GB; gu.Xp = L.Xgu;
     gu.dW = out->dW_up; gu.dXp = nullptr; gu.mt_off = L.mt_off;
     gu.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
     LRM_TRY_HIP(launch_grouped_gemm(gu, s));
+    LRM_TRY_HIP(mark(11));
+    LRM_TRY_HIP(mark(12));
     sa.pos[0] = L.pos; sa.src[0] = L.dXp; sa.src_rows[0] = (int)z.Md;
   } else {
     const void* GAsrc[2] = {L.GA, L.GB};
@@ -872,7 +910,7 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
       cg.G = GAsrc[k]; cg.ldg = I; cg.gcols = I; cg.g_by_id = 1; cg.Gp = Gpv[k];
       LRM_TRY_HIP(launch_compact(cg, s));
     }
-    LRM_TRY_HIP(mark(7));
+    LRM_TRY_HIP(mark(8));
     for (int k = 0; k < 2; ++k) {
       GemmArgs gk{};
       gk.E = E; gk.bf16 = bf16; gk.max_rows = (int)cap[k]; gk.d_in = H; gk.d_out = I;
@@ -880,19 +918,20 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
       gk.W = Wv[k]; gk.w_stride = (int64_t)I * H;
       gk.dW = dWv[k]; gk.dXp = dXv[k]; gk.mt_off = L.mt_off;
       gk.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
+      gk.mid_event = mark.at(9 + 2 * k);
       LRM_TRY_HIP(launch_grouped_gemm(gk, s));
+      LRM_TRY_HIP(mark(10 + 2 * k));
       sa.pos[k] = L.pos; sa.pos2[k] = posv[k]; sa.src[k] = dXv[k];
       sa.pos2_rows[k] = (int)z.Md; sa.src_rows[k] = (int)cap[k];
     }
   }
-  LRM_TRY_HIP(mark(8));
   if (x_tok) {
     if (p->N == 0) LRM_TRY_HIP(launch_token_offsets(p->N, p->T, p->token, L.tok_off, s));
     sa.tok_off = L.tok_off;
   }
   sa.dX = out->dX;
   LRM_TRY_HIP(launch_unpermute(sa, s));
-  LRM_TRY_HIP(mark(9));
+  LRM_TRY_HIP(mark(13));
   return LRM_OK;
 }
 

@@ -30,7 +30,6 @@
 namespace lrm {
 
 constexpr int kPlanThreads = 1024;
-constexpr uint32_t kErrAssign = 8u;  // assignment does not match the kept counts
 
 // Planning block.  rep_off[e][g] = sum_{g' < g} x[e][g'] (G+1 per expert);
 // blk_off[g][e] = sum_{e' < e} x[e'][g] (E+1 per receiver); send_off[g] =

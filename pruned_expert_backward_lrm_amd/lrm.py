@@ -100,6 +100,9 @@ _sigs = {
     "lrm_workspace_size": (_SZ, [C.POINTER(lrm_problem)]),
     "lrm_check_device_errors": (C.c_int, [_P, _P]),
     "lrm_quota_waterfill": (C.c_int, [_I32, _P, C.c_int64, _P]),
+    "lrm_quota_waterfill_device": (C.c_int, [C.POINTER(lrm_pairs), _P, C.c_int64, _P, _P, _SZ,
+                                             _P]),
+    "lrm_quota_waterfill_device_workspace_size": (_SZ, [C.POINTER(lrm_pairs)]),
     "lrm_redistribute": (C.c_int, [_I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ]),
     "lrm_redistribute_workspace_size": (_SZ, [_I32, _I32]),
     "lrm_receiver_layout": (C.c_int, [_I32, _I32, _P, _P, _I32, _P, _P, _P, _P, _SZ, _P]),
@@ -254,6 +257,19 @@ def lrm_quota_waterfill(counts, budget: int) -> np.ndarray:
     _check(_lib.lrm_quota_waterfill(int(n.shape[0]), _ptr(n), int(budget), _ptr(q)),
            "lrm_quota_waterfill")
     return q
+
+
+def lrm_quota_waterfill_device(pairs: Pairs, budget: int, quota, counts=None, ws=None,
+                               stream=None):
+    """Device call: water-filling quotas written to the device int32 [E] tensor
+    `quota`, from device counts [E] or (counts None) the pairs' own counts.
+    Returns the workspace (its error word reports pairs out of range)."""
+    need = _lib.lrm_quota_waterfill_device_workspace_size(C.byref(pairs.c))
+    ws = _ws(need, quota.device, ws)
+    _check(_lib.lrm_quota_waterfill_device(C.byref(pairs.c), _ptr(counts), int(budget),
+                                           _ptr(quota), _ptr(ws), ws.numel(), _stream(stream)),
+           "lrm_quota_waterfill_device")
+    return ws
 
 
 def lrm_redistribute(kept, replica, base=None, cap=None):
