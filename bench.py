@@ -5,17 +5,24 @@ input already resident in HBM, through the fused C-ABI call: LRM score ->
 per-expert top-quota select -> compaction -> grouped GEMM (dW, dX rows) ->
 unpermute to token layout; SwiGLU workloads chain down -> gate/up stages.
 
+The default workload is the largest single-GPU one, the heavy-skew SwiGLU
+expert layer (T=65536, H=4096, I=1408, E=128, top-8, Zipf 1.6, bf16, fp32
+weight gradients, per-expert caps keeping 0.1-1.0 of each expert's pairs).
+
 Prints ONE JSON line.  `value` is kept pairs per second of the fused call
 (for SwiGLU, pairs kept by the down stage), over K plain fused calls.  Stage
 times come from a second pass of K calls in which the library records HIP
-events on its launch stream at stage boundaries; the
-`roofline` block covers the dominant kernel: for a linear layer the longer
-of the two grouped-GEMM launches (dW or dX), timed alone with HIP events on
-the packed operands of the same call; its `traffic` comes from the committed
-counter runs when they match the kernel source; the `cpu_baseline` block
-times the fp64 CPU oracle on the host cores.
+events on its launch stream at stage boundaries, one boundary after every
+grouped-GEMM launch, so each launch has its own average duration.  The
+`roofline` block covers the dominant kernel, the longest grouped-GEMM launch
+of the call: its algorithmic flops (or bytes, below the ridge) over its
+average duration from those events; `traffic` and `mfma_util` come from the
+committed counter runs (profiles/gemm_counters.json) when they were taken on
+this workload and this GEMM source.  The unpruned call (LRM_KEEP_ALL: every
+pair kept, no score or select) is timed beside it, and the `cpu_baseline`
+block times the fp64 CPU oracle on a stated sample.
 
-    python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu] [--full]
+    python bench.py [--steps K] [--warmup W] [--config 5] [--no-cpu] [--no-full]
 
 `--redistribute` instead prints one JSON line on the redistribution of the
 kept pairs over G=8 GPUs (each expert owned by one, the 16 most loaded
@@ -30,10 +37,10 @@ controller (water-filling caps, lrm_quota_waterfill).
 with every quota at floor(r * n_e) for r in 0.1, 0.25, 0.5, 0.75, 1.0 (all
 projections alike), and the unpruned call, on the chosen workload.
 
-The HBM-traffic record the `roofline.traffic` field reads is written on any
-host, without a GPU, from two profiler passes over `--copy-probe` runs:
+The counter record the `roofline` fields read is written on any host, without
+a GPU, from profiler passes over `--copy-probe --no-full` runs:
 
-    python bench.py --record-traffic FETCH_DIR WRITE_DIR [--config 2]
+    python bench.py --record-counters FETCH_DIR WRITE_DIR [MFMA_DIR] [--config 5]
 """
 
 from __future__ import annotations
@@ -53,6 +60,7 @@ sys.path.insert(0, ROOT)
 METRIC = "kept pairs/s + grouped-GEMM TFLOP/s (% MFMA peak), score/compact GB/s"
 PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+DEFAULT_CONFIG = 5
 
 
 def log(*a):
@@ -62,16 +70,15 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=DEFAULT_CONFIG)
     ap.add_argument("--variant", default=None, help="3b: a real gate/up second selection")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--full", action="store_true",
-                    help="also time the unpruned (keep-all) call: its GEMM launches run other "
-                         "shapes, so it is off by default to keep the kernel statistics of a "
-                         "profiled bench run those of the pruned call")
-    ap.add_argument("--no-full", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--no-full", action="store_true",
+                    help="skip the unpruned (keep-all) call, e.g. in profiler runs whose "
+                         "kernel statistics should be those of the pruned call alone")
+    ap.add_argument("--full", action="store_true", help=argparse.SUPPRESS)  # the default now
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 512 MiB device copy (a known-size kernel that "
                          "calibrates the HBM byte counters of a profiler pass)")
@@ -86,15 +93,16 @@ def parse():
                     help="time the redistribution onto replicas instead of the bench line")
     ap.add_argument("--sweep", action="store_true",
                     help="keep-ratio sweep (quota = floor(r n_e)) instead of the bench line")
-    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="write profiles/hbm_traffic.json from the output folders of a "
-                         "rocprofv3 --pmc FETCH_SIZE and a --pmc WRITE_SIZE pass over "
-                         "`bench.py --no-cpu --copy-probe` (no GPU needed)")
+    ap.add_argument("--record-counters", nargs="+", metavar="DIR",
+                    help="write profiles/gemm_counters.json from the output folders of a "
+                         "rocprofv3 --pmc FETCH_SIZE pass, a --pmc WRITE_SIZE pass and "
+                         "optionally a --pmc MfmaUtil pass over `bench.py --no-cpu --no-full "
+                         "--copy-probe` (no GPU needed)")
     return ap.parse_args()
 
 
 COPY_KIB = 512 * 1024  # bytes moved each way by one copy of copy_probe, in KiB
-TRAFFIC_PATH = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+COUNTERS_PATH = os.path.join(ROOT, "profiles", "gemm_counters.json")
 GEMM_SRC = os.path.join(ROOT, "pruned_expert_backward_lrm_amd", "csrc", "k_gemm.hip")
 
 
@@ -117,92 +125,172 @@ def workload_name(spec, T, E, k, shape, variant=None):
     return f"{spec['name']}{'-' + variant if variant else ''}: {shape} E={E} top-{k} zipf={spec['zipf']}"
 
 
-def gemm_work(E, Me, d_in, d_out, b):
-    """Algorithmic bytes and flops of the two grouped-GEMM launches of a
-    linear layer call with kept counts Me: the dW launch writes every
-    expert's fp32 dW and reads the packed rows once; the dX launch reads W of
-    the active experts and the packed G rows, and writes the fp32 dX rows."""
-    M, act = int(np.sum(Me)), int(np.count_nonzero(Me))
-    return {
-        "dW": dict(bytes=E * d_out * d_in * 4 + M * (d_in + d_out) * b, flops=2.0 * M * d_in * d_out),
-        "dX": dict(bytes=act * d_out * d_in * b + M * d_out * b + M * d_in * 4,
-                   flops=2.0 * M * d_in * d_out),
-    }
+def gemm_roles(kind, pass_through):
+    """The grouped-GEMM launches of one fused call, in launch order."""
+    if kind == "linear":
+        return ["gemm_dW", "gemm_dX"]
+    if pass_through:
+        return ["gemm_down_dW", "gemm_down_dX", "gemm_gate_dW", "gemm_gate_dX", "gemm_up_dW"]
+    return ["gemm_down_dW", "gemm_down_dX", "gemm_gate_dW", "gemm_gate_dX", "gemm_up_dW",
+            "gemm_up_dX"]
 
 
-def record_traffic(fetch_dir, write_dir, cfg):
-    """profiles/hbm_traffic.json from two counter passes: per GEMM launch, the
-    average FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by what the same
-    counter reads for the three 512 MiB copies of --copy-probe."""
+def glu_pass_through(p):
+    """The gate/up selections keep every down-kept row (one shared dX launch)."""
+    return bool(np.all(np.asarray(p["quota_gate"]) >= np.asarray(p["quota_down"]))
+                and np.all(np.asarray(p["quota_up"]) >= np.asarray(p["quota_down"])))
+
+
+def workload_of(cfg, variant=None):
+    """Workload name and the per-launch algorithmic work of one pruned call,
+    from the routing and the quotas alone (no GPU)."""
+    from pruned_expert_backward_lrm_amd import synth
+    spec = synth.CONFIGS[cfg]
+    r = synth.make_routing(spec["T"], spec["E"], spec["k"], spec["zipf"], "cfg", cfg,
+                           local=spec.get("local"))
+    q = synth._quotas(cfg, r, variant)
+    b = 2 if spec["dtype"] == "bf16" else 4
+    if spec["kind"] == "linear":
+        shape = f"T={r.T} d_in={spec['d_in']} d_out={spec['d_out']}"
+        Me = np.minimum(q["quota"], r.counts).astype(np.int64)
+        work = gemm_launch_work("linear", r.E, b, 4, Me, d_in=spec["d_in"], d_out=spec["d_out"])
+        return workload_name(spec, r.T, r.E, r.k, shape, variant), work, True
+    shape = f"T={r.T} H={spec['H']} I={spec['I']}"
+    Md = np.minimum(q["quota_down"], r.counts).astype(np.int64)
+    Mg = np.minimum(q["quota_gate"], Md)
+    Mu = np.minimum(q["quota_up"], Md)
+    pt = glu_pass_through(q)
+    work = gemm_launch_work("swiglu", r.E, b, 4, Md, Mg, Mu, H=spec["H"], I=spec["I"],
+                            pass_through=pt)
+    return workload_name(spec, r.T, r.E, r.k, shape, variant), work, pt
+
+
+def gemm_launch_work(kind, E, b, wb, Md, Mg=None, Mu=None, d_in=0, d_out=0, H=0, I=0,
+                     pass_through=True):
+    """Algorithmic bytes and flops of each grouped-GEMM launch of one call.
+    A dW launch writes every expert's dW (wb bytes an element) and reads its
+    packed operands once; a dX launch reads W of the experts that kept rows
+    and its packed gradient rows once, and writes the fp32 dX rows."""
+    def dw(M, do, di):
+        return dict(bytes=E * do * di * wb + int(M.sum()) * (di + do) * b,
+                    flops=2.0 * int(M.sum()) * di * do)
+
+    def dx(M, do, di, nseg=1):
+        act = int(np.count_nonzero(M))
+        return dict(bytes=nseg * (act * do * di * b + int(M.sum()) * do * b)
+                    + int(M.sum()) * di * 4,
+                    flops=2.0 * nseg * int(M.sum()) * di * do)
+
+    if kind == "linear":
+        return {"gemm_dW": dw(Md, d_out, d_in), "gemm_dX": dx(Md, d_out, d_in)}
+    w = {"gemm_down_dW": dw(Md, H, I), "gemm_down_dX": dx(Md, H, I),
+         "gemm_gate_dW": dw(Mg, I, H), "gemm_up_dW": dw(Mu, I, H)}
+    if pass_through:
+        w["gemm_gate_dX"] = dx(Md, I, H, nseg=2)   # gate and up in one launch, K = 2I
+    else:
+        w["gemm_gate_dX"] = dx(Mg, I, H)
+        w["gemm_up_dX"] = dx(Mu, I, H)
+    return w
+
+
+def record_counters(dirs, cfg, variant=None):
+    """profiles/gemm_counters.json from counter passes: per grouped-GEMM launch
+    of the call, the average FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
+    scaled by what the same counter reads for the three 512 MiB copies of
+    --copy-probe, and (third pass, optional) the average MfmaUtil.  The
+    dispatches of each fused call come in launch order (gemm_roles)."""
     import csv
     import glob
 
+    workload, work, pt = workload_of(cfg, variant)
     from pruned_expert_backward_lrm_amd import synth
-    spec = synth.CONFIGS[cfg]
-    if spec["kind"] != "linear":
-        raise SystemExit("--record-traffic covers the linear workloads (one dW and one dX launch)")
-    r = synth.make_routing(spec["T"], spec["E"], spec["k"], spec["zipf"], "cfg", cfg,
-                           local=spec.get("local"))
-    q = synth._quotas(cfg, r, None)["quota"]
-    Me = np.minimum(np.maximum(q, 0), r.counts).astype(np.int64)
-    b = torch.tensor([], dtype=synth.torch_dtype(spec["dtype"])).element_size()
-    work = gemm_work(r.E, Me, spec["d_in"], spec["d_out"], b)
-    workload = workload_name(spec, r.T, r.E, r.k,
-                             f"T={r.T} d_in={spec['d_in']} d_out={spec['d_out']}")
-    per, scale, names = {"dW": {}, "dX": {}}, {}, {}
-    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+    roles = gemm_roles(synth.CONFIGS[cfg]["kind"], pt)
+    counters = ["FETCH_SIZE", "WRITE_SIZE", "MfmaUtil"][:len(dirs)]
+    per = {role: {} for role in roles}
+    names, scale = {}, {}
+    for counter, d in zip(counters, dirs):
         rows = [row for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"),
                                        recursive=True)
                 for row in csv.DictReader(open(f)) if row["Counter_Name"] == counter]
         rows.sort(key=lambda row: int(row["Dispatch_Id"]))
-        copies = [float(row["Counter_Value"]) for row in rows
-                  if row["Kernel_Name"] == "__amd_rocclr_copyBuffer"][:3]
-        if len(copies) != 3:
-            raise SystemExit(f"{d}: no --copy-probe copies found for {counter}")
-        scale[counter] = float(np.mean(copies)) / COPY_KIB
-        for kind, tail in (("dW", "false>(lrm::GemmPlan)"), ("dX", "true>(lrm::GemmPlan)")):
-            vals = [float(row["Counter_Value"]) for row in rows
-                    if "k_gemm_stream<" in row["Kernel_Name"] and row["Kernel_Name"].endswith(tail)]
-            if not vals:
-                raise SystemExit(f"{d}: no {kind} grouped-GEMM dispatches")
-            names[kind] = next(row["Kernel_Name"] for row in rows
-                               if "k_gemm_stream<" in row["Kernel_Name"]
-                               and row["Kernel_Name"].endswith(tail))
-            per[kind][counter] = (float(np.mean(vals)), len(vals))
+        if counter != "MfmaUtil":
+            copies = [float(row["Counter_Value"]) for row in rows
+                      if row["Kernel_Name"] == "__amd_rocclr_copyBuffer"][:3]
+            if len(copies) != 3:
+                raise SystemExit(f"{d}: no --copy-probe copies found for {counter}")
+            scale[counter] = float(np.mean(copies)) / COPY_KIB
+        gemm = [row for row in rows if "k_gemm_stream" in row["Kernel_Name"]
+                or "k_grouped_gemm" in row["Kernel_Name"]]
+        if not gemm or len(gemm) % len(roles):
+            raise SystemExit(f"{d}: {len(gemm)} grouped-GEMM dispatches, not a whole number "
+                             f"of calls of {len(roles)} launches")
+        for i, role in enumerate(roles):
+            vals = [float(row["Counter_Value"]) for row in gemm[i::len(roles)]]
+            names[role] = gemm[i]["Kernel_Name"]
+            per[role][counter] = (float(np.mean(vals)), len(vals))
     sha = gemm_source_sha()
-    kernels = []
-    for kind in ("dW", "dX"):
-        fk, n = per[kind]["FETCH_SIZE"]
-        wk, _ = per[kind]["WRITE_SIZE"]
+    launches = []
+    for role in roles:
+        fk, n = per[role]["FETCH_SIZE"]
+        wk, _ = per[role]["WRITE_SIZE"]
         fb = fk / scale["FETCH_SIZE"] * 1024
-        wb = wk / scale["WRITE_SIZE"] * 1024
-        alg = work[kind]["bytes"]
-        kernels.append({"kernel": f"k_gemm_stream<{kind}>", "profiler_name": names[kind],
-                        "workload": workload, "source_sha256": sha, "dispatches": n,
-                        "fetch_kib_raw": round(fk, 1), "write_kib_raw": round(wk, 1),
-                        "fetch_bytes": int(round(fb)), "write_bytes": int(round(wb)),
-                        "hbm_bytes": int(round(fb + wb)), "algorithmic_bytes": int(alg),
-                        "traffic_over_algorithmic": round((fb + wb) / alg, 3)})
+        wbytes = wk / scale["WRITE_SIZE"] * 1024
+        alg = work[role]["bytes"]
+        e = {"launch": role, "profiler_name": names[role], "workload": workload,
+             "source_sha256": sha, "dispatches": n,
+             "fetch_kib_raw": round(fk, 1), "write_kib_raw": round(wk, 1),
+             "fetch_bytes": int(round(fb)), "write_bytes": int(round(wbytes)),
+             "hbm_bytes": int(round(fb + wbytes)), "algorithmic_bytes": int(alg),
+             "traffic_over_algorithmic": round((fb + wbytes) / alg, 3),
+             "algorithmic_flops": work[role]["flops"]}
+        if "MfmaUtil" in per[role]:
+            e["mfma_util_pct"] = round(per[role]["MfmaUtil"][0], 2)
+        launches.append(e)
+    try:
+        with open(COUNTERS_PATH) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    keep = [e for e in rec.get("launches", []) if e.get("workload") != workload]
+    cmd_tail = f"--config {cfg}{' --variant ' + variant if variant else ''}"
     rec = {
-        "note": ("HBM bytes per launch of the grouped-GEMM kernels, from two rocprofv3 --pmc "
+        "note": ("Per grouped-GEMM launch of the fused call: HBM bytes from rocprofv3 --pmc "
                  "passes (FETCH_SIZE, WRITE_SIZE, KiB per dispatch) scaled by what the same "
-                 f"counters read for a 512 MiB device copy (FETCH_SIZE reads "
-                 f"{scale['FETCH_SIZE']:.4f}, WRITE_SIZE {scale['WRITE_SIZE']:.4f} of the true "
-                 "bytes). source_sha256 is the SHA-256 of csrc/k_gemm.hip, comments and "
-                 "whitespace removed, that the counters were taken on."),
+                 "counter reads for a 512 MiB device copy in the same run, and the average "
+                 "MfmaUtil (MFMA busy cycles over GPU active cycles and SIMDs, %).  "
+                 "source_sha256 is the SHA-256 of csrc/k_gemm.hip, comments and whitespace "
+                 "removed, that the counters were taken on."),
         "commands": [
-            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d " + fetch_dir
-            + f" -o run -- python bench.py --config {cfg} --no-cpu --copy-probe --steps 5 --warmup 2",
-            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d " + write_dir
-            + f" -o run -- python bench.py --config {cfg} --no-cpu --copy-probe --steps 5 --warmup 2",
-            f"python bench.py --config {cfg} --record-traffic {fetch_dir} {write_dir}",
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d FETCH_DIR -o run -- python "
+            f"bench.py {cmd_tail} --no-cpu --no-full --copy-probe --steps 3 --warmup 1",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d WRITE_DIR -o run -- python "
+            f"bench.py {cmd_tail} --no-cpu --no-full --copy-probe --steps 3 --warmup 1",
+            "rocprofv3 --pmc MfmaUtil --output-format csv -d MFMA_DIR -o run -- python "
+            f"bench.py {cmd_tail} --no-cpu --no-full --copy-probe --steps 3 --warmup 1",
+            f"python bench.py {cmd_tail} --record-counters FETCH_DIR WRITE_DIR MFMA_DIR",
         ],
-        "kernels": kernels,
+        "launches": keep + launches,
     }
-    with open(TRAFFIC_PATH, "w") as f:
+    with open(COUNTERS_PATH, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
-    print(json.dumps(rec, indent=1))
+    print(json.dumps({"workload": workload, "launches": launches}, indent=1))
+
+
+def counters_of(role, workload):
+    """The committed counter record of one launch, or None when it was taken on
+    another workload or another version of the GEMM source."""
+    try:
+        with open(COUNTERS_PATH) as f:
+            rec = json.load(f)
+        sha = gemm_source_sha()
+    except (OSError, ValueError):
+        return None
+    for e in rec.get("launches", []):
+        if e.get("launch") == role and e.get("workload") == workload \
+                and e.get("source_sha256") == sha:
+            return e
+    return None
 
 
 def copy_probe(dev):
@@ -247,8 +335,9 @@ class Workload:
             rows = r.T if p["X_rows"] == "token" else r.N
             self.out = dict(dW=torch.empty(r.E, p["d_out"], p["d_in"], dtype=wdt, device=dev),
                             dX=torch.empty(rows, p["d_in"], **f32))
-            self.stages = ["score", "select", "compact", "grouped_gemm", "unpermute"]
-            self.gemm_stages = ["grouped_gemm"]
+            self.pass_through = True
+            # the spans between the library's stage boundaries (lrm.h)
+            self.stages = ["score", "select", "compact", "gemm_dW", "gemm_dX", "unpermute"]
         else:
             t = [p[k] for k in ("X", "G", "A", "B", "W_gate", "W_up", "W_down")]
             q = (p["quota_down"], p["quota_gate"], p["quota_up"])
@@ -260,14 +349,19 @@ class Workload:
             wd = dict(dtype=wdt, device=dev)
             self.out = dict(dW_gate=torch.empty(r.E, I, H, **wd),
                             dW_up=torch.empty(r.E, I, H, **wd),
-                            dW_down=torch.empty(r.E, H, I, **wd), dX=torch.empty(r.T, H, **f32))
-            self.stages = ["score_down", "select_down", "compact_down", "gemm_down", "glu_bwd",
-                           "select_gate_up", "compact_gate_up", "gemm_gate_up", "unpermute"]
-            self.gemm_stages = ["gemm_down", "gemm_gate_up"]
+                            dW_down=torch.empty(r.E, H, I, **wd), dX=torch.empty(r.T, H, **f32),
+                            offsets_gate=torch.empty(r.E + 1, **i32),
+                            offsets_up=torch.empty(r.E + 1, **i32))
+            self.pass_through = glu_pass_through(p)
+            self.stages = ["score_down", "select_down", "compact_down", "gemm_down_dW",
+                           "gemm_down_dX", "glu_bwd", "select_gate_up", "compact_gate_up",
+                           "gemm_gate_dW", "gemm_gate_dX", "gemm_up_dW", "gemm_up_dX",
+                           "unpermute"]
+        self.gemm_roles = gemm_roles(self.kind, self.pass_through)
         self.out["offsets"] = torch.empty(r.E + 1, **i32)
         u8 = dict(dtype=torch.uint8, device=dev)
         self.ws = torch.empty(L.lrm_workspace_size(self.pb), **u8)
-        self.ws_full = torch.empty(L.lrm_workspace_size(self.pb_full), **u8)
+        self.ws_full = None
         self.out_full = dict(self.out)
         self.out_full["offsets"] = torch.empty(r.E + 1, **i32)
 
@@ -278,56 +372,65 @@ class Workload:
             self.L.lrm_expert_backward_events(self.pb, self.out, events, ws=self.ws)
 
     def step_full(self):
+        if self.ws_full is None:
+            self.ws_full = torch.empty(self.L.lrm_workspace_size(self.pb_full), dtype=torch.uint8,
+                                       device=self.ws.device)
         self.L.lrm_expert_backward(self.pb_full, self.out_full, ws=self.ws_full)
 
     def kept(self):
+        """Kept rows per expert of the last pruned call: down (or the single
+        projection), gate, up."""
         torch.cuda.synchronize()
-        offs = self.out["offsets"].cpu().numpy().astype(np.int64)
-        return int(offs[-1]), np.diff(offs)
+        d = lambda k: np.diff(self.out[k].cpu().numpy().astype(np.int64))  # noqa: E731
+        Me = d("offsets")
+        if self.kind == "linear":
+            return Me, Me, Me
+        return Me, d("offsets_gate"), d("offsets_up")
 
-    def work(self, M, Me):
+    def work(self, Md, Mg, Mu):
         """Algorithmic bytes (and flops) of each stage: what the method must
         move, with the packed rows counted once and fp32 outputs."""
         p, r = self.p, self.r
         b = self.p["X"].element_size()
         wb = 2 if self.dwb else 4  # bytes of a stored weight-gradient element
-        act = int(np.count_nonzero(Me))
         E, N, T = r.E, r.N, r.T
+        M = int(Md.sum())
         if self.kind == "linear":
             di, do = p["d_in"], p["d_out"]
             xr = T if p["X_rows"] == "token" else N
             gr = T if p["G_rows"] == "token" else N
-            return {
+            w = {
                 "score": dict(bytes=(xr * di + gr * do) * b + N * 12),
                 "select": dict(bytes=N * 8 + M * 4),
                 "compact": dict(bytes=2 * M * (di + do) * b),
-                "grouped_gemm": dict(bytes=E * do * di * wb + act * do * di * b
-                                     + M * (di + do) * b + M * di * 4,
-                                     flops=4.0 * M * di * do),
                 "unpermute": dict(bytes=M * di * 4 + T * di * 4),
             }
+            w.update(gemm_launch_work("linear", E, b, wb, Md, d_in=di, d_out=do))
+            return w
         H, I = p["H"], p["I"]
-        return {
+        Mgs, Mus = int(Mg.sum()), int(Mu.sum())
+        w = {
             "score_down": dict(bytes=T * H * b + (N * 8 if self.htab is not None else 2 * N * I * b)
                                + N * 12),
             "select_down": dict(bytes=N * 8 + M * 4),
             "compact_down": dict(bytes=2 * M * H * b + 3 * M * I * b),
-            "gemm_down": dict(bytes=act * H * I * b + E * H * I * wb + M * (H + I) * b
-                              + M * I * 4, flops=4.0 * M * H * I),
             "glu_bwd": dict(bytes=T * H * b + M * I * 4 + 4 * M * I * b),
-            "select_gate_up": dict(bytes=2 * (M * 8)),
-            "compact_gate_up": dict(bytes=2 * M * H * b),
-            "gemm_gate_up": dict(bytes=2 * act * I * H * b + 2 * E * I * H * wb
-                                 + M * (2 * I + H) * b + M * H * 4, flops=8.0 * M * H * I),
-            "unpermute": dict(bytes=M * H * 4 + T * H * 4),
+            "select_gate_up": dict(bytes=2 * (M * 8) + (Mgs + Mus) * 4),
+            "compact_gate_up": dict(bytes=2 * M * H * b if self.pass_through
+                                    else 2 * (Mgs + Mus) * (H + I) * b),
+            "unpermute": dict(bytes=M * H * 4 * (1 if self.pass_through else 2) + T * H * 4),
         }
+        w.update(gemm_launch_work("swiglu", E, b, wb, Md, Mg, Mu, H=H, I=I,
+                                  pass_through=self.pass_through))
+        return w
 
 
 def time_fused(W, steps, warmup):
     """Wall time per step of the plain fused call (the timed region holds the
     steps only), then the per-stage split from a second pass of the same
-    steps with HIP events recorded at the stage boundaries (the events cost a
-    little GPU time of their own, so they stay out of the first pass)."""
+    steps with HIP events recorded by the library at its stage boundaries,
+    one after every grouped-GEMM launch (the events cost a little GPU time of
+    their own, so they stay out of the first pass)."""
     wall = time_loop(W.step, steps, warmup)
     n = len(W.stages) + 1
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n)] for _ in range(steps)]
@@ -343,68 +446,6 @@ def time_fused(W, steps, warmup):
     per = {name: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)]))
            for i, name in enumerate(W.stages)}
     return wall, per, wall_ev
-
-
-def gemm_kernels(W, steps, warmup):
-    """Times the two grouped-GEMM launches of a linear layer call on their
-    own, on the same packed operands the fused call builds: the dW kernel
-    (dW_e = Gp_e^T Xp_e) and the dX kernel (dXp_e = Gp_e W_e).  HIP events on
-    the launch stream around `steps` launches each.  Returns, per kernel, the
-    average launch duration and its algorithmic bytes and flops."""
-    L, p, r = W.L, W.p, W.r
-    dev = W.out["dW"].device
-    i32 = dict(dtype=torch.int32, device=dev)
-    X, G = L.mat(p["X"], p["X_rows"]), L.mat(p["G"], p["G_rows"])
-    score = torch.empty(r.N, dtype=torch.float32, device=dev)
-    L.lrm_score(W.pairs, X, G, score)
-    pos, kept = torch.empty(r.N, **i32), torch.empty(max(r.N, 1), **i32)
-    offsets = torch.empty(r.E + 1, **i32)
-    L.lrm_select(W.pairs, score, p["quota"], pos, offsets, kept, device=dev)
-    M = int(offsets[-1].item())
-    di, do = p["d_in"], p["d_out"]
-    Xp = torch.empty(max(M, 1), di, dtype=p["X"].dtype, device=dev)
-    Gp = torch.empty(max(M, 1), do, dtype=p["G"].dtype, device=dev)
-    L.lrm_compact(W.pairs, kept, offsets, M, X, G, Xp, Gp)
-    dW = torch.empty(r.E, do, di, dtype=torch.float32, device=dev)
-    dXp = torch.empty(max(M, 1), di, dtype=torch.float32, device=dev)
-    ws = torch.empty(1 << 16, dtype=torch.uint8, device=dev)
-    Me = np.diff(offsets.cpu().numpy().astype(np.int64))
-    work = gemm_work(r.E, Me, di, do, p["X"].element_size())
-    runs = {
-        "dW": (lambda: L.lrm_grouped_bwd(r.E, offsets, M, Gp, Xp, p["W"], di, do, dW, None, ws=ws),
-               work["dW"]),
-        "dX": (lambda: L.lrm_grouped_bwd(r.E, offsets, M, Gp, Xp, p["W"], di, do, None, dXp, ws=ws),
-               work["dX"]),
-    }
-    res = {}
-    for name, (fn, work) in runs.items():
-        for _ in range(warmup):
-            fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(steps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        res[name] = dict(work, ms=e0.elapsed_time(e1) / steps)
-    return res
-
-
-def traffic_of(kernel, workload):
-    """HBM bytes per launch from the committed counter runs (profiles/
-    hbm_traffic.json), or None when they were taken on another workload or on
-    another version of the kernel source."""
-    try:
-        with open(TRAFFIC_PATH) as f:
-            rec = json.load(f)
-        sha = gemm_source_sha()
-    except (OSError, ValueError):
-        return None
-    for e in rec.get("kernels", []):
-        if e.get("kernel") == kernel and e.get("workload") == workload and e.get("source_sha256") == sha:
-            return e.get("hbm_bytes")
-    return None
 
 
 def copy_gbs(dev, reps=10):
@@ -561,12 +602,13 @@ def cpu_baseline(p, M, Me):
                 "sample": f"the whole workload, one pass (score, select, pack, dW, dX) in fp64 "
                           f"NumPy; {dt:.1f} s on {cores} host cores"}
     # SwiGLU: all down scores and selections, then the full backward of a
-    # sample of experts holding about 5% of the kept rows
+    # sample of experts (every third by kept rows, largest first) holding
+    # about a third of the kept rows
     host = dict(p, **{k: p[k].cpu() for k in ("X", "G", "A", "B", "W_gate", "W_up", "W_down")})
-    order = np.argsort(Me)
+    order = np.argsort(Me, kind="stable")
     ex, tot = [], 0
-    for e in order[::-1][::7]:
-        if tot > 0.05 * M:
+    for e in order[::-1][::3]:
+        if tot >= M / 3:
             break
         if Me[e] > 0:
             ex.append(int(e))
@@ -582,8 +624,10 @@ def cpu_baseline(p, M, Me):
 
 def main():
     a = parse()
-    if a.record_traffic:
-        record_traffic(a.record_traffic[0], a.record_traffic[1], a.config)
+    if a.record_counters:
+        if not 2 <= len(a.record_counters) <= 3:
+            raise SystemExit("--record-counters FETCH_DIR WRITE_DIR [MFMA_DIR]")
+        record_counters(a.record_counters, a.config, a.variant)
         return
     if a.gpus != 1:
         log("bench.py: this build runs on exactly one GPU (one GPU's share of the experts); "
@@ -617,19 +661,23 @@ def main():
     r = p["routing"]
     log("bench: timing the pruned backward")
     wall, per, wall_ev = time_fused(W, a.steps, a.warmup)
-    M, Me = W.kept()
+    Md, Mg, Mu = W.kept()
+    M = int(Md.sum())
     ms_full = None
-    if a.full and not a.no_full:
+    if not a.no_full:
         log("bench: timing the unpruned backward (every pair kept)")
         ms_full = time_loop(W.step_full, a.steps, a.warmup) * 1e3
-    work = W.work(M, Me)
-    flops = sum(work[s]["flops"] for s in W.gemm_stages)
-    gbytes = sum(work[s]["bytes"] for s in W.gemm_stages)
-    t_g = sum(per[s] for s in W.gemm_stages) * 1e-3
+        W.ws_full = None
+        torch.cuda.empty_cache()
+    work = W.work(Md, Mg, Mu)
+    roles = W.gemm_roles
+    flops = sum(work[s]["flops"] for s in roles)
+    gbytes = sum(work[s]["bytes"] for s in roles)
+    gemm_stages = [s for s in W.stages if s.startswith("gemm_")]
+    t_g = sum(per[s] for s in gemm_stages) * 1e-3
     ai = flops / gbytes
     peak_tf = PEAK_TFLOPS[p["dtype"]]
     ridge = peak_tf * 1e12 / (PEAK_HBM_GBS * 1e9)
-    gbs = gbytes / t_g / 1e9
     tflops = flops / t_g / 1e12
     spec = synth.CONFIGS[a.config]
     if p["kind"] == "linear":
@@ -637,33 +685,40 @@ def main():
     else:
         shape = f"T={r.T} H={p['H']} I={p['I']}"
     workload = workload_name(spec, r.T, r.E, r.k, shape, a.variant)
-    kernels = None
-    if p["kind"] == "linear" and not a.dw_bf16:
-        # the dominant kernel: the longer of the two GEMM launches, timed alone
-        log("bench: timing the grouped-GEMM kernels alone")
-        kernels = gemm_kernels(W, a.steps, a.warmup)
-        name = max(kernels, key=lambda k: kernels[k]["ms"])
-        kd = kernels[name]
-        # bf16 runs the two stream kernels; fp32 one tiled FMA kernel over either tile kind
-        kname = (f"k_gemm_stream<{name}>" if p["dtype"] == "bf16"
-                 else f"k_grouped_gemm_f32 ({name} tiles)")
-        k_ai, k_t = kd["flops"] / kd["bytes"], kd["ms"] * 1e-3
-        k_gbs, k_tf = kd["bytes"] / k_t / 1e9, kd["flops"] / k_t / 1e12
-        traffic = traffic_of(kname, workload)
+    launches = {}
+    for role in roles:
+        t = per[role] * 1e-3
+        w = work[role]
+        launches[role] = {"ms": round(per[role], 4), "flops": w["flops"], "bytes": w["bytes"],
+                          "tflops": round(w["flops"] / t / 1e12, 2),
+                          "pct_mfma_peak": round(100 * w["flops"] / t / 1e12 / peak_tf, 2),
+                          "gbs": round(w["bytes"] / t / 1e9, 1),
+                          "pct_attainable": round(100 * w["flops"] / t / 1e12 / attainable_tflops(
+                              w["flops"] / w["bytes"], peak_tf), 2)}
+    # the dominant kernel: the longest grouped-GEMM launch of the call
+    dom = max(roles, key=lambda k: per[k])
+    kd, k_t = work[dom], per[dom] * 1e-3
+    rec = counters_of(dom, workload) if not a.dw_bf16 and not a.h_table else None
+    if kd["flops"] / kd["bytes"] < ridge:
+        k_gbs = kd["bytes"] / k_t / 1e9
+        roof = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(k_gbs / PEAK_HBM_GBS, 4)}
     else:
-        # SwiGLU: the GEMM stages as a whole (several launches)
-        kname, k_ai, k_gbs, k_tf, traffic = "gemm stages", ai, gbs, tflops, None
-    if k_ai < ridge:
-        roof = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(k_gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
-    else:
+        k_tf = kd["flops"] / k_t / 1e12
         roof = {"bound": "mfma", "achieved": round(k_tf, 2), "peak": peak_tf,
-                "unit": "TFLOP/s", "frac": round(k_tf / peak_tf, 4), "traffic": traffic}
-    roof["kernel"] = kname
-    mem_stages = [s for s in W.stages if s not in W.gemm_stages]
+                "unit": "TFLOP/s", "frac": round(k_tf / peak_tf, 4)}
+    roof["traffic"] = rec["hbm_bytes"] if rec else None
+    roof["kernel"] = dom
+    roof["profiler_name"] = rec["profiler_name"] if rec else None
+    roof["mfma_util_pct"] = rec.get("mfma_util_pct") if rec else None
+    roof["algorithmic_flops"] = kd["flops"]
+    roof["algorithmic_bytes"] = kd["bytes"]
+    roof["launch_ms"] = round(per[dom], 4)
+    mem_stages = [s for s in W.stages if not s.startswith("gemm_") and s in work]
     log("bench: measuring device-copy bandwidth")
     cgbs = copy_gbs(dev)
     sc = [s for s in W.stages if s.startswith("score") or s.startswith("compact")]
+    gbs_of = lambda s: work[s]["bytes"] / (per[s] * 1e-3) / 1e9  # noqa: E731
     line = {
         "metric": METRIC,
         "value": round(M / wall, 1),
@@ -680,34 +735,31 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload, "dw_dtype": "bf16" if a.dw_bf16 else "f32",
                    "h_table": bool(a.h_table and p["kind"] != "linear"),
-                   "pairs": r.N, "kept_pairs": M, "active_experts": int(np.count_nonzero(Me))},
+                   "pairs": r.N, "kept_pairs": M, "active_experts": int(np.count_nonzero(Md)),
+                   **({} if p["kind"] == "linear" else
+                      {"kept_gate": int(Mg.sum()), "kept_up": int(Mu.sum())})},
         "roofline": roof,
-        "gemm_kernels": ({k: {"ms": round(v["ms"], 4), "bytes": v["bytes"], "flops": v["flops"],
-                              "gbs": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1),
-                              "tflops": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 2),
-                              "pct_attainable": round(
-                                  100 * v["flops"] / (v["ms"] * 1e-3) / 1e12
-                                  / attainable_tflops(v["flops"] / v["bytes"], peak_tf), 2)}
-                          for k, v in kernels.items()} if kernels else None),
+        "gemm_launches": launches,
         "grouped_gemm": {"ms": round(t_g * 1e3, 4), "tflops": round(tflops, 2),
                          "pct_mfma_peak": round(100 * tflops / peak_tf, 2),
                          "pct_attainable": round(100 * tflops / attainable_tflops(ai, peak_tf), 2),
-                         "gbs": round(gbs, 1), "flops": flops, "bytes": gbytes,
+                         "gbs": round(gbytes / t_g / 1e9, 1), "flops": flops, "bytes": gbytes,
                          "arith_intensity": round(ai, 1)},
         "stages_ms": {s: round(v, 4) for s, v in per.items()},
-        "stages_gbs": {s: round(work[s]["bytes"] / (per[s] * 1e-3) / 1e9, 1) for s in mem_stages},
-        "copy_gbs": round(cgbs, 1),
-        "stages_frac_of_copy": {s: round(work[s]["bytes"] / (per[s] * 1e-3) / 1e9 / cgbs, 3)
-                                for s in mem_stages},
+        "stages_gbs": {s: round(gbs_of(s), 1) for s in mem_stages},
+        "stages_frac_of_hbm_peak": {s: round(gbs_of(s) / PEAK_HBM_GBS, 3) for s in mem_stages},
+        "memory_stages_gbs": round(sum(work[s]["bytes"] for s in mem_stages)
+                                   / (sum(per[s] for s in mem_stages) * 1e-3) / 1e9, 1),
         "score_compact_gbs": round(sum(work[s]["bytes"] for s in sc)
                                    / (sum(per[s] for s in sc) * 1e-3) / 1e9, 1),
+        "copy_gbs": round(cgbs, 1),
         "unpruned_ms_per_step": round(ms_full, 4) if ms_full else None,
         "kept_fraction": round(M / r.N, 4),
         "pruned_over_unpruned_time": round(wall * 1e3 / ms_full, 4) if ms_full else None,
     }
     if not a.no_cpu:
         log("bench: timing the CPU oracle")
-        line["cpu_baseline"] = cpu_baseline(p, M, Me)
+        line["cpu_baseline"] = cpu_baseline(p, M, Md)
     print(json.dumps(line), flush=True)
 
 
