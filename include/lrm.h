@@ -181,6 +181,22 @@ lrm_status lrm_select(const lrm_pairs* pairs, const float* score, const int32_t*
                       size_t ws_bytes, void* stream);
 size_t lrm_select_workspace_size(const lrm_pairs* pairs);
 
+/* lrm_select for callers that cannot allocate memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * selection, results and flags, with its scratch in a device array of the
+ * library, LRM_SELECT_STATIC_SCRATCH_BYTES per GPU, held from the first use
+ * on a GPU until the process ends.  Calls no allocation routine.  Returns
+ * LRM_ERR_WORKSPACE, having enqueued nothing, when
+ * lrm_select_workspace_size(pairs) exceeds that size (for example more than
+ * about a million pairs with 4096 experts).  Every call on one GPU uses that
+ * GPU's one array: calls that overlap on one GPU (concurrent streams or
+ * threads) race and give undefined results; calls ordered on one stream do
+ * not.  The first call on a device also looks the array's address up. */
+#define LRM_SELECT_STATIC_SCRATCH_BYTES (32u << 20)
+lrm_status lrm_select_static(const lrm_pairs* pairs, const float* score, const int32_t* quota,
+                             uint32_t flags, int32_t* pos, int32_t* offsets, int32_t* kept,
+                             void* stream);
+
 /* Physical compaction (page 1, bullet "Физическое уплотнение"): gathers the
  * kept rows into dense per-expert blocks,
  *   Xp[m] = w_p * (X row of p)   (rounded to X's dtype)

@@ -2,6 +2,7 @@
 // workspace planning and the stream-ordered launch sequences.  Nothing here
 // allocates device memory; scratch comes from the caller's workspace.
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "lrm.h"
@@ -328,6 +329,53 @@ lrm_status lrm_select(const lrm_pairs* pairs, const float* score, const int32_t*
   SelectWs w = carve_select(r, pairs->N, pairs->E);
   return run_select(pairs, score, keep_all ? nullptr : quota, pos, offsets, kept, w, s, nullptr,
                     nullptr, 0, qdev);
+}
+
+}  // extern "C"
+
+// Scratch of lrm_select_static: one array per GPU, loaded with the code
+// object and held until the process ends.  Host code never uses its name as
+// an address: the device address comes from hipGetSymbolAddress, taken once
+// per device with that device current.
+static __device__ __align__(256) unsigned char scratch[LRM_SELECT_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of scratch.
+lrm_status static_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LRM_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return LRM_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LRM_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LRM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lrm_status lrm_select_static(const lrm_pairs* pairs, const float* score, const int32_t* quota,
+                             uint32_t flags, int32_t* pos, int32_t* offsets, int32_t* kept,
+                             void* stream) {
+  LRM_TRY(check_pairs(pairs));
+  if (lrm_select_workspace_size(pairs) > (size_t)LRM_SELECT_STATIC_SCRATCH_BYTES)
+    return LRM_ERR_WORKSPACE;
+  void* ws = nullptr;
+  LRM_TRY(static_scratch(&ws));
+  // every scratch word the selection reads is written earlier in the same
+  // call, so the previous call's contents need no clearing
+  return lrm_select(pairs, score, quota, flags, pos, offsets, kept, ws,
+                    LRM_SELECT_STATIC_SCRATCH_BYTES, stream);
 }
 
 lrm_status lrm_compact(const lrm_pairs* pairs, const int32_t* kept, const int32_t* offsets,

@@ -99,6 +99,7 @@ _sigs = {
                                              _SZ, _P, C.POINTER(C.c_void_p), _I32]),
     "lrm_workspace_size": (_SZ, [C.POINTER(lrm_problem)]),
     "lrm_check_device_errors": (C.c_int, [_P, _P]),
+    "lrm_select_static": (C.c_int, [C.POINTER(lrm_pairs), _P, _P, C.c_uint32, _P, _P, _P, _P]),
     "lrm_quota_waterfill": (C.c_int, [_I32, _P, C.c_int64, _P]),
     "lrm_quota_waterfill_device": (C.c_int, [C.POINTER(lrm_pairs), _P, C.c_int64, _P, _P, _SZ,
                                              _P]),
@@ -214,6 +215,15 @@ def lrm_select(pairs: Pairs, score, quota, pos, offsets, kept, flags=0, ws=None,
                            _ptr(offsets), _ptr(kept), _ptr(ws), ws.numel(), _stream(stream)),
            "lrm_select")
     return ws
+
+
+def lrm_select_static(pairs: Pairs, score, quota, pos, offsets, kept, flags=0, stream=None):
+    """lrm_select with the library's own scratch array (no workspace, no
+    allocation)."""
+    q = _quota_arr(quota) if quota is not None else None
+    _check(_lib.lrm_select_static(C.byref(pairs.c), _ptr(score), _ptr(q), flags, _ptr(pos),
+                                  _ptr(offsets), _ptr(kept), _stream(stream)),
+           "lrm_select_static")
 
 
 def lrm_compact(pairs: Pairs, kept, offsets, max_rows: int, X: lrm_mat, G: lrm_mat, Xp, Gp,

@@ -78,6 +78,12 @@ inline hipError_t hipOccupancyMaxActiveBlocksPerMultiprocessor(int* n, K, int, s
   *n = 1;
   return hipSuccess;
 }
+#define __align__(n) __attribute__((aligned(n)))
+#define HIP_SYMBOL(x) (&(x))
+inline hipError_t hipGetSymbolAddress(void** p, const void* sym) {
+  *p = const_cast<void*>(sym);
+  return hipSuccess;
+}
 typedef void* hipEvent_t;
 inline hipError_t hipEventRecord(hipEvent_t, hipStream_t) { return hipSuccess; }
 
