@@ -93,6 +93,11 @@ def parse():
                     help="time the redistribution onto replicas instead of the bench line")
     ap.add_argument("--sweep", action="store_true",
                     help="keep-ratio sweep (quota = floor(r n_e)) instead of the bench line")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print a markdown summary of a rocprofv3 --kernel-trace --stats run of "
+                         "this bench (same --config/--steps/--warmup): every grouped-GEMM "
+                         "launch of the pruned calls on its own, and the kernel statistics "
+                         "(no GPU needed)")
     ap.add_argument("--record-counters", nargs="+", metavar="DIR",
                     help="write profiles/gemm_counters.json from the output folders of a "
                          "rocprofv3 --pmc FETCH_SIZE pass, a --pmc WRITE_SIZE pass and "
@@ -275,6 +280,57 @@ def record_counters(dirs, cfg, variant=None):
         json.dump(rec, f, indent=1)
         f.write("\n")
     print(json.dumps({"workload": workload, "launches": launches}, indent=1))
+
+
+def summarize_trace(d, cfg, steps, warmup, variant=None):
+    """Markdown summary of a kernel-trace run of this bench: the dispatches of
+    the grouped-GEMM kernels come in calls of len(gemm_roles) launches; the
+    first warmup + 2 * steps calls are the pruned ones (plain, then with
+    stage events), so each launch of the pruned call gets its own average
+    duration, comparable with the events of the bench line."""
+    import csv
+    import glob
+
+    from pruned_expert_backward_lrm_amd import synth
+    workload, work, pt = workload_of(cfg, variant)
+    roles = gemm_roles(synth.CONFIGS[cfg]["kind"], pt)
+    trace = sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True))
+    stats = sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True))
+    if not trace:
+        raise SystemExit(f"{d}: no kernel trace")
+    rows = [r for f in trace for r in csv.DictReader(open(f))]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    gemm = [r for r in rows if "k_gemm_stream" in r["Kernel_Name"]
+            or "k_grouped_gemm" in r["Kernel_Name"]]
+    ncalls = warmup + 2 * steps
+    pruned = gemm[:ncalls * len(roles)]
+    if len(pruned) != ncalls * len(roles):
+        raise SystemExit(f"{d}: {len(gemm)} grouped-GEMM dispatches, fewer than {ncalls} calls")
+    out = [f"Workload: {workload}.", "",
+           f"Each pruned call makes {len(roles)} grouped-GEMM launches; the first {ncalls} "
+           f"calls of the run ({warmup} warm-up, {steps} plain, {steps} with stage events) "
+           "are pruned calls.  Per launch (kernel trace, end minus start of each dispatch):", "",
+           "| launch | kernel | dispatches | avg µs | min µs | max µs | algorithmic TFLOP/s "
+           "at avg | % of 2.5 PF |", "|---|---|---|---|---|---|---|---|"]
+    for i, role in enumerate(roles):
+        ds = pruned[i::len(roles)]
+        us = np.array([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in ds])
+        name = ds[0]["Kernel_Name"].replace("lrm::", "").replace("void ", "")
+        tf = work[role]["flops"] / (us.mean() * 1e-6) / 1e12
+        out.append(f"| {role} | `{name}` | {us.size} | {us.mean():.1f} | {us.min():.1f} | "
+                   f"{us.max():.1f} | {tf:.1f} | {100 * tf / PEAK_TFLOPS['bf16']:.1f} |")
+    if stats:
+        out += ["", "Kernel statistics of the whole run (`*_kernel_stats.csv`, library "
+                "kernels, every call of the run including the unpruned ones):", "",
+                "| kernel | calls | avg µs | min µs | max µs | % of GPU time |",
+                "|---|---|---|---|---|---|"]
+        srows = [r for r in csv.DictReader(open(stats[0])) if "lrm::" in r["Name"]]
+        for r in srows[:16]:
+            name = r["Name"].replace("lrm::", "").replace("void ", "")
+            out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                       f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                       f"{float(r['Percentage']):.2f} |")
+    print("\n".join(out))
 
 
 def counters_of(role, workload):
@@ -624,6 +680,9 @@ def cpu_baseline(p, M, Me):
 
 def main():
     a = parse()
+    if a.summarize_trace:
+        summarize_trace(a.summarize_trace, a.config, a.steps, a.warmup, a.variant)
+        return
     if a.record_counters:
         if not 2 <= len(a.record_counters) <= 3:
             raise SystemExit("--record-counters FETCH_DIR WRITE_DIR [MFMA_DIR]")
