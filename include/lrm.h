@@ -209,6 +209,18 @@ lrm_status lrm_compact(const lrm_pairs* pairs, const int32_t* kept, const int32_
                        int32_t max_rows, const lrm_mat* X, const lrm_mat* G, void* Xp, void* Gp,
                        void* stream);
 
+/* Compaction into dense blocks per receiver and expert (page 1, bullets
+ * "Перераспределение" and "Физическое уплотнение"): lrm_compact with packed
+ * row m written to row dst[m] of Xp and Gp instead of row m.
+ * dst: device [max_rows] int32, the receiver-major row of every expert-major
+ * packed row, as lrm_receiver_layout writes it (receiver g's rows from
+ * send_off[g], expert e's inside them from blk_off[g][e]); NULL is the
+ * identity (lrm_compact).  dst must map the rows m < offsets[E] one to one
+ * into [0, max_rows); a row whose dst lies outside is not written. */
+lrm_status lrm_compact_rows(const lrm_pairs* pairs, const int32_t* kept, const int32_t* offsets,
+                            int32_t max_rows, const int32_t* dst, const lrm_mat* X,
+                            const lrm_mat* G, void* Xp, void* Gp, void* stream);
+
 /* Variable-size grouped GEMMs on the packed blocks, no zero padding (page 1,
  * bullet "Физическое уплотнение"): for every expert e with packed rows
  * [offsets[e], offsets[e+1]) of Gp [rows][d_out] and Xp [rows][d_in]:

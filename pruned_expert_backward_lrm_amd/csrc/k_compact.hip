@@ -1,6 +1,7 @@
 // Physical compaction: kept gradient and activation rows are gathered into
 // dense per-expert blocks, expert after expert, with no padding (LRMoE page 1,
-// section on what LRMoE does, bullet "Физическое уплотнение").  The routing
+// section on what LRMoE does, bullet "Физическое уплотнение"), or, through a
+// row map, into dense blocks per receiver and expert (the same bullet).  The routing
 // weight is folded into the activation side here (Xp = w x), so the grouped
 // GEMM computes dW_e = Gp_e^T Xp_e directly.
 //
@@ -97,6 +98,8 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   const int M = min(a.offsets[a.E], a.max_rows);
   const int nw = gridDim.x * 4;
   for (int j = blockIdx.x * 4 + (threadIdx.x >> 6); j < M; j += nw) {
+    const int o = a.dst ? a.dst[j] : j;  // output row (wave-uniform)
+    if (o < 0 || o >= a.max_rows) continue;
     const int id = a.kept[j];
     const int p = a.pairmap ? a.pairmap[id] : id;
     const int t = a.token[p];
@@ -104,7 +107,7 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
       const float w = a.weight[p];
       const int64_t xr = (a.x_pair || a.glu) ? (int64_t)p : (int64_t)t;
       const u32x4* src = reinterpret_cast<const u32x4*>((const char*)a.X + xr * a.ldx * kEsz);
-      u32x4* dst = reinterpret_cast<u32x4*>((char*)a.Xp + (int64_t)j * a.xcols * kEsz);
+      u32x4* dst = reinterpret_cast<u32x4*>((char*)a.Xp + (int64_t)o * a.xcols * kEsz);
       if (a.glu) {
         const u32x4* src2 =
             reinterpret_cast<const u32x4*>((const char*)a.X2 + xr * a.ldx2 * kEsz);
@@ -119,7 +122,7 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
     if (a.Gp) {
       const int64_t gr = a.g_by_id ? (int64_t)id : (a.g_pair ? (int64_t)p : (int64_t)t);
       const u32x4* src = reinterpret_cast<const u32x4*>((const char*)a.G + gr * a.ldg * kEsz);
-      u32x4* dst = reinterpret_cast<u32x4*>((char*)a.Gp + (int64_t)j * a.gcols * kEsz);
+      u32x4* dst = reinterpret_cast<u32x4*>((char*)a.Gp + (int64_t)o * a.gcols * kEsz);
       copy_row(dst, src, a.gcols / kEpc, [](u32x4 v) { return v; });
     }
   }

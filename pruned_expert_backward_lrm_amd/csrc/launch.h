@@ -116,10 +116,13 @@ hipError_t launch_quota_waterfill(const QuotaArgs& a, hipStream_t s);
 //   Xp[j] = w_p * X[x_pair ? p : token[p]]            (glu = 0)
 //   Xp[j] = w_p * silu(X[p]) * X2[p]                  (glu = 1, PAIR rows)
 //   Gp[j] = G[g_by_id ? a : (g_pair ? p : token[p])]
+// written to row dst[j] instead of j when dst is given (rows outside
+// [0, max_rows) are skipped).
 struct CompactArgs {
   int T, bf16, max_rows, E;
   const int32_t* offsets;
   const int32_t* kept;
+  const int32_t* dst;
   const int32_t* pairmap;
   const int32_t* token;
   const float* weight;

@@ -381,6 +381,12 @@ lrm_status lrm_select_static(const lrm_pairs* pairs, const float* score, const i
 lrm_status lrm_compact(const lrm_pairs* pairs, const int32_t* kept, const int32_t* offsets,
                        int32_t max_rows, const lrm_mat* X, const lrm_mat* G, void* Xp, void* Gp,
                        void* stream) {
+  return lrm_compact_rows(pairs, kept, offsets, max_rows, nullptr, X, G, Xp, Gp, stream);
+}
+
+lrm_status lrm_compact_rows(const lrm_pairs* pairs, const int32_t* kept, const int32_t* offsets,
+                            int32_t max_rows, const int32_t* dst, const lrm_mat* X,
+                            const lrm_mat* G, void* Xp, void* Gp, void* stream) {
   LRM_TRY(check_pairs(pairs));
   if (!X || !G) return LRM_ERR_NULL;
   LRM_TRY(check_mat(X, pairs, X->dtype, -1, -1));
@@ -390,7 +396,8 @@ lrm_status lrm_compact(const lrm_pairs* pairs, const int32_t* kept, const int32_
   if ((Xp && !aligned16(Xp)) || (Gp && !aligned16(Gp))) return LRM_ERR_ALIGN;
   CompactArgs a{};
   a.T = pairs->T; a.bf16 = X->dtype == LRM_BF16; a.max_rows = max_rows; a.E = pairs->E;
-  a.offsets = offsets; a.kept = kept; a.token = pairs->token; a.weight = pairs->weight;
+  a.offsets = offsets; a.kept = kept; a.dst = dst; a.token = pairs->token;
+  a.weight = pairs->weight;
   a.X = X->ptr; a.ldx = X->ld; a.xcols = X->cols; a.x_pair = X->rows == LRM_ROWS_PAIR; a.Xp = Xp;
   a.G = G->ptr; a.ldg = G->ld; a.gcols = G->cols; a.g_pair = G->rows == LRM_ROWS_PAIR; a.Gp = Gp;
   LRM_TRY_HIP(launch_compact(a, as_stream(stream)));

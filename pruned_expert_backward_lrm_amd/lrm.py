@@ -88,6 +88,8 @@ _sigs = {
     "lrm_select_workspace_size": (_SZ, [C.POINTER(lrm_pairs)]),
     "lrm_compact": (C.c_int, [C.POINTER(lrm_pairs), _P, _P, _I32, C.POINTER(lrm_mat),
                               C.POINTER(lrm_mat), _P, _P, _P]),
+    "lrm_compact_rows": (C.c_int, [C.POINTER(lrm_pairs), _P, _P, _I32, _P, C.POINTER(lrm_mat),
+                                   C.POINTER(lrm_mat), _P, _P, _P]),
     "lrm_grouped_bwd": (C.c_int, [_I32, _P, _I32, _I32, _P, _P, _P, C.c_int64, _I32, _I32, _P, _P,
                                   _P, _SZ, _P]),
     "lrm_grouped_bwd_workspace_size": (_SZ, [_I32]),
@@ -231,6 +233,15 @@ def lrm_compact(pairs: Pairs, kept, offsets, max_rows: int, X: lrm_mat, G: lrm_m
     _check(_lib.lrm_compact(C.byref(pairs.c), _ptr(kept), _ptr(offsets), int(max_rows),
                             C.byref(X), C.byref(G), _ptr(Xp), _ptr(Gp), _stream(stream)),
            "lrm_compact")
+
+
+def lrm_compact_rows(pairs: Pairs, kept, offsets, max_rows: int, dst, X: lrm_mat, G: lrm_mat,
+                     Xp, Gp, stream=None):
+    """lrm_compact writing packed row m to row dst[m] (receiver-major rows)."""
+    _check(_lib.lrm_compact_rows(C.byref(pairs.c), _ptr(kept), _ptr(offsets), int(max_rows),
+                                 _ptr(dst), C.byref(X), C.byref(G), _ptr(Xp), _ptr(Gp),
+                                 _stream(stream)),
+           "lrm_compact_rows")
 
 
 def lrm_grouped_bwd(E: int, offsets, max_rows: int, Gp, Xp, W, d_in: int, d_out: int, dW, dXp,

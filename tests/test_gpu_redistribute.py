@@ -91,3 +91,54 @@ def test_layout_after_selection():
     peak, x = L.lrm_redistribute(Me, Rm)
     assert peak == R.min_peak(Me, Rm)[0]
     _layout(Me, x)
+
+
+def test_compaction_into_receiver_blocks():
+    """The config-2 selection spread over 8 GPUs (experts owned round robin,
+    the 16 most loaded replicated on all), then compaction straight into the
+    receiver-major blocks: the row map matches the oracle's receiver layout
+    bit for bit, every receiver-major row is the expert-major packed row it
+    maps from (bit for bit), and equals the fp64 w x (or g) row of the pair
+    packed there, within one bf16 rounding (exactly for g)."""
+    from oracle import lrm_oracle as O
+    p = synth.make_config(2, device=DEV)
+    r = p["routing"]
+    pairs = L.Pairs.from_routing(r, DEV)
+    X, G = L.mat(p["X"], "token"), L.mat(p["G"], "pair")
+    score = torch.empty(r.N, dtype=torch.float32, device=DEV)
+    L.lrm_score(pairs, X, G, score)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    pos, kept, offsets = torch.empty(r.N, **i32), torch.empty(r.N, **i32), torch.empty(r.E + 1, **i32)
+    L.lrm_select(pairs, score, p["quota"], pos, offsets, kept, device=DEV)
+    offs = offsets.cpu().numpy().astype(np.int64)
+    Me = np.diff(offs)
+    M = int(offs[-1])
+    Rm = np.zeros((r.E, 8), bool)
+    Rm[np.arange(r.E), np.arange(r.E) % 8] = True
+    Rm[np.argsort(-Me, kind="stable")[:16]] = True
+    _, x = L.lrm_redistribute(Me, Rm)
+    dst = torch.as_tensor(_layout(Me, x), device=DEV)
+    di, do = p["d_in"], p["d_out"]
+    bf = dict(dtype=torch.bfloat16, device=DEV)
+    Xp, Gp = torch.zeros(M, di, **bf), torch.zeros(M, do, **bf)
+    Xr, Gr = torch.zeros(M, di, **bf), torch.zeros(M, do, **bf)
+    L.lrm_compact(pairs, kept, offsets, M, X, G, Xp, Gp)
+    L.lrm_compact_rows(pairs, kept, offsets, M, dst, X, G, Xr, Gr)
+    torch.cuda.synchronize()
+    d = dst.long()
+    assert torch.equal(Xr[d], Xp) and torch.equal(Gr[d], Gp)
+    # against the oracle: its row map for these kept counts, and the fp64 rows
+    # of the pairs packed there (the kept sets themselves are judged by the
+    # selection parity tests)
+    host = dict(p, X=p["X"].cpu(), G=p["G"].cpu())
+    _, _, odst = R.receiver_layout(offs, x)
+    assert odst.tolist() == dst.cpu().numpy().tolist()
+    ids = kept[:M].cpu().numpy().astype(np.int64)
+    inv = np.empty(M, np.int64)
+    inv[odst] = np.arange(M)
+    ids_at = ids[inv]  # pair packed at each receiver-major row
+    g64 = O.pair_rows(host["G"], "pair", r.token, ids_at)
+    x64 = O.pair_rows(host["X"], "token", r.token, ids_at) * r.weight[ids_at][:, None]
+    assert np.array_equal(Gr.double().cpu().numpy(), g64)
+    rel = np.abs(Xr.double().cpu().numpy() - x64) / np.maximum(np.abs(x64), 1e-30)
+    assert rel.max() <= 2.0 ** -8, rel.max()
