@@ -87,6 +87,9 @@ def parse():
                          "(computed before timing), so the down score reads no A/B rows")
     ap.add_argument("--dw-bf16", action="store_true",
                     help="weight gradients stored as bf16 (LRM_DW_BF16) instead of fp32")
+    ap.add_argument("--gather", action="store_true",
+                    help="LRM_GATHER_LOADS: the w*x operand of the weight-gradient GEMMs is "
+                         "gathered by their loaders instead of packed by compaction")
     ap.add_argument("--controller", action="store_true",
                     help="compare the workload's quotas with water-filling quotas of equal budget")
     ap.add_argument("--redistribute", action="store_true",
@@ -363,9 +366,10 @@ def copy_probe(dev):
 class Workload:
     """Problem descriptors, outputs and workspaces of one layer call."""
 
-    def __init__(self, L, p, dev, dw_bf16=False, h_table=False):
+    def __init__(self, L, p, dev, dw_bf16=False, h_table=False, gather=False):
         self.L, self.p, self.r = L, p, p["routing"]
         self.dwb = dw_bf16
+        self.gather = gather
         self.htab = None
         if h_table and p["kind"] != "linear":
             # what a forward pass would save: |silu(a) b|^2 per pair, fp64
@@ -375,7 +379,7 @@ class Workload:
                 a, b = A[i:i + (1 << 16)].float(), B[i:i + (1 << 16)].float()
                 h = a * torch.sigmoid(a) * b
                 self.htab[i:i + (1 << 16)] = (h * h).sum(dim=1, dtype=torch.float64)
-        fl = L.LRM_DW_BF16 if dw_bf16 else 0
+        fl = (L.LRM_DW_BF16 if dw_bf16 else 0) | (L.LRM_GATHER_LOADS if gather else 0)
         wdt = torch.bfloat16 if dw_bf16 else torch.float32
         r = self.r
         self.pairs = L.Pairs.from_routing(r, dev)
@@ -458,7 +462,8 @@ class Workload:
             w = {
                 "score": dict(bytes=(xr * di + gr * do) * b + N * 12),
                 "select": dict(bytes=N * 8 + M * 4),
-                "compact": dict(bytes=2 * M * (di + do) * b),
+                "compact": dict(bytes=2 * M * do * b + M * 8 if self.gather
+                                else 2 * M * (di + do) * b),
                 "unpermute": dict(bytes=M * di * 4 + T * di * 4),
             }
             w.update(gemm_launch_work("linear", E, b, wb, Md, d_in=di, d_out=do))
@@ -472,8 +477,10 @@ class Workload:
             "compact_down": dict(bytes=2 * M * H * b + 3 * M * I * b),
             "glu_bwd": dict(bytes=T * H * b + M * I * 4 + 4 * M * I * b),
             "select_gate_up": dict(bytes=2 * (M * 8) + (Mgs + Mus) * 4),
-            "compact_gate_up": dict(bytes=2 * M * H * b if self.pass_through
-                                    else 2 * (Mgs + Mus) * (H + I) * b),
+            "compact_gate_up": dict(bytes=(M * 8 if self.gather else 2 * M * H * b)
+                                    if self.pass_through
+                                    else 2 * (Mgs + Mus) * ((0 if self.gather else H) + I) * b
+                                    + ((Mgs + Mus) * 8 if self.gather else 0)),
             "unpermute": dict(bytes=M * H * 4 * (1 if self.pass_through else 2) + T * H * 4),
         }
         w.update(gemm_launch_work("swiglu", E, b, wb, Md, Mg, Mu, H=H, I=I,
@@ -716,7 +723,7 @@ def main():
         log("bench: keep-ratio sweep")
         print(json.dumps(keep_sweep(L, synth, p, dev, a.steps, a.warmup, a.config)), flush=True)
         return
-    W = Workload(L, p, dev, a.dw_bf16, a.h_table)
+    W = Workload(L, p, dev, a.dw_bf16, a.h_table, a.gather)
     r = p["routing"]
     log("bench: timing the pruned backward")
     wall, per, wall_ev = time_fused(W, a.steps, a.warmup)
@@ -757,7 +764,7 @@ def main():
     # the dominant kernel: the longest grouped-GEMM launch of the call
     dom = max(roles, key=lambda k: per[k])
     kd, k_t = work[dom], per[dom] * 1e-3
-    rec = counters_of(dom, workload) if not a.dw_bf16 and not a.h_table else None
+    rec = counters_of(dom, workload) if not (a.dw_bf16 or a.h_table or a.gather) else None
     if kd["flops"] / kd["bytes"] < ridge:
         k_gbs = kd["bytes"] / k_t / 1e9
         roof = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": PEAK_HBM_GBS,
@@ -793,6 +800,7 @@ def main():
         "dtype": p["dtype"],
         "data": "synthetic",
         "config": {"workload": workload, "dw_dtype": "bf16" if a.dw_bf16 else "f32",
+                   "gather_loads": bool(a.gather),
                    "h_table": bool(a.h_table and p["kind"] != "linear"),
                    "pairs": r.N, "kept_pairs": M, "active_experts": int(np.count_nonzero(Md)),
                    **({} if p["kind"] == "linear" else

@@ -107,6 +107,16 @@ typedef enum lrm_kind { LRM_LINEAR = 0, LRM_SWIGLU = 1 } lrm_kind;
  * out of range, or tokens out of order (what lrm_check_device_errors reports,
  * and clears, without the extra call). */
 #define LRM_DEBUG_CHECKS 8u
+/* Gathering GEMM loaders (bf16 inputs): the weight-gradient GEMMs whose
+ * packed operand is w * x (LINEAR; the SwiGLU gate and up projections) read
+ * the kept rows of X themselves, scaling them by w and rounding to bf16 in
+ * the loader, instead of reading a packed copy that compaction writes; the
+ * compaction then writes only a row map (4 + 4 bytes per kept row).  Results
+ * are bit for bit those of the call without the flag.  Trades time for
+ * memory: the workspace loses the packed copy (kept rows x d_in x 2 bytes),
+ * but the gathering loaders are slower than the packed ones on MI355X.
+ * Ignored for fp32 inputs and when X takes 2 GiB or more. */
+#define LRM_GATHER_LOADS 16u
 
 /* The routed pairs of one layer call (the page's "pair": one token -> expert
  * choice; page 1 introduction). */
@@ -342,7 +352,8 @@ size_t lrm_receiver_layout_workspace_size(int32_t E, int32_t G);
 
 typedef struct lrm_problem {
   int32_t kind;    /* lrm_kind */
-  uint32_t flags;  /* LRM_KEEP_ALL, LRM_DW_BF16, LRM_QUOTA_ON_DEVICE, LRM_DEBUG_CHECKS */
+  uint32_t flags;  /* LRM_KEEP_ALL, LRM_DW_BF16, LRM_QUOTA_ON_DEVICE, LRM_DEBUG_CHECKS,
+                      LRM_GATHER_LOADS */
   int32_t dtype;   /* lrm_dtype of every dense input */
   int32_t _pad;
   lrm_pairs pairs;

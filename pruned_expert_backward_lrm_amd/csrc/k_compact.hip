@@ -128,6 +128,26 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   }
 }
 
+// One thread per packed row: the source row and routing weight of each kept
+// row, for a GEMM loader that gathers and scales the rows itself.
+__global__ __launch_bounds__(256) void k_row_map(CompactArgs a, int32_t* __restrict__ xrow,
+                                                 float* __restrict__ xw) {
+  const int M = min(a.offsets[a.E], a.max_rows);
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= M) return;
+  const int id = a.kept[j];
+  const int p = a.pairmap ? a.pairmap[id] : id;
+  xrow[j] = a.x_pair ? p : a.token[p];
+  xw[j] = a.weight[p];
+}
+
+hipError_t launch_row_map(const CompactArgs& a, int32_t* xrow, float* xw, hipStream_t s) {
+  if (a.max_rows <= 0) return hipSuccess;
+  if (!a.offsets || !a.kept || !a.token || !a.weight || !xrow || !xw) return hipErrorInvalidValue;
+  LRM_LAUNCH((a.max_rows + 255) / 256, 256, 0, s, k_row_map)(a, xrow, xw);
+  return hipGetLastError();
+}
+
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
   if (a.max_rows <= 0 || (!a.Xp && !a.Gp)) return hipSuccess;
   if (!a.offsets || !a.kept || !a.token || !a.weight) return hipErrorInvalidValue;

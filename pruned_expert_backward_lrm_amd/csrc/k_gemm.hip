@@ -243,6 +243,85 @@ struct TransTile {
   }
 };
 
+// The B panel of dW gathered from its source rows: packed row k of B is
+// w_k * src[row_k] rounded to bf16 (what compaction would have stored), so no
+// packed copy is written or read.  The same 4(k) x 8(n) blocks and register
+// transposition as TransTile; each of a lane's four rows has its own source
+// row and weight, read from the row map of the k-tile.  Rows at or past kend
+// load zeros.  src rows are addressed with 32-bit byte offsets (the host
+// keeps src under 2 GiB).
+template <int R, int NT>
+struct GatherTile {
+  using T = TransTile<R, NT>;
+  static constexpr int Q = T::Q;
+  u32x4 v[Q][4];
+  float w[Q][4];
+  int kgq[Q], col[Q];  // k group of the lane's block, byte offset of its 8 columns
+  // the row map of the next load, requested one load ahead (prefetch()), so
+  // that the X rows of a k-tile do not wait for their row indices
+  int nrow[Q][4];
+  float nw[Q][4];
+  __device__ __forceinline__ void init(int64_t) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int b = threadIdx.x + q * NT;
+      int kg, ng;
+      T::block_of(b, &kg, &ng);
+      kgq[q] = b < T::NB ? kg : 1 << 20;  // (threadIdx.x < NT: every lane has a block)
+      col[q] = ng * 8 * 2;
+    }
+  }
+  // the row map of k-tile k0 of a segment, for the next load(); rows at or
+  // past kend get -1 (zeros)
+  __device__ __forceinline__ void prefetch(const int32_t* rows, const float* wts, int k0,
+                                           int kend) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int k = k0 + kgq[q] * 4 + r;
+        const bool ok = k < kend;
+        nrow[q][r] = ok ? rows[k] : -1;
+        nw[q][r] = ok ? wts[k] : 0.f;
+      }
+  }
+  // the X rows of the k-tile whose row map the last prefetch() requested
+  __device__ __forceinline__ void load(const char* src, int64_t ld, int64_t src_rows, int n0) {
+    const rsrc_t rs = make_rsrc(src, src_rows * ld * 2);
+    const int rb = (int)(ld * 2);
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        w[q][r] = nw[q][r];
+        v[q][r] = bload(rs, nrow[q][r] >= 0 ? nrow[q][r] * rb + n0 * 2 + col[q] : 0x7ffffff0);
+      }
+  }
+  __device__ __forceinline__ void store(uint16_t* lds) const {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int b = threadIdx.x + q * NT;
+      if (T::NB % NT != 0 && b >= T::NB) continue;
+      int kg, ng;
+      T::block_of(b, &kg, &ng);
+      u32x4 s[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s[r][i] = pack_bf16x2(bf16_lo(v[q][r][i]) * w[q][r], bf16_hi(v[q][r][i]) * w[q][r]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int wd = c >> 1, h = c & 1;
+        u32x2 o;
+        o[0] = pick_half(s[0][wd], s[1][wd], h);
+        o[1] = pick_half(s[2][wd], s[3][wd], h);
+        *reinterpret_cast<u32x2*>(lds + lds_off(ng * 8 + c, kg)) = o;
+      }
+    }
+  }
+};
+
 // One K segment of an output tile.  A panel: direct (dX: Gp rows, k
 // contiguous) or transposed (dW: Gp columns); B panel: always transposed.
 // Both segments of a dual-K tile share the leading dimensions.
@@ -251,6 +330,7 @@ struct TileSrc {
   int a_rows_valid;  // direct A: rows of the tile inside the expert's block
   int a_n0, b_n0;    // transposed panels: first column of the tile
   int K;             // k extent (direct: columns of A; transposed: valid rows)
+  const int32_t* brow; const float* bw;  // gathered B: row map of the expert's rows
 };
 
 __device__ __forceinline__ TileSrc pick_seg(const TileSrc& x, const TileSrc& y, bool first) {
@@ -261,19 +341,25 @@ __device__ __forceinline__ TileSrc pick_seg(const TileSrc& x, const TileSrc& y, 
   r.a_n0 = first ? x.a_n0 : y.a_n0;
   r.b_n0 = first ? x.b_n0 : y.b_n0;
   r.K = first ? x.K : y.K;
+  r.brow = first ? x.brow : y.brow;
+  r.bw = first ? x.bw : y.bw;
   return r;
 }
 
-template <class C, bool A_DIRECT>
+// GB: the B panel gathered (GatherTile) instead of read from packed rows.
+template <class C, bool A_DIRECT, bool GB = false>
 struct Stage {
   using ATile = typename std::conditional<A_DIRECT, DirectTile<C::BM, C::NT>,
                                           TransTile<C::BM, C::NT>>::type;
+  using BTile = typename std::conditional<GB, GatherTile<C::BN, C::NT>,
+                                          TransTile<C::BN, C::NT>>::type;
   ATile A;
-  TransTile<C::BN, C::NT> B;
-  int64_t lda, ldb;
-  __device__ __forceinline__ void init(int64_t la, int64_t lb) {
+  BTile B;
+  int64_t lda, ldb, b_rows;
+  __device__ __forceinline__ void init(int64_t la, int64_t lb, int64_t brows = 0) {
     lda = la;
     ldb = lb;
+    b_rows = brows;
     A.init(la);
     B.init(lb);
   }
@@ -282,7 +368,14 @@ struct Stage {
       A.load(s.a, lda, s.a_rows_valid, k0, s.K);
     else
       A.load(s.a, lda, k0, s.K, s.a_n0);
-    B.load(s.b, ldb, k0, s.K, s.b_n0);
+    if constexpr (GB)
+      B.load(s.b, ldb, b_rows, s.b_n0);
+    else
+      B.load(s.b, ldb, k0, s.K, s.b_n0);
+  }
+  // gathered B: the row map of the load after this one
+  __device__ __forceinline__ void prefetch(const TileSrc& s, int k0) {
+    if constexpr (GB) B.prefetch(s.brow, s.bw, k0, s.K);
   }
   __device__ __forceinline__ void store(uint16_t* As, uint16_t* Bs) const {
     A.store(As);
@@ -317,7 +410,15 @@ __device__ __forceinline__ Job make_job(const GemmPlan& P, int t) {
     const int kb = ld_table(a.offsets, e);
     const int Me = max(0, min(ld_table(a.offsets, e + 1), a.max_rows) - kb);
     j.s0.a = (const char*)a.Gp + (int64_t)kb * a.d_out * 2;
-    j.s0.b = (const char*)a.Xp + (int64_t)kb * a.d_in * 2;
+    if (a.xrow) {  // gathered B: the source matrix and the expert's row map
+      j.s0.b = (const char*)a.xsrc;
+      j.s0.brow = a.xrow + kb;
+      j.s0.bw = a.xw + kb;
+    } else {
+      j.s0.b = (const char*)a.Xp + (int64_t)kb * a.d_in * 2;
+      j.s0.brow = nullptr;
+      j.s0.bw = nullptr;
+    }
     j.s0.a_rows_valid = 0; j.s0.a_n0 = i0; j.s0.b_n0 = j0;
     j.s0.K = Me;
     j.s1 = j.s0;
@@ -336,6 +437,8 @@ __device__ __forceinline__ Job make_job(const GemmPlan& P, int t) {
     j.s0.b = (const char*)a.W + (int64_t)e * a.w_stride * 2;
     j.s0.a_rows_valid = rows; j.s0.a_n0 = 0; j.s0.b_n0 = j0;
     j.s0.K = a.d_out;
+    j.s0.brow = nullptr;
+    j.s0.bw = nullptr;
     j.s1 = j.s0;
     j.nk0 = j.nk = (a.d_out + BK - 1) / BK;
     if (a.Gp2) {  // second segment of the same shape (host-checked: d_out2 == d_out)
@@ -511,7 +614,7 @@ __device__ __forceinline__ void dw_share(const GemmPlan& P, int x, int* lo, int*
 // ahead, one barrier per k-tile.  The loads of a tile's first k-tiles are thus
 // in flight while the previous tile's outputs are written.  A tile with no
 // k-tiles (an expert that kept no rows) writes zeros.
-template <class C, bool DX, bool DWB>
+template <class C, bool DX, bool DWB, bool GB = false>
 __device__ __forceinline__ void gemm_stream(const GemmPlan& P) {
   __shared__ __attribute__((aligned(16))) uint16_t As[C::STAGES * C::BM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[C::STAGES * C::BN * BK];
@@ -544,11 +647,15 @@ __device__ __forceinline__ void gemm_stream(const GemmPlan& P) {
   }
   if (tc >= hi) return;
 
-  Stage<C, DX> st;
-  st.init(a.d_out, a.d_in);
+  Stage<C, DX, GB> st;
+  if constexpr (GB)
+    st.init(a.d_out, a.ldxs, a.xsrc_rows);
+  else
+    st.init(a.d_out, a.d_in);
   // load cursor: tile tl (job jl), k-tile kl, two k-tiles ahead of the compute
   int tl = tc, kl = 0;
   Job jl = jc;
+  if constexpr (GB) st.prefetch(jl.s0, 0);  // the row map of the first load
 #define LRM_ISSUE_LOAD()                                                        \
   if (tl < hi) {                                                                \
     const bool first = kl < jl.nk0;                                             \
@@ -559,6 +666,10 @@ __device__ __forceinline__ void gemm_stream(const GemmPlan& P) {
         jl = make_job<C, DX>(P, tl);                                            \
         if (jl.nk > 0) break;                                                   \
       }                                                                         \
+    }                                                                           \
+    if (GB && tl < hi) {                                                        \
+      const bool f2 = kl < jl.nk0;                                              \
+      st.prefetch(pick_seg(jl.s0, jl.s1, f2), (f2 ? kl : kl - jl.nk0) * BK);   \
     }                                                                           \
   }
   // With two LDS stages the loads of k-tile i+2 are issued as soon as k-tile
@@ -623,6 +734,12 @@ __global__ __launch_bounds__(C::NT, C::WPE) void k_gemm_stream(GemmPlan P) {
 template <class C>
 __global__ __launch_bounds__(C::NT, C::WPE) void k_gemm_stream_dwbf16(GemmPlan P) {
   gemm_stream<C, false, true>(P);
+}
+
+// dW products with the B panel gathered from its source rows (fp32 or bf16 dW)
+template <class C, bool DWB>
+__global__ __launch_bounds__(C::NT, C::WPE) void k_gemm_stream_gather(GemmPlan P) {
+  gemm_stream<C, false, DWB, true>(P);
 }
 
 // ------------------------------------------------------------------ fp32
@@ -797,6 +914,17 @@ static hipError_t launch_stream(const GemmPlan& P, int ntiles_max, hipStream_t s
   if (ntiles_max <= 0) return hipSuccess;
   const int64_t want = ((int64_t)ntiles_max + 7) & ~7ll;
   if constexpr (!DX) {
+    if (P.a.xrow) {
+      // the gathering dW kernels (their residency is that of the plain ones)
+      const int G = per_tile ? (int)want
+                             : (int)std::min<int64_t>(
+                                   want, std::max(8, stream_grid_cap<C, false>() & ~7));
+      if (P.a.dw_bf16)
+        LRM_LAUNCH(G, C::NT, 0, s, k_gemm_stream_gather<C, true>)(P);
+      else
+        LRM_LAUNCH(G, C::NT, 0, s, k_gemm_stream_gather<C, false>)(P);
+      return hipGetLastError();
+    }
     if (P.a.dw_bf16) {
       const int G = per_tile ? (int)want
                              : (int)std::min<int64_t>(
@@ -859,7 +987,11 @@ int gemm_dx_tile_rows(const GemmArgs& a) {
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s) {
   if (!a.offsets || (a.dXp && (!a.W || !a.mt_off || !a.Gp)) || (a.dW && !a.Gp) ||
-      (a.dW && a.max_rows > 0 && !a.Xp) || (a.Gp2 && (!a.W2 || a.d_out2 != a.d_out)))
+      (a.dW && a.max_rows > 0 && !a.Xp && !a.xrow) ||
+      (a.Gp2 && (!a.W2 || a.d_out2 != a.d_out)))
+    return hipErrorInvalidValue;
+  if (a.xrow && (!a.bf16 || !a.xsrc || !a.xw || a.xsrc_rows * a.ldxs * 2 >= (1ll << 31) ||
+                 a.ldxs < a.d_in))
     return hipErrorInvalidValue;
   if (a.bf16) {
     // 32-bit store offsets inside a tile (the public entry points check this)

@@ -131,6 +131,10 @@ struct CompactArgs {
   const void* G; int64_t ldg; int gcols; int g_pair; int g_by_id; void* Gp;
 };
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+// The row map of the gathering GEMM loader instead of a packed copy: for
+// packed row j < min(offsets[E], max_rows), p = kept[j]:
+//   xrow[j] = x_pair ? p : token[p];  xw[j] = weight[p]
+hipError_t launch_row_map(const CompactArgs& a, int32_t* xrow, float* xw, hipStream_t s);
 
 // --------------------------------------------------------- grouped GEMM
 // For each expert e with packed rows [offsets[e], offsets[e+1]):
@@ -149,6 +153,12 @@ struct GemmArgs {
   int mt_ready;     // mt_off already holds the prefix for gemm_dx_tile_rows(*this)
   int dw_bf16;      // dW is stored as bf16 (round to nearest even), bf16 kernels only
   hipEvent_t mid_event;  // recorded after the dW launch, before the dX launch (or null)
+  // dW with the B operand gathered by its loader instead of read from Xp
+  // (bf16 only; xrow != nullptr): packed row m of B is
+  // bf16(xw[m] * xsrc[xrow[m]]), the value compaction would have written;
+  // xsrc has xsrc_rows rows of leading dimension ldxs, under 2 GiB.
+  const void* xsrc; int64_t ldxs; int64_t xsrc_rows;
+  const int32_t* xrow; const float* xw;
 };
 int gemm_tile_choice(const GemmArgs& a);
 // Rows of a dX tile of the bf16 kernels (the prefix mt_off is built for it).

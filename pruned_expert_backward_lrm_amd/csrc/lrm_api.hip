@@ -537,8 +537,19 @@ struct LinearPlan {
   int32_t* mt_off;
   void* Gp;
   void* Xp;
+  int32_t* xrow;  // gathering loaders: source row and weight of each packed row
+  float* xw;
   float* dXp;
 };
+
+// LRM_GATHER_LOADS: the weight-gradient GEMM gathers its w*x operand from X
+// (bf16, X under 2 GiB for the loader's 32-bit offsets) instead of reading a
+// packed copy.
+bool gather_loads(const lrm_problem* pb) {
+  if (!(pb->flags & LRM_GATHER_LOADS) || pb->dtype != LRM_BF16) return false;
+  const int64_t rows = pb->X.rows == LRM_ROWS_PAIR ? pb->pairs.N : pb->pairs.T;
+  return rows * pb->X.ld * 2 < (1ll << 31);
+}
 
 LinearPlan carve_linear(Carve& c, const lrm_problem* pb, const lrm_outputs* out, int64_t Mcap) {
   const lrm_pairs& p = pb->pairs;
@@ -554,7 +565,12 @@ LinearPlan carve_linear(Carve& c, const lrm_problem* pb, const lrm_outputs* out,
   L.tok_off = c.take<int32_t>((int64_t)p.T + 1);
   L.mt_off = c.take<int32_t>(p.E + 1);
   L.Gp = c.take<char>(Mcap * pb->d_out * es);
-  L.Xp = c.take<char>(Mcap * pb->d_in * es);
+  if (gather_loads(pb)) {
+    L.xrow = c.take<int32_t>(Mcap);
+    L.xw = c.take<float>(Mcap);
+  } else {
+    L.Xp = c.take<char>(Mcap * pb->d_in * es);
+  }
   L.dXp = c.take<float>(Mcap * pb->d_in);
   if (out) {
     if (out->score) L.score = out->score;
@@ -591,6 +607,10 @@ struct GluPlan {
   float* dXp;    // pass-through: [Md][H]
   void* GAp; void* Xg; float* dXg;  // separate: gate [Mg]
   void* GBp; void* Xu; float* dXu;  // separate: up [Mu]
+  // gathering loaders: row maps of the x rows (pass-through: [Md]; separate:
+  // gate [Mg], up [Mu])
+  int32_t* xrow_g; float* xw_g;
+  int32_t* xrow_u; float* xw_u;
 };
 
 GluPlan carve_glu(Carve& c, const lrm_problem* pb, const lrm_outputs* out, int64_t Md,
@@ -624,16 +644,29 @@ GluPlan carve_glu(Carve& c, const lrm_problem* pb, const lrm_outputs* out, int64
   L.pos_u = c.take<int32_t>(Md);
   L.off_u = c.take<int32_t>(p.E + 1);
   L.kept_u = c.take<int32_t>(Md);
+  const bool gl = gather_loads(pb);
   if (pass_through) {
-    L.Xgu = c.take<char>(Md * H * es);
+    if (gl) {
+      L.xrow_g = L.xrow_u = c.take<int32_t>(Md);
+      L.xw_g = L.xw_u = c.take<float>(Md);
+    } else {
+      L.Xgu = c.take<char>(Md * H * es);
+    }
     L.dXp = c.take<float>(Md * H);
   } else {
     L.GAp = c.take<char>(Mg * I * es);
-    L.Xg = c.take<char>(Mg * H * es);
     L.dXg = c.take<float>(Mg * H);
     L.GBp = c.take<char>(Mu * I * es);
-    L.Xu = c.take<char>(Mu * H * es);
     L.dXu = c.take<float>(Mu * H);
+    if (gl) {
+      L.xrow_g = c.take<int32_t>(Mg);
+      L.xw_g = c.take<float>(Mg);
+      L.xrow_u = c.take<int32_t>(Mu);
+      L.xw_u = c.take<float>(Mu);
+    } else {
+      L.Xg = c.take<char>(Mg * H * es);
+      L.Xu = c.take<char>(Mu * H * es);
+    }
   }
   if (out) {
     if (out->score) L.score = out->score;
@@ -684,7 +717,8 @@ GluSizes glu_sizes(const lrm_problem* pb) {
 lrm_status check_problem(const lrm_problem* pb, const lrm_outputs* out) {
   if (!pb) return LRM_ERR_NULL;
   LRM_TRY(check_pairs(&pb->pairs));
-  if (pb->flags & ~(LRM_KEEP_ALL | LRM_DW_BF16 | LRM_QUOTA_ON_DEVICE | LRM_DEBUG_CHECKS))
+  if (pb->flags & ~(LRM_KEEP_ALL | LRM_DW_BF16 | LRM_QUOTA_ON_DEVICE | LRM_DEBUG_CHECKS |
+                    LRM_GATHER_LOADS))
     return LRM_ERR_UNSUPPORTED;
   if (pb->dtype != LRM_F32 && pb->dtype != LRM_BF16) return LRM_ERR_DTYPE;
   if ((pb->flags & LRM_DW_BF16) && pb->dtype != LRM_BF16) return LRM_ERR_UNSUPPORTED;
@@ -803,6 +837,10 @@ lrm_status run_linear(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   ca.x_pair = pb->X.rows == LRM_ROWS_PAIR; ca.Xp = L.Xp;
   ca.G = pb->G.ptr; ca.ldg = pb->G.ld; ca.gcols = pb->d_out;
   ca.g_pair = pb->G.rows == LRM_ROWS_PAIR; ca.Gp = L.Gp;
+  if (L.xrow) {  // the dW loader gathers w x itself: pack g, map the x rows
+    ca.Xp = nullptr;
+    LRM_TRY_HIP(launch_row_map(ca, L.xrow, L.xw, s));
+  }
   LRM_TRY_HIP(launch_compact(ca, s));
   LRM_TRY_HIP(mark(3));
   // 4. grouped GEMM: dW_e = Gp_e^T Xp_e, dXp_e = Gp_e W_e
@@ -810,6 +848,10 @@ lrm_status run_linear(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   g.offsets = L.offsets; g.Gp = L.Gp; g.Xp = L.Xp; g.W = pb->W; g.w_stride = pb->w_stride;
   g.dW = out->dW; g.dXp = L.dXp; g.mt_off = L.mt_off; g.mt_ready = 1;
   g.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
+  if (L.xrow) {
+    g.xrow = L.xrow; g.xw = L.xw; g.xsrc = pb->X.ptr; g.ldxs = pb->X.ld;
+    g.xsrc_rows = pb->X.rows == LRM_ROWS_PAIR ? p->N : p->T;
+  }
   g.mid_event = mark.at(4);
   LRM_TRY_HIP(launch_grouped_gemm(g, s));
   LRM_TRY_HIP(mark(5));
@@ -924,7 +966,10 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
     cx.T = p->T; cx.bf16 = bf16; cx.max_rows = (int)z.Md; cx.E = E;
     cx.offsets = L.offsets; cx.kept = L.kept; cx.token = p->token; cx.weight = p->weight;
     cx.X = pb->X.ptr; cx.ldx = pb->X.ld; cx.xcols = H; cx.x_pair = x_pair; cx.Xp = L.Xgu;
-    LRM_TRY_HIP(launch_compact(cx, s));
+    if (L.xrow_g)  // the gate/up dW loaders gather w x: map the rows only
+      LRM_TRY_HIP(launch_row_map(cx, L.xrow_g, L.xw_g, s));
+    else
+      LRM_TRY_HIP(launch_compact(cx, s));
     LRM_TRY_HIP(mark(8));
     GemmArgs gg{};
     gg.E = E; gg.bf16 = bf16; gg.max_rows = (int)z.Md; gg.d_in = H; gg.d_out = I;
@@ -933,6 +978,11 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
     gg.Gp2 = L.GB; gg.W2 = pb->W_up; gg.w2_stride = (int64_t)I * H; gg.d_out2 = I;
     gg.dW = out->dW_gate; gg.dXp = L.dXp; gg.mt_off = L.mt_off;
     gg.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
+    const int64_t xsrc_rows = x_pair ? p->N : p->T;
+    if (L.xrow_g) {
+      gg.xrow = L.xrow_g; gg.xw = L.xw_g; gg.xsrc = pb->X.ptr; gg.ldxs = pb->X.ld;
+      gg.xsrc_rows = xsrc_rows;
+    }
     gg.mid_event = mark.at(9);
     LRM_TRY_HIP(launch_grouped_gemm(gg, s));
     LRM_TRY_HIP(mark(10));
@@ -941,6 +991,10 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
     gu.offsets = L.offsets; gu.Gp = L.GB; gu.Xp = L.Xgu;
     gu.dW = out->dW_up; gu.dXp = nullptr; gu.mt_off = L.mt_off;
     gu.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
+    if (L.xrow_u) {
+      gu.xrow = L.xrow_u; gu.xw = L.xw_u; gu.xsrc = pb->X.ptr; gu.ldxs = pb->X.ld;
+      gu.xsrc_rows = xsrc_rows;
+    }
     LRM_TRY_HIP(launch_grouped_gemm(gu, s));
     LRM_TRY_HIP(mark(11));
     LRM_TRY_HIP(mark(12));
@@ -956,6 +1010,8 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
     float* dWv[2] = {out->dW_gate, out->dW_up};
     const int64_t cap[2] = {z.Mg, z.Mu};
     int32_t* posv[2] = {L.pos_g, L.pos_u};
+    int32_t* xrowv[2] = {L.xrow_g, L.xrow_u};
+    float* xwv[2] = {L.xw_g, L.xw_u};
     for (int k = 0; k < 2; ++k) {
       CompactArgs cg{};
       cg.T = p->T; cg.bf16 = bf16; cg.max_rows = (int)cap[k]; cg.E = E;
@@ -963,6 +1019,10 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
       cg.token = p->token; cg.weight = p->weight;
       cg.X = pb->X.ptr; cg.ldx = pb->X.ld; cg.xcols = H; cg.x_pair = x_pair; cg.Xp = Xpv[k];
       cg.G = GAsrc[k]; cg.ldg = I; cg.gcols = I; cg.g_by_id = 1; cg.Gp = Gpv[k];
+      if (xrowv[k]) {  // the dW loader gathers w x: map the rows, pack g only
+        LRM_TRY_HIP(launch_row_map(cg, xrowv[k], xwv[k], s));
+        cg.Xp = nullptr;
+      }
       LRM_TRY_HIP(launch_compact(cg, s));
     }
     LRM_TRY_HIP(mark(8));
@@ -973,6 +1033,10 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
       gk.W = Wv[k]; gk.w_stride = (int64_t)I * H;
       gk.dW = dWv[k]; gk.dXp = dXv[k]; gk.mt_off = L.mt_off;
       gk.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
+      if (xrowv[k]) {
+        gk.xrow = xrowv[k]; gk.xw = xwv[k]; gk.xsrc = pb->X.ptr; gk.ldxs = pb->X.ld;
+        gk.xsrc_rows = x_pair ? p->N : p->T;
+      }
       gk.mid_event = mark.at(9 + 2 * k);
       LRM_TRY_HIP(launch_grouped_gemm(gk, s));
       LRM_TRY_HIP(mark(10 + 2 * k));

@@ -34,6 +34,7 @@ LRM_KEEP_ALL = 1
 LRM_DW_BF16 = 2
 LRM_QUOTA_ON_DEVICE = 4
 LRM_DEBUG_CHECKS = 8
+LRM_GATHER_LOADS = 16
 ROWS = {"token": LRM_ROWS_TOKEN, "pair": LRM_ROWS_PAIR}
 
 

@@ -278,3 +278,16 @@ def test_emu_selection_past_packed_capacity(driver, tmp_path, kind):
     if kind == "swiglu":
         for k in ("offsets_gate", "offsets_up"):
             assert out[k].numpy()[-1] <= cap
+
+
+def test_emu_gather_loads(driver, tmp_path):
+    """LRM_GATHER_LOADS (16) under AddressSanitizer: the dW loader that
+    gathers and scales the x rows itself stays in bounds (a ragged k tail,
+    experts that keep nothing) and gives the outputs of the packed path bit
+    for bit."""
+    p = synth.make_linear(400, 4, 2, 72, 264, dtype="bf16", x_rows="pair", g_rows="token",
+                          seed=3, zipf=1.6, quota=lambda c: np.where(np.arange(c.size) == 3, 0, c))
+    ref = run_emu(driver, tmp_path, p, env_extra={"LRM_GEMM_TILE": "L"})
+    got = run_emu(driver, tmp_path, p, flags=16, env_extra={"LRM_GEMM_TILE": "L"})
+    for k in ("dW", "dX", "score", "pos", "offsets"):
+        assert torch.equal(got[k], ref[k]), k

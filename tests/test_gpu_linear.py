@@ -520,3 +520,32 @@ def test_capture_refused_for_copied_host_quotas(L):
     for got in _graph_replays(L, pbd, outd, wsd):
         for k in outd:
             assert torch.equal(got[k], eager[k]), k
+
+
+@pytest.mark.parametrize("x_rows,g_rows", [("token", "pair"), ("pair", "token")])
+@pytest.mark.parametrize("tile", ["L", "X"])
+def test_fused_linear_gather_loads_bit_exact(L, x_rows, g_rows, tile, monkeypatch):
+    """LRM_GATHER_LOADS: the dW GEMM gathers w x from X in its loader instead
+    of reading the packed copy; every output must equal the call without the
+    flag bit for bit (ragged shapes, experts that keep 0..all rows), with
+    fp32 and bf16 weight gradients."""
+    monkeypatch.setenv("LRM_GEMM_TILE", tile)
+    say("gather loads, linear", x_rows, g_rows, tile)
+    p = synth.make_linear(700, 10, 4, 200, 136, dtype="bf16", x_rows=x_rows, g_rows=g_rows,
+                          seed=19, zipf=1.4, quota=lambda c: (c * 5) // 8 + (c % 3 == 0))
+    for extra in (0, L.LRM_DW_BF16):
+        ref = run_linear(L, p, DEV, flags=extra)
+        got = run_linear(L, p, DEV, flags=extra | L.LRM_GATHER_LOADS)
+        for k in ("dW", "dX", "score", "pos", "offsets"):
+            assert torch.equal(got[k].view(torch.int16) if got[k].dtype == torch.bfloat16
+                               else got[k], ref[k].view(torch.int16)
+                               if ref[k].dtype == torch.bfloat16 else ref[k]), (k, extra)
+    judge_linear(p, got)
+
+
+def test_fused_linear_config2_gather_loads(L):
+    p = synth.make_config(2, device=DEV)
+    ref = run_linear(L, p, DEV)
+    got = run_linear(L, p, DEV, flags=L.LRM_GATHER_LOADS)
+    for k in ("dW", "dX", "pos", "offsets"):
+        assert torch.equal(got[k], ref[k]), k

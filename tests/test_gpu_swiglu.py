@@ -111,6 +111,24 @@ def test_fused_swiglu_h_sumsq_table(L, variant):
     say("  ", s)
 
 
+@pytest.mark.parametrize("variant", ["same", "second"])
+@pytest.mark.parametrize("tile", ["L", "X"])
+def test_fused_swiglu_gather_loads_bit_exact(L, variant, tile, monkeypatch):
+    """LRM_GATHER_LOADS: the gate and up dW GEMMs gather w x from X in their
+    loaders (one shared row map, or one per projection after a second
+    selection); every output equals the call without the flag bit for bit."""
+    monkeypatch.setenv("LRM_GEMM_TILE", tile)
+    say("gather loads, swiglu", variant, tile)
+    p = synth.make_swiglu(700, 6, 2, 200, 136, dtype="bf16", seed=18, zipf=1.2,
+                          quotas=QUOTAS[variant], g_std=1e-2)
+    ref = run_swiglu(L, p, DEV)
+    got = run_swiglu(L, p, DEV, flags=L.LRM_GATHER_LOADS)
+    for k in ("dW_gate", "dW_up", "dW_down", "dX", "score", "pos", "score_gate", "pos_gate",
+              "pos_up", "dH"):
+        assert torch.equal(got[k], ref[k]), k
+    judge_swiglu(p, got)
+
+
 def test_fused_swiglu_deterministic(L):
     p = synth.make_swiglu(500, 8, 2, 256, 128, dtype="bf16", seed=8, zipf=1.1,
                           quotas=QUOTAS["second"])
