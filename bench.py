@@ -101,6 +101,11 @@ def parse():
                          "this bench (same --config/--steps/--warmup): every grouped-GEMM "
                          "launch of the pruned calls on its own, and the kernel statistics "
                          "(no GPU needed)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="print a markdown table of rocprofv3 --pmc passes (GEMM_COUNTER_PASSES, "
+                         "one folder each) over `bench.py --no-cpu --no-full` with the same "
+                         "--config: stall, LDS, L1/L2 latency and TLB ratios per grouped-GEMM "
+                         "launch (no GPU needed)")
     ap.add_argument("--record-counters", nargs="+", metavar="DIR",
                     help="write profiles/gemm_counters.json from the output folders of a "
                          "rocprofv3 --pmc FETCH_SIZE pass, a --pmc WRITE_SIZE pass and "
@@ -201,6 +206,98 @@ def gemm_launch_work(kind, E, b, wb, Md, Mg=None, Mu=None, d_in=0, d_out=0, H=0,
     return w
 
 
+def is_gemm_kernel(name):
+    """A grouped-GEMM kernel of the library (register path, LDS-DMA or fp32)."""
+    return any(k in name for k in ("k_gemm_stream", "k_gemm_dma", "k_grouped_gemm"))
+
+
+# Counter passes for --summarize-counters (each within one pass's limits)
+GEMM_COUNTER_PASSES = [
+    "SQ_WAVE_CYCLES SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_ACTIVE_INST_LDS SQ_LDS_BANK_CONFLICT "
+    "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE",
+    "TCP_TCC_READ_REQ_sum TCP_TCC_READ_REQ_LATENCY_sum TCP_PENDING_STALL_CYCLES_sum "
+    "TCP_UTCL1_STALL_INFLIGHT_MAX_sum TCC_HIT_sum TCC_MISS_sum GRBM_GUI_ACTIVE",
+    "TCP_UTCL1_TRANSLATION_MISS_sum TCP_UTCL1_TRANSLATION_HIT_sum TCC_EA0_RDREQ_LEVEL_sum "
+    "TCC_EA0_RDREQ_sum GRBM_GUI_ACTIVE",
+]
+
+
+def summarize_counters(dirs, cfg, variant=None):
+    """Markdown table of the GEMM_COUNTER_PASSES over `bench.py --no-cpu
+    --no-full` (any order of folders): per grouped-GEMM launch of the pruned
+    call (dispatches in launch order, as in record_counters), ratios of the
+    per-dispatch means.  Per-CU fractions divide by the active cycles of one
+    XCD (GRBM_GUI_ACTIVE, which the csv sums over the 8 XCDs when it reads
+    more than 8 cycles per ns of dispatch) times the 256 CUs."""
+    import csv
+    import glob
+
+    from pruned_expert_backward_lrm_amd import synth
+    workload, work, pt = workload_of(cfg, variant)
+    roles = gemm_roles(synth.CONFIGS[cfg]["kind"], pt)
+    mean = {role: {} for role in roles}
+    names = {}
+    for d in dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        rows = [r for f in files for r in csv.DictReader(open(f))
+                if is_gemm_kernel(r["Kernel_Name"])]
+        by_counter = {}
+        for r in rows:
+            by_counter.setdefault(r["Counter_Name"], []).append(r)
+        for counter, rs in by_counter.items():
+            rs.sort(key=lambda r: int(r["Dispatch_Id"]))
+            if len(rs) % len(roles):
+                raise SystemExit(f"{d}: {len(rs)} dispatches of {counter}, not whole calls")
+            for i, role in enumerate(roles):
+                vals = [float(r["Counter_Value"]) for r in rs[i::len(roles)]]
+                ns = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rs[i::len(roles)]]
+                key = counter if counter != "GRBM_GUI_ACTIVE" else f"GRBM_GUI_ACTIVE@{d}"
+                mean[role][key] = float(np.mean(vals))
+                mean[role].setdefault("ns", float(np.mean(ns)))
+                names[role] = rs[i]["Kernel_Name"].split("(")[0].replace("lrm::", "").replace(
+                    "void ", "")
+
+    def cycles(m):
+        g = [v for k, v in m.items() if k.startswith("GRBM_GUI_ACTIVE@")]
+        if not g:
+            return None
+        c = float(np.mean(g))
+        return c / 8 if c / m["ns"] > 8 else c
+
+    def ratio(m, a, b, scale=100.0):
+        return f"{scale * m[a] / m[b]:.1f}" if a in m and b in m and m[b] else "–"
+
+    out = [f"Workload: {workload}.  Per grouped-GEMM launch of the pruned call, means "
+           "over its dispatches:", "",
+           "| launch | kernel | wait (any) % of wave cycles | LDS wait % | LDS issue % | "
+           "LDS bank conflicts | MFMA busy % | L1 stalled on L2 % of CU cycles | "
+           "L1 in-flight counter saturated % | L1→L2 reads | mean L1→L2 read latency "
+           "(cycles) | L2 hit % | mean L2→memory read latency (cycles) | TLB misses / hits |",
+           "|" + "---|" * 14]
+    for role in roles:
+        m = mean[role]
+        cyc = cycles(m)
+        cu = (lambda k: f"{100 * m[k] / (cyc * 256):.1f}" if k in m and cyc else "–")
+        mfma = f"{100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * 1024):.1f}" \
+            if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in m else "–"
+        hit = (f"{100 * m['TCC_HIT_sum'] / (m['TCC_HIT_sum'] + m['TCC_MISS_sum']):.1f}"
+               if "TCC_HIT_sum" in m and "TCC_MISS_sum" in m else "–")
+        tlb = (f"{m['TCP_UTCL1_TRANSLATION_MISS_sum']:.0f} / "
+               f"{m['TCP_UTCL1_TRANSLATION_HIT_sum']:.3g}"
+               if "TCP_UTCL1_TRANSLATION_MISS_sum" in m else "–")
+        reqs = f"{m['TCP_TCC_READ_REQ_sum']:.3g}" if "TCP_TCC_READ_REQ_sum" in m else "–"
+        out.append(
+            f"| {role} | `{names.get(role, '?')}` | "
+            f"{ratio(m, 'SQ_WAIT_INST_ANY', 'SQ_WAVE_CYCLES')} | "
+            f"{ratio(m, 'SQ_WAIT_INST_LDS', 'SQ_WAVE_CYCLES')} | "
+            f"{ratio(m, 'SQ_ACTIVE_INST_LDS', 'SQ_WAVE_CYCLES')} | "
+            f"{m.get('SQ_LDS_BANK_CONFLICT', float('nan')):.0f} | {mfma} | "
+            f"{cu('TCP_PENDING_STALL_CYCLES_sum')} | {cu('TCP_UTCL1_STALL_INFLIGHT_MAX_sum')} | "
+            f"{reqs} | {ratio(m, 'TCP_TCC_READ_REQ_LATENCY_sum', 'TCP_TCC_READ_REQ_sum', 1.0)} | "
+            f"{hit} | {ratio(m, 'TCC_EA0_RDREQ_LEVEL_sum', 'TCC_EA0_RDREQ_sum', 1.0)} | {tlb} |")
+    print("\n".join(out))
+
+
 def record_counters(dirs, cfg, variant=None):
     """profiles/gemm_counters.json from counter passes: per grouped-GEMM launch
     of the call, the average FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
@@ -227,8 +324,7 @@ def record_counters(dirs, cfg, variant=None):
             if len(copies) != 3:
                 raise SystemExit(f"{d}: no --copy-probe copies found for {counter}")
             scale[counter] = float(np.mean(copies)) / COPY_KIB
-        gemm = [row for row in rows if "k_gemm_stream" in row["Kernel_Name"]
-                or "k_grouped_gemm" in row["Kernel_Name"]]
+        gemm = [row for row in rows if is_gemm_kernel(row["Kernel_Name"])]
         if not gemm or len(gemm) % len(roles):
             raise SystemExit(f"{d}: {len(gemm)} grouped-GEMM dispatches, not a whole number "
                              f"of calls of {len(roles)} launches")
@@ -303,8 +399,7 @@ def summarize_trace(d, cfg, steps, warmup, variant=None):
         raise SystemExit(f"{d}: no kernel trace")
     rows = [r for f in trace for r in csv.DictReader(open(f))]
     rows.sort(key=lambda r: int(r["Dispatch_Id"]))
-    gemm = [r for r in rows if "k_gemm_stream" in r["Kernel_Name"]
-            or "k_grouped_gemm" in r["Kernel_Name"]]
+    gemm = [r for r in rows if is_gemm_kernel(r["Kernel_Name"])]
     ncalls = warmup + 2 * steps
     pruned = gemm[:ncalls * len(roles)]
     if len(pruned) != ncalls * len(roles):
@@ -689,6 +784,9 @@ def main():
     a = parse()
     if a.summarize_trace:
         summarize_trace(a.summarize_trace, a.config, a.steps, a.warmup, a.variant)
+        return
+    if a.summarize_counters:
+        summarize_counters(a.summarize_counters, a.config, a.variant)
         return
     if a.record_counters:
         if not 2 <= len(a.record_counters) <= 3:

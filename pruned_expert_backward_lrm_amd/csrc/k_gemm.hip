@@ -19,7 +19,9 @@
 // store.  Two LDS stages; global loads run up to two k-tiles ahead of the
 // MFMAs.  The MFMA is issued with the N-side fragment first, so each lane's
 // four accumulators are four consecutive output columns (one 16-byte store,
-// or 8 bytes when dW is stored as bf16).
+// or 8 bytes when dW is stored as bf16).  An opt-in variant of the 256x256
+// kernels (LRM_GEMM_DMA) loads operand tiles straight into LDS and reads the
+// k-strided ones with gfx950's transposing LDS reads instead.
 //
 // fp32: plain LDS-tiled fp32 FMA (64x64 tile), one launch over the combined
 // dW and dX tile list.
@@ -422,7 +424,7 @@ __device__ __forceinline__ Job make_job(const GemmPlan& P, int t) {
     j.s0.a_rows_valid = 0; j.s0.a_n0 = i0; j.s0.b_n0 = j0;
     j.s0.K = Me;
     j.s1 = j.s0;
-    j.nk0 = j.nk = (Me + BK - 1) / BK;
+    j.nk0 = j.nk = (Me + C::BK - 1) / C::BK;
     j.C = a.dW + (int64_t)e * a.d_out * a.d_in + (int64_t)i0 * a.d_in + j0;
     j.rows = min(C::BM, a.d_out - i0);
     j.cols = min(C::BN, a.d_in - j0);
@@ -440,7 +442,7 @@ __device__ __forceinline__ Job make_job(const GemmPlan& P, int t) {
     j.s0.brow = nullptr;
     j.s0.bw = nullptr;
     j.s1 = j.s0;
-    j.nk0 = j.nk = (a.d_out + BK - 1) / BK;
+    j.nk0 = j.nk = (a.d_out + C::BK - 1) / C::BK;
     if (a.Gp2) {  // second segment of the same shape (host-checked: d_out2 == d_out)
       j.s1.a = (const char*)a.Gp2 + (int64_t)m0 * a.d_out * 2;
       j.s1.b = (const char*)a.W2 + (int64_t)e * a.w2_stride * 2;
@@ -742,6 +744,344 @@ __global__ __launch_bounds__(C::NT, C::WPE) void k_gemm_stream_gather(GemmPlan P
   gemm_stream<C, false, DWB, true>(P);
 }
 
+// ------------------------------------------------------------ LDS-DMA stream
+//
+// An alternative to the register path for 256x256 tiles whose operand rows
+// start on 16-byte boundaries (and, for dX, whose K is a whole number of
+// k-tiles), selected with LRM_GEMM_DMA (see dma_choice).  Operand tiles go from
+// global memory straight into LDS: buffer loads with the LDS-destination flag,
+// 16 bytes per lane, each instruction filling 1 KB of LDS (lane p at byte
+// 16p).  No staging registers, register transposes or LDS stores; the
+// registers left over go to fragments.  k-strided operands (dW's A and B,
+// dX's B) stay in LDS as they lie in memory, [k][n] with n contiguous, and
+// are read with ds_read_b64_tr_b16: within each 16-lane group, output lane j
+// element r is element j % 4 of the 8 bytes addressed by lane 4r + j / 4
+// (measured), so lanes addressing 4 k-rows x 16 columns receive one column's
+// 4 consecutive k each; two such reads make an MFMA operand fragment.  dX's A
+// (k contiguous) keeps the [m][k] layout of the register path.
+//
+// STAGES LDS stages of BK k each; loads run STAGES - 1 k-tiles ahead of the
+// MFMAs.  A k-tile is consumed after a wait for the wave's own loads of it
+// (the vector memory counter retires loads and stores in issue order, so the
+// wait names how many younger instructions may still be outstanding) and a
+// barrier; the barrier also frees the stage consumed one k-tile earlier, which
+// receives the next loads.
+template <int BK_, int STAGES_>
+struct DmaCfg {
+  static constexpr int BM = 256, BN = 256, BK = BK_, STAGES = STAGES_;
+  static constexpr int MINB = 1, WGM = 4, WGN = 2, NW = 8, NT = 512, WPE = 2;
+  static constexpr int TM = 64, TN = 128, FM = 4, FN = 8, FCH = 4;
+  static constexpr int NQ = BK / 16;  // LDS-DMA instructions per operand, wave and k-tile
+  static constexpr int NSTORE = FM * FN;  // buffer stores per wave and output tile
+  static_assert(BK == 32 || BK == 64, "k-tile");
+  static_assert(2 * NQ * (STAGES - 1) + NSTORE <= 63, "vector memory counter range");
+};
+
+#ifdef LRM_CPU_EMU
+typedef void* lds_vptr;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef s16x4* lds_s16x4;
+#else
+typedef __attribute__((address_space(3))) void* lds_vptr;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
+#endif
+
+// 16 bytes per lane from r at byte voff into LDS at lds + 16 * lane (lds is
+// wave-uniform); past the bound the lane writes zeros (measured).  Written
+// as inline asm so that the compiler, which does not track these loads, does
+// not wait for every one in flight before each LDS read: the kernel orders
+// them itself (dma_barrier).  The LDS address goes in M0 as an input operand.
+#ifdef LRM_CPU_EMU
+typedef rsrc_t dma_rsrc;
+__device__ __forceinline__ dma_rsrc make_dma_rsrc(const char* base, int64_t nbytes) {
+  return make_rsrc(base, nbytes);
+}
+__device__ __forceinline__ void dma16(dma_rsrc r, uint16_t* lds, int voff) {
+  const u32x4 v = bload(r, voff);
+  std::memcpy(reinterpret_cast<char*>(lds) + 16 * lane_id(), &v, 16);
+}
+#else
+typedef u32x4 dma_rsrc;  // buffer resource words: base, bound, raw access
+__device__ __forceinline__ dma_rsrc make_dma_rsrc(const char* base, int64_t nbytes) {
+  const int n = nbytes <= 0 ? 0 : (nbytes > 0x7ffffff0ll ? 0x7ffffff0 : (int)nbytes);
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  return dma_rsrc{(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, (uint32_t)n, (uint32_t)kRsrcWord3};
+}
+__device__ __forceinline__ void dma16(dma_rsrc r, uint16_t* lds, int voff) {
+  const uint32_t la = (uint32_t)(uintptr_t)(lds_vptr)lds;
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r), "{m0}"(la)
+               : "memory");
+}
+#endif
+
+// [k][n] LDS tile of 256 columns (512-byte rows) in 32-byte segments; segment
+// c of row k sits at c ^ trh(k).  A transposed read by 16 lanes covers one
+// segment of 4 consecutive rows; two 16-lane groups read rows 8 (or 16) apart.
+// trh gives those 8 row-segments distinct positions modulo 8, i.e. distinct
+// 32-byte bank slots of the 256-byte bank cycle.
+__device__ __forceinline__ int trh(int k) {
+  return (k & 3) | (((k >> 3) ^ (k >> 4)) & 1) << 2;
+}
+// [m][k] rows of 32 k (64 bytes): granule G of row r at G ^ swz32(r).  With
+// the four 16-lane passes of a ds_read_b128 (lanes 0-3, 12-15, 20-23, 24-27;
+// 4-7, 8-11, 16-19, 28-31; the same +32) every pass hits 16 distinct granule
+// slots of the bank cycle.
+__device__ __forceinline__ int swz32(int r) { return (4 - ((r >> 2) & 3)) & 3; }
+
+__device__ __forceinline__ s16x4 ldtr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)const_cast<uint16_t*>(p));
+}
+// fragment of 16 columns, k rows kr..kr+3 and kr+4..kr+7 (p at row kr)
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* p) {
+  const s16x4 lo = ldtr(p), hi = ldtr(p + 4 * 256);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Per-lane byte offsets of a wave's LDS-DMA granules (fixed for the launch:
+// the operand's leading dimension does not change) and the k-tile loads.
+template <class C, bool DX>
+struct DmaStage {
+  static constexpr int NQ = C::NQ;
+  int offa[NQ], offb[NQ];
+  int w;
+  int64_t lda, ldb;
+  // granule p of 1 KB block b of a [k][256] tile (rows 2b, 2b + 1)
+  __device__ __forceinline__ static int kstr_off(int b, int p, int64_t ld) {
+    const int k = 2 * b + (p >> 5), s = p & 31;
+    const int c = (s >> 1) ^ trh(k);
+    return (int)(k * ld * 2) + c * 32 + (s & 1) * 16;
+  }
+  // granule p of 1 KB block b of a [256][BK] tile
+  __device__ __forceinline__ static int kcont_off(int b, int p, int64_t ld) {
+    if constexpr (C::BK == 64) {
+      const int r = 8 * b + (p >> 3);
+      return (int)(r * ld * 2) + (((p & 7) ^ lds_swz(r)) << 4);
+    } else {
+      const int r = 16 * b + (p >> 2);
+      return (int)(r * ld * 2) + (((p & 3) ^ swz32(r)) << 4);
+    }
+  }
+  __device__ __forceinline__ void init(int64_t la, int64_t lb) {
+    lda = la;
+    ldb = lb;
+    w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int p = lane_id();
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int b = w * NQ + q;
+      offa[q] = DX ? kcont_off(b, p, la) : kstr_off(b, p, la);
+      offb[q] = kstr_off(b, p, lb);
+    }
+  }
+  // k-tile [k0, k0 + BK) of segment s into the stage (As, Bs).  Bounds as in
+  // the register path: rows past the expert's block (dX's A) or past K (the
+  // k-strided panels) read zeros; columns past the operand's width read the
+  // next row, which only reaches output columns that are never stored.
+  __device__ __forceinline__ void load(const TileSrc& s, int k0, uint16_t* As, uint16_t* Bs) const {
+    const dma_rsrc ra =
+        DX ? make_dma_rsrc(s.a + (int64_t)k0 * 2, (int64_t)s.a_rows_valid * lda * 2 - k0 * 2)
+           : make_dma_rsrc(s.a + ((int64_t)k0 * lda + s.a_n0) * 2,
+                           (int64_t)(s.K - k0) * lda * 2 - (int64_t)s.a_n0 * 2);
+    const dma_rsrc rb = make_dma_rsrc(s.b + ((int64_t)k0 * ldb + s.b_n0) * 2,
+                                      (int64_t)(s.K - k0) * ldb * 2 - (int64_t)s.b_n0 * 2);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) dma16(ra, As + (w * NQ + q) * 512, offa[q]);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) dma16(rb, Bs + (w * NQ + q) * 512, offb[q]);
+  }
+};
+
+// Per-lane LDS element offsets of a wave's fragments at k = 0 of a stage.
+template <class C, bool DX>
+struct DmaFrag {
+  int tb[C::FN];   // B fragment j ([k][n])
+  int ta[C::FM];   // A fragment i ([k][m]; dX: [m][k], k 0..31)
+  int ta1[C::FM];  // dX with BK 64: A fragment i, k 32..63
+  __device__ __forceinline__ void init() {
+    const int l = lane_id(), w = threadIdx.x >> 6;
+    const int wm = w / C::WGN, wn = w % C::WGN;
+    const int g = l >> 4, i = l & 15;
+    const int kr = 8 * g + (i >> 2);  // first k row of this lane's transposed reads
+    const int t = trh(kr);            // the same for rows kr + 32 and kr + 4
+    const int base = kr * 256 + 4 * (i & 3);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) tb[j] = base + (((wn * (C::TN / 16) + j) ^ t) << 4);
+#pragma unroll
+    for (int f = 0; f < C::FM; ++f) {
+      if constexpr (DX) {
+        const int row = wm * C::TM + f * 16 + i;
+        if constexpr (C::BK == 64) {
+          ta[f] = lds_off(row, 2 * g);
+          ta1[f] = lds_off(row, 2 * (4 + g));
+        } else {
+          ta[f] = row * 32 + ((g ^ swz32(row)) << 3);
+          ta1[f] = ta[f];
+        }
+      } else {
+        ta[f] = base + (((wm * (C::TM / 16) + f) ^ t) << 4);
+        ta1[f] = ta[f];
+      }
+    }
+  }
+};
+
+// The MFMAs of k 32h..32h+31 of a stage.
+template <class C, bool DX>
+__device__ __forceinline__ void mma_dma(f32x4 (&acc)[C::FM][C::FN], const uint16_t* As,
+                                        const uint16_t* Bs, const DmaFrag<C, DX>& f, int h) {
+  bf16x8 bf[C::FN], af[C::FM];
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) bf[j] = tr_frag(Bs + h * 32 * 256 + f.tb[j]);
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+    if constexpr (DX)
+      af[i] = *reinterpret_cast<const bf16x8*>(As + (h ? f.ta1[i] : f.ta[i]));
+    else
+      af[i] = tr_frag(As + h * 32 * 256 + f.ta[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt not waited on)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+// Wait until at most n vector memory instructions of this wave are
+// outstanding, then the block barrier.  n is rounded down to a value of the
+// ladder {0, L, 2L, NSTORE, NSTORE + L, NSTORE + 2L, 60} (L = 2 NQ, the loads
+// of one k-tile): the counts that occur are the loads of up to two younger
+// k-tiles, plus one output tile's stores; anything past that waits for 60.
+// The empty asm statements keep the compiler from moving LDS accesses across.
+template <class C>
+__device__ __forceinline__ void dma_barrier(int n) {
+  constexpr int L = 2 * C::NQ, T = C::NSTORE;
+  static_assert(T + 2 * L <= 60, "ladder");
+  asm volatile("" ::: "memory");
+  if (n >= 60) wait_vm<60>();
+  else if (n >= T + 2 * L) wait_vm<T + 2 * L>();
+  else if (n >= T + L) wait_vm<T + L>();
+  else if (n >= T) wait_vm<T>();
+  else if (n >= 2 * L) wait_vm<2 * L>();
+  else if (n >= L) wait_vm<L>();
+  else wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <class C, bool DX, bool DWB>
+__device__ __forceinline__ void gemm_dma(const GemmPlan& P) {
+  constexpr int S = C::STAGES;
+  constexpr int SA = C::BM * C::BK, SS = (C::BM + C::BN) * C::BK;  // elements
+  __shared__ __attribute__((aligned(1024))) uint16_t L[S * SS];
+  const GemmArgs& a = P.a;
+  const int x = blockIdx.x & 7, nbx = gridDim.x >> 3;
+  int lo, hi;
+  if constexpr (DX) {
+    const int n = ld_table(a.mt_off, a.E) * P.ntn_x;
+    lo = (int)((int64_t)n * x / 8);
+    hi = (int)((int64_t)n * (x + 1) / 8);
+  } else {
+    dw_share(P, x, &lo, &hi);
+  }
+  int tc = lo + (blockIdx.x >> 3);
+
+  f32x4 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Tiles with no k-tiles (experts that kept no rows) are written from acc,
+  // which is zero wherever they are met (stored as constants, the zeros of
+  // the fp32 stores end up spilled as scalar registers).
+  Job jc;
+  for (; tc < hi; tc += nbx) {
+    jc = make_job<C, DX>(P, tc);
+    if (jc.nk > 0) break;
+    if (jc.rows > 0) store_tile<C, DWB>(a, acc, false, jc.C, jc.rows, jc.cols);
+  }
+  if (tc >= hi) return;
+
+  DmaStage<C, DX> st;
+  st.init(a.d_out, a.d_in);
+  DmaFrag<C, DX> fr;
+  fr.init();
+  // vm: vector memory instructions this wave has issued since the first load
+  // (every wave issues the same ones); mk[s]: vm just after the loads of the
+  // s-th oldest k-tile in flight
+  int vm = 0, mk[S];
+  int tl = tc, kl = 0, nxt = 0;
+  Job jl = jc;
+  // the next k-tile of the stream (if any) into stage nxt, its mark in mk[slot]
+  auto issue = [&](int slot) {
+    if (tl < hi) {
+      const bool first = kl < jl.nk0;
+      uint16_t* dst = L + nxt * SS;
+      st.load(pick_seg(jl.s0, jl.s1, first), (first ? kl : kl - jl.nk0) * C::BK, dst, dst + SA);
+      vm += 2 * C::NQ;
+      if (++kl == jl.nk) {
+        kl = 0;
+        for (tl += nbx; tl < hi; tl += nbx) {
+          jl = make_job<C, DX>(P, tl);
+          if (jl.nk > 0) break;
+        }
+      }
+    }
+    mk[slot] = vm;
+    nxt = nxt + 1 == S ? 0 : nxt + 1;
+  };
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) issue(s);
+  int cur = 0, kc = 0;
+  for (;;) {
+    dma_barrier<C>(vm - mk[0]);
+    issue(S - 1);
+    const uint16_t* Ac = L + cur * SS;
+#pragma unroll
+    for (int h = 0; h < C::BK / 32; ++h) mma_dma<C, DX>(acc, Ac, Ac + SA, fr, h);
+    cur = cur + 1 == S ? 0 : cur + 1;
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s) mk[s] = mk[s + 1];
+    if (++kc == jc.nk) {
+      // the finished tile, then any tiles with no k-tiles up to the next one
+      // that has some (one store site: a second one costs scalar spills)
+      bool done = false;
+      for (;;) {
+        if (jc.rows > 0) {
+          store_tile<C, DWB>(a, acc, false, jc.C, jc.rows, jc.cols);
+          vm += C::NSTORE;
+        }
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        tc += nbx;
+        if (tc >= hi) {
+          done = true;
+          break;
+        }
+        jc = make_job<C, DX>(P, tc);
+        if (jc.nk > 0) break;
+      }
+      if (done) break;
+      kc = 0;
+    }
+  }
+}
+
+template <class C, bool DX, bool DWB>
+__global__ __launch_bounds__(C::NT, C::WPE) void k_gemm_dma(GemmPlan P) {
+  gemm_dma<C, DX, DWB>(P);
+}
+
 // ------------------------------------------------------------------ fp32
 
 constexpr int FBM = 64, FBN = 64, FBK = 16;
@@ -878,11 +1218,11 @@ static hipError_t plan_tiles(const GemmArgs& a, int tmw, int tnw, int tmx, int t
   return hipSuccess;
 }
 
-// Resident blocks of one stream kernel on the current device, cached for the
+// Resident blocks of a GEMM kernel on the current device, cached for the
 // first 16 devices (concurrent callers may both compute it; they store the
 // same value).
-template <class C, bool DX, bool DWB = false>
-static int stream_grid_cap() {
+template <auto Kern, int NTH>
+static int grid_cap_of() {
   static std::atomic<int> cap[16];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
@@ -894,15 +1234,19 @@ static int stream_grid_cap() {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
     cus = 256;
-  hipError_t e;
-  if constexpr (DWB)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemm_stream_dwbf16<C>, C::NT, 0);
-  else
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemm_stream<C, DX>, C::NT, 0);
-  if (e != hipSuccess || occ <= 0) occ = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, Kern, NTH, 0) != hipSuccess || occ <= 0)
+    occ = 1;
   const int c = cus * occ;
   if (dev < 16) cap[dev].store(c, std::memory_order_relaxed);
   return c;
+}
+
+template <class C, bool DX, bool DWB = false>
+static int stream_grid_cap() {
+  if constexpr (DWB)
+    return grid_cap_of<k_gemm_stream_dwbf16<C>, C::NT>();
+  else
+    return grid_cap_of<k_gemm_stream<C, DX>, C::NT>();
 }
 
 // per_tile: one block per tile (a multiple of 8 blocks), the hardware handing
@@ -940,6 +1284,66 @@ static hipError_t launch_stream(const GemmPlan& P, int ntiles_max, hipStream_t s
   return hipGetLastError();
 }
 
+// The LDS-DMA kernels (256x256 tiles), opt-in: LRM_GEMM_DMA=2 (k-tiles of
+// 64, two stages) or 4 (k-tiles of 32, four stages).  Measured on the
+// 65536-token SwiGLU shapes they match the register path (dW, four stages)
+// or trail it by 3-15% (dX): both wait on L2 for about 43% of the wave
+// cycles, bound by the requests a CU may have in flight (its L1 stalls on
+// pending L2 data most of the time), which direct loads do not change.
+using CfgD = DmaCfg<64, 2>;
+using CfgD4 = DmaCfg<32, 4>;
+
+static int dma_choice() {
+  const char* env = getenv("LRM_GEMM_DMA");
+  if (env && env[0] == '2') return 2;
+  if (env && env[0] == '4') return 4;
+  return 0;
+}
+
+// Operand rows and bases on 16-byte boundaries; dX: K a whole number of
+// k-tiles (the k-contiguous A panel has no per-lane k bound); dW: packed B
+// rows (the gathering loaders scale rows in registers).
+template <class C>
+static bool dma_ok(const GemmArgs& a, bool dx) {
+  auto al = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  if (a.d_in % 8 || a.d_out % 8 || !al(a.Gp)) return false;
+  if (!dx) return !a.xrow && al(a.Xp);
+  if (a.d_out % C::BK || !al(a.W) || a.w_stride % 8) return false;
+  return !a.Gp2 || (al(a.Gp2) && al(a.W2) && a.w2_stride % 8 == 0);
+}
+
+template <class C, bool DX>
+static hipError_t launch_dma(const GemmPlan& P, int ntiles_max, hipStream_t s, bool per_tile) {
+  if (ntiles_max <= 0) return hipSuccess;
+  const int64_t want = ((int64_t)ntiles_max + 7) & ~7ll;
+  const bool dwb = !DX && P.a.dw_bf16;
+  const int cap = DX    ? grid_cap_of<k_gemm_dma<C, true, false>, C::NT>()
+                  : dwb ? grid_cap_of<k_gemm_dma<C, false, true>, C::NT>()
+                        : grid_cap_of<k_gemm_dma<C, false, false>, C::NT>();
+  const int G = per_tile ? (int)want : (int)std::min<int64_t>(want, std::max(8, cap & ~7));
+  if (DX)
+    LRM_LAUNCH(G, C::NT, 0, s, k_gemm_dma<C, true, false>)(P);
+  else if (dwb)
+    LRM_LAUNCH(G, C::NT, 0, s, k_gemm_dma<C, false, true>)(P);
+  else
+    LRM_LAUNCH(G, C::NT, 0, s, k_gemm_dma<C, false, false>)(P);
+  return hipGetLastError();
+}
+
+// One product's launch: the LDS-DMA kernel for 256x256 tiles when the
+// operands allow it, the register-path stream otherwise.
+template <class C, bool DX>
+static hipError_t launch_product(const GemmPlan& P, int ntiles_max, hipStream_t s,
+                                 bool per_tile) {
+  if constexpr (std::is_same<C, CfgL>::value) {
+    const int d = dma_choice();
+    if (d == 2 && dma_ok<CfgD>(P.a, DX)) return launch_dma<CfgD, DX>(P, ntiles_max, s, per_tile);
+    if (d == 4 && dma_ok<CfgD4>(P.a, DX))
+      return launch_dma<CfgD4, DX>(P, ntiles_max, s, per_tile);
+  }
+  return launch_stream<C, DX>(P, ntiles_max, s, per_tile);
+}
+
 template <class CW, class CX>
 static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
   GemmPlan P{};
@@ -955,10 +1359,10 @@ static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
   // expert the persistent stream keeps its one-k-tile tiles fed.
   const int rounds = std::max(P.nW, P.nX) / std::max(1, stream_grid_cap<CW, false>());
   const bool per_tile = gemm_tile_choice(a) == 2 && rounds <= 16;
-  err = launch_stream<CW, false>(P, P.nW, s, per_tile);
+  err = launch_product<CW, false>(P, P.nW, s, per_tile);
   if (err != hipSuccess) return err;
   if (a.mid_event && (err = hipEventRecord(a.mid_event, s)) != hipSuccess) return err;
-  return launch_stream<CX, true>(P, P.nX, s, per_tile);
+  return launch_product<CX, true>(P, P.nX, s, per_tile);
 }
 
 // Tile choice: 256x256 dW tiles; 256-row dX tiles when experts keep many rows

@@ -303,6 +303,31 @@ inline int update_dpp(int old, int src, int ctrl, int row_mask) {
 #define __builtin_amdgcn_wave_barrier() ::emu::wave_barrier()
 #define __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, x, y, z) ::emu::mfma16x16x32((a), (b), (c))
 
+namespace emu {
+// ds_read_b64_tr_b16: each lane addresses 8 bytes (four 16-bit elements);
+// within each group of 16 lanes, output lane j element r is element j % 4 of
+// the 8 bytes addressed by lane 4r + j / 4 of the group.
+template <typename V4>
+inline V4 ds_read_tr16(const V4* p) {
+  Wave& w = wave();
+  std::memcpy(w.wide[ctx.lane], p, 8);
+  w.bar->arrive_and_wait();
+  const int l = ctx.lane, g = l & ~15, j = l & 15;
+  V4 out;
+  for (int r = 0; r < 4; ++r) {
+    short v;
+    std::memcpy(&v, w.wide[g + 4 * r + (j >> 2)] + 2 * (j & 3), 2);
+    out[r] = v;
+  }
+  w.bar->arrive_and_wait();
+  return out;
+}
+}  // namespace emu
+#define __builtin_amdgcn_ds_read_tr16_b64_v4i16(p) ::emu::ds_read_tr16(p)
+// memory operations complete at once here: waits have nothing to wait for
+#define __builtin_amdgcn_s_waitcnt(imm) ((void)(imm))
+#define __builtin_amdgcn_s_barrier() ::emu::syncthreads()
+
 template <typename T, typename U>
 inline T min(T a, U b) { return a < (T)b ? a : (T)b; }
 template <typename T, typename U>

@@ -214,7 +214,7 @@ def test_quota_on_device_and_debug_flags():
     assert lib.lrm_workspace_size(C.byref(pb)) == n_all
     pb.quota = None
     assert lib.lrm_workspace_size(C.byref(pb)) == 0
-    pb.quota, pb.flags = 0x10, 16  # not a flag of the ABI
+    pb.quota, pb.flags = 0x10, 32  # not a flag of the ABI
     assert lib.lrm_workspace_size(C.byref(pb)) == 0
     # lrm_select: device quotas must be present; the workspace is still checked
     p = _pairs(E=3)

@@ -6,9 +6,10 @@ access of a kernel or of the host code aborts the run; the outputs must pass
 the same oracle checks as the GPU parity tests.  Runs without a GPU.
 
 Every lane is an OS thread and every wave collective two 64-thread barriers,
-so a case takes 30-130 s.  The default run keeps two: the tiny fp32 workload
-(every step, the fp32 GEMM) and the bf16 grouped GEMM in its 256x256 tiles;
-LRM_EMU_FULL=1 runs all of them (about 20 minutes on 8 cores).
+so a case takes 30-130 s.  The default run keeps three: the tiny fp32
+workload (every step, the fp32 GEMM), the bf16 grouped GEMM in its 256x256
+tiles, and the same tiles on the LDS-DMA kernels; LRM_EMU_FULL=1 runs all of
+them (about 25 minutes on 8 cores).
 """
 
 from __future__ import annotations
@@ -186,6 +187,25 @@ def test_emu_linear_tile_configs(driver, tmp_path, tile):
     p = synth.make_linear(400, 4, 2, 72, 264, dtype="bf16", seed=3, zipf=1.6,
                           quota=lambda c: np.where(np.arange(c.size) == 3, 0, c))
     judge_linear(p, run_emu(driver, tmp_path, p, env_extra={"LRM_GEMM_TILE": tile}))
+
+
+@pytest.mark.parametrize("dma", ["2", pytest.param("4", marks=extended)])
+def test_emu_gemm_lds_dma(driver, tmp_path, dma):
+    """The 256x256 kernels whose operand tiles go straight into LDS and whose
+    k-strided operands are read with transposing LDS reads (LRM_GEMM_DMA=2:
+    k-tiles of 64 in two stages; 4: of 32 in four), dW and dX, on a ragged
+    shape (a partial last column tile, an expert over several row tiles, one
+    that keeps nothing): judged against the oracle and, with LRM_EMU_FULL=1,
+    compared bit for bit with the register path (LRM_GEMM_DMA=0), which issues
+    the same MFMAs in the same order on the same operands."""
+    p = synth.make_linear(400, 4, 2, 200, 320, dtype="bf16", seed=3, zipf=1.6,
+                          quota=lambda c: np.where(np.arange(c.size) == 3, 0, c))
+    got = run_emu(driver, tmp_path, p, env_extra={"LRM_GEMM_TILE": "L", "LRM_GEMM_DMA": dma})
+    judge_linear(p, got)
+    if os.environ.get("LRM_EMU_FULL"):  # the bit-for-bit comparison costs a second run
+        ref = run_emu(driver, tmp_path, p, env_extra={"LRM_GEMM_TILE": "L", "LRM_GEMM_DMA": "0"})
+        for k in ("dW", "dX"):
+            assert torch.equal(ref[k], got[k]), k
 
 
 @extended

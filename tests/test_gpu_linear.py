@@ -284,6 +284,47 @@ def test_gemm_tile_configs(L, tile, monkeypatch):
         assert rel_fro(dXp[a:b].cpu().numpy(), G64[a:b] @ O.f64(W[e].cpu())) < 1e-5
 
 
+@pytest.mark.parametrize("d_out", [320, 200])
+def test_gemm_lds_dma_bit_exact(L, d_out, monkeypatch):
+    """The 256x256 kernels that load operand tiles straight into LDS and read
+    the k-strided ones with transposing LDS reads (LRM_GEMM_DMA=2: k-tiles of
+    64, two stages; 4: k-tiles of 32, four stages) give the register path's
+    results bit for bit (the same MFMAs in the same order on the same
+    operands), on empty, 1-row and tile-edge experts and a partial last column
+    tile.  With d_out = 200, dX's K is not a whole number of k-tiles and dX
+    stays on the register path."""
+    monkeypatch.setenv("LRM_GEMM_TILE", "L")
+    E, d_in = 8, 200
+    sizes = [0, 1, 63, 64, 65, 257, 700, 0]
+    W = synth.normal((E, d_out, d_in), 0.02, torch.bfloat16, DEV, "dma", 1)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M = int(offsets[-1])
+    Gp = synth.normal((M, d_out), 1.0, torch.bfloat16, DEV, "dma", 2)
+    Xp = synth.normal((M, d_in), 1.0, torch.bfloat16, DEV, "dma", 3)
+    off = torch.as_tensor(offsets, device=DEV)
+    res = {}
+    for dma in ("0", "2", "4"):
+        say("gemm lds dma", d_out, dma)
+        monkeypatch.setenv("LRM_GEMM_DMA", dma)
+        dW = torch.full((E, d_out, d_in), float("nan"), device=DEV)
+        dXp = torch.full((M, d_in), float("nan"), device=DEV)
+        L.lrm_grouped_bwd(E, off, M, Gp, Xp, W, d_in, d_out, dW, dXp)
+        torch.cuda.synchronize()
+        res[dma] = (dW.cpu(), dXp.cpu())
+    for dma in ("2", "4"):
+        assert torch.equal(res[dma][0], res["0"][0]), f"dW, LRM_GEMM_DMA={dma}"
+        assert torch.equal(res[dma][1], res["0"][1]), f"dX, LRM_GEMM_DMA={dma}"
+    dW, dXp = res["2"]
+    G64, X64 = Gp.double().cpu().numpy(), Xp.double().cpu().numpy()
+    for e in range(E):
+        a, b = offsets[e], offsets[e + 1]
+        if a == b:
+            assert not dW[e].numpy().any()
+            continue
+        assert rel_fro(dW[e].numpy(), G64[a:b].T @ X64[a:b]) < 1e-5
+        assert rel_fro(dXp[a:b].numpy(), G64[a:b] @ O.f64(W[e].cpu())) < 1e-5
+
+
 # ------------------------------------------------------------ fused call
 
 @pytest.mark.parametrize("x_rows,g_rows", [("token", "pair"), ("pair", "token")])

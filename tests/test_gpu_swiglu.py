@@ -129,6 +129,28 @@ def test_fused_swiglu_gather_loads_bit_exact(L, variant, tile, monkeypatch):
     judge_swiglu(p, got)
 
 
+@pytest.mark.parametrize("flags", [0, 2])
+def test_fused_swiglu_lds_dma_bit_exact(L, flags, monkeypatch):
+    """The LDS-DMA 256x256 kernels (LRM_GEMM_DMA=2 and 4) in the fused SwiGLU
+    call, fp32 and bf16 (LRM_DW_BF16 = 2) weight gradients, the gate/up dX
+    product over its two K segments: every output equals the register path's
+    (LRM_GEMM_DMA=0) bit for bit.  H = 320 and I = 192 leave partial column
+    tiles and let every product take the DMA kernels."""
+    monkeypatch.setenv("LRM_GEMM_TILE", "L")
+    p = synth.make_swiglu(900, 6, 2, 320, 192, dtype="bf16", seed=21, zipf=1.2,
+                          quotas=QUOTAS["second"], g_std=1e-2)
+    res = {}
+    for dma in ("0", "2", "4"):
+        say("swiglu lds dma", flags, dma)
+        monkeypatch.setenv("LRM_GEMM_DMA", dma)
+        res[dma] = run_swiglu(L, p, DEV, flags=flags)
+    for dma in ("2", "4"):
+        for k in ("dW_gate", "dW_up", "dW_down", "dX", "dH"):
+            assert torch.equal(res[dma][k], res["0"][k]), (k, dma)
+    if flags == 0:
+        judge_swiglu(p, res["2"])
+
+
 def test_fused_swiglu_deterministic(L):
     p = synth.make_swiglu(500, 8, 2, 256, 128, dtype="bf16", seed=8, zipf=1.1,
                           quotas=QUOTAS["second"])
