@@ -560,57 +560,162 @@ __device__ __forceinline__ void mma_k32(f32x4 (&acc)[C::FM][C::FN], const uint16
   }
 }
 
-// dW shares: the tiles, in order, are cut into 8 shares of equal cost, a tile
-// of expert e costing ceil(M_e / 64) + kStoreCost: its k-tiles, plus its fp32
-// output, weighted as two k-tiles (the best of 1, 2, 3, 4, 8 and count-only
-// shares measured over the Qwen3 linear, GLM-4.5 local-32 and large SwiGLU
-// shapes).  Computed by every wave alike (no barrier): per-expert costs 64
-// experts at a time, wave sums and scans, the boundary expert found with a
-// ballot.
+// dW schedule.  The dW tiles, in expert order, are cut into 8 shares of equal
+// cost, one per XCD, a tile of expert e costing ceil(M_e / 64) + kStoreCost:
+// its k-tiles, plus its fp32 output, weighted as two k-tiles (the best of 1,
+// 2, 3, 4, 8 and count-only shares measured over the Qwen3 linear, GLM-4.5
+// local-32 and large SwiGLU shapes).  Inside a share the experts' runs of
+// tiles are taken longest first (cost, then expert id), so that the long
+// tiles of skewed experts start early and the short ones fill in at the end:
+// one block per tile then is the hardware's greedy dispatch in that order (a
+// longest-first schedule), and persistent blocks deal the sorted tiles in
+// snake order (block b takes positions b, 2nbx - 1 - b, 2nbx + b, ...).
+// Host model on the skewed workloads, longest block over the ideal share:
+// 1.093 -> 1.062 (persistent, 65536 tokens) and 1.46 -> 1.13 (one block per
+// tile, GLM-4.5 shape).  Tiles inside a run keep their raster order.
+//
+// One block (k_dw_plan) writes the schedule of a launch into the GEMM
+// workspace after mt_off:
+//   [0..8]   share starts in the tile list (share x = [lo_x, lo_{x+1}))
+//   [9..17]  first run of each share (runs of share x: [base_x, base_{x+1}))
+//   then three arrays of kPlanRuns(E) entries, in run order: the run's first
+//   position inside its share, its expert, its first tile within the expert.
 constexpr int kStoreCost = 2;
+constexpr int kPlanHead = 18;
+constexpr int kPlanMaxE = 4096;
+__host__ __device__ constexpr int plan_runs(int E) { return E + 8; }
 
 __device__ __forceinline__ int dw_cost(const GemmArgs& a, int e) {
   const int Me = max(0, min(a.offsets[e + 1], a.max_rows) - a.offsets[e]);
   return (Me + BK - 1) / BK + kStoreCost;
 }
 
-// First dW tile whose start cost is >= target (target <= total cost).
-__device__ __forceinline__ int dw_tile_at(const GemmArgs& a, int per, int64_t target) {
-  const int l = lane_id();
-  int64_t cum = 0;  // cost of the experts before this chunk
-  for (int e0 = 0; e0 < a.E; e0 += kWave) {
-    const int e = e0 + l;
-    const int c = e < a.E ? dw_cost(a, e) : 0;
-    const int incl = wave_incl_scan(c);
-    const int64_t end = cum + (int64_t)per * incl;  // cost through expert e
-    const uint64_t past = __ballot(e < a.E && end > target);
-    if (past) {
-      const int f = __builtin_ctzll(past);
-      const int cf = __shfl(c, f, kWave);
-      const int64_t before = cum + (int64_t)per * (__shfl(incl, f, kWave) - cf);
-      return (e0 + f) * per + (int)((target - before + cf - 1) / cf);
+constexpr int kPlanThreads = 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void k_dw_plan(GemmPlan P) {
+  const GemmArgs& a = P.a;
+  const int E = a.E, per = P.ntm_w * P.ntn, R = plan_runs(E);
+  int32_t* plan = a.dw_plan;
+  __shared__ int cum[kPlanMaxE + 1];  // exclusive prefix of the expert costs
+  __shared__ int lds[kPlanThreads / kWave + 1];
+  __shared__ int lo[9], base[9];
+  __shared__ int re[plan_runs(kPlanMaxE)], rf[plan_runs(kPlanMaxE)];
+  __shared__ int rn[plan_runs(kPlanMaxE)], rc[plan_runs(kPlanMaxE)];
+  block_scan_array<kPlanThreads>(E, [&](int e) { return dw_cost(a, e); }, cum, lds);
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t <= 8) {
+    // share start: the first tile whose start cost is >= total * t / 8
+    int v = t == 0 ? 0 : E * per;
+    if (t > 0 && t < 8) {
+      const int64_t target = (int64_t)per * cum[E] * t / 8;
+      int l = 0, h = E;  // largest e < E with per * cum[e] <= target
+      while (h - l > 1) {
+        const int m = (l + h) >> 1;
+        if ((int64_t)per * cum[m] <= target) l = m; else h = m;
+      }
+      const int c = cum[l + 1] - cum[l];
+      const int64_t j = (target - (int64_t)per * cum[l] + c - 1) / c;
+      v = l * per + (int)min<int64_t>(j, per);
     }
-    cum += (int64_t)per * __shfl(incl, kWave - 1, kWave);
+    lo[t] = v;
   }
-  return a.E * per;
+  __syncthreads();
+  if (t == 0) {
+    int n = 0;
+    for (int x = 0; x < 8; ++x) {
+      base[x] = n;
+      if (lo[x + 1] > lo[x]) n += (lo[x + 1] - 1) / per - lo[x] / per + 1;
+    }
+    base[8] = n;
+    for (int x = 0; x <= 8; ++x) {
+      plan[x] = lo[x];
+      plan[9 + x] = base[x];
+    }
+  }
+  __syncthreads();
+  const int nr = base[8];
+  // the runs in expert order: share x, expert e, tiles [a0, a1) of the list
+  for (int r = t; r < nr; r += kPlanThreads) {
+    int x = 0;
+    while (base[x + 1] <= r) ++x;
+    const int e = lo[x] / per + (r - base[x]);
+    const int a0 = max(lo[x], e * per), a1 = min(lo[x + 1], (e + 1) * per);
+    re[r] = e;
+    rf[r] = a0 - e * per;
+    rn[r] = a1 - a0;
+    rc[r] = cum[e + 1] - cum[e];
+  }
+  __syncthreads();
+  // rank of each run inside its share (cost descending, then expert order)
+  // and its first position: the tiles of the runs ranked before it
+  for (int r = t; r < nr; r += kPlanThreads) {
+    int x = 0;
+    while (base[x + 1] <= r) ++x;
+    int rank = 0, pos = 0;
+    for (int q = base[x]; q < base[x + 1]; ++q) {
+      if (rc[q] > rc[r] || (rc[q] == rc[r] && q < r)) {
+        ++rank;
+        pos += rn[q];
+      }
+    }
+    plan[kPlanHead + base[x] + rank] = pos;
+    plan[kPlanHead + R + base[x] + rank] = re[r];
+    plan[kPlanHead + 2 * R + base[x] + rank] = rf[r];
+  }
 }
 
-__device__ __forceinline__ void dw_share(const GemmPlan& P, int x, int* lo, int* hi) {
-  const GemmArgs& a = P.a;
-  const int per = P.ntm_w * P.ntn;
-  int64_t total = 0;
-  for (int e0 = 0; e0 < a.E; e0 += kWave) {
-    const int e = e0 + lane_id();
-    total += (int64_t)per * wave_sum(e < a.E ? dw_cost(a, e) : 0);
+// The tiles one block runs, in order: tile at(k) of the launch's list, or -1
+// past the block's part of its XCD share.  dX: the share's tiles lo + b,
+// lo + b + nbx, ...  dW: the scheduled order above (runs scanned forward:
+// a block's positions only grow).
+struct TileSeq {
+  const int32_t* pre;  // dW: run starts of the share; experts at +R, first tiles at +2R
+  int R, lo, len, b, nbx, per, nrun, s;
+  __device__ __forceinline__ int at(int k) {
+    if (!pre) {
+      const int i = b + k * nbx;
+      return i < len ? lo + i : -1;
+    }
+    const int p = k * nbx + ((k & 1) ? nbx - 1 - b : b);
+    if (p >= len) return -1;
+    while (s + 1 < nrun && ld_table(pre, s + 1) <= p) ++s;
+    return ld_table(pre, R + s) * per + ld_table(pre, 2 * R + s) + (p - ld_table(pre, s));
   }
-  // wave-uniform values: keep them (and the tile cursors built on them) scalar
-  *lo = __builtin_amdgcn_readfirstlane(dw_tile_at(a, per, total * x / 8));
-  *hi = __builtin_amdgcn_readfirstlane(x == 7 ? P.nW : dw_tile_at(a, per, total * (x + 1) / 8));
+};
+
+template <bool DX>
+__device__ __forceinline__ TileSeq tile_seq(const GemmPlan& P) {
+  const GemmArgs& a = P.a;
+  const int x = blockIdx.x & 7;
+  TileSeq q;
+  q.b = blockIdx.x >> 3;
+  q.nbx = gridDim.x >> 3;
+  q.per = P.ntm_w * P.ntn;
+  q.s = 0;
+  q.nrun = 0;
+  q.R = 0;
+  q.pre = nullptr;
+  if constexpr (DX) {
+    // every dX tile runs K = d_out: equal shares of the tile count
+    const int n = ld_table(a.mt_off, a.E) * P.ntn_x;
+    q.lo = (int)((int64_t)n * x / 8);
+    q.len = (int)((int64_t)n * (x + 1) / 8) - q.lo;
+  } else {
+    const int32_t* pl = a.dw_plan;
+    q.R = plan_runs(a.E);
+    q.lo = ld_table(pl, x);
+    q.len = ld_table(pl, x + 1) - q.lo;
+    const int b0 = ld_table(pl, 9 + x);
+    q.nrun = ld_table(pl, 10 + x) - b0;
+    q.pre = pl + kPlanHead + b0;
+  }
+  return q;
 }
 
 // Persistent tile stream.  Each XCD takes a contiguous eighth of the tile list
 // (consecutive tiles share operand panels in its L2) and its blocks take the
-// tiles of that range in turn.  A block runs the k-tiles of all its tiles as
+// tiles of that range in turn (dW: in the scheduled order, TileSeq).  A block runs the k-tiles of all its tiles as
 // one stream: two LDS stages, the registers of the next k-tile stored into the
 // idle stage while the MFMAs consume the current one, global loads two k-tiles
 // ahead, one barrier per k-tile.  The loads of a tile's first k-tiles are thus
@@ -621,18 +726,10 @@ __device__ __forceinline__ void gemm_stream(const GemmPlan& P) {
   __shared__ __attribute__((aligned(16))) uint16_t As[C::STAGES * C::BM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[C::STAGES * C::BN * BK];
   const GemmArgs& a = P.a;
-  const int x = blockIdx.x & 7, nbx = gridDim.x >> 3;
-  int lo, hi;
-  if constexpr (DX) {
-    // every dX tile runs K = d_out: equal shares of the tile count
-    const int n = ld_table(a.mt_off, a.E) * P.ntn_x;
-    lo = (int)((int64_t)n * x / 8);
-    hi = (int)((int64_t)n * (x + 1) / 8);
-  } else {
-    // dW tiles of expert e run ceil(M_e / 64) k-tiles: equal shares of the cost
-    dw_share(P, x, &lo, &hi);
-  }
-  int tc = lo + (blockIdx.x >> 3);
+  // the block's tiles, in order (compute cursor sc, load cursor sl)
+  TileSeq sc = tile_seq<DX>(P);
+  int kcn = 0;
+  int tc = sc.at(0);
 
   f32x4 acc[C::FM][C::FN];
 #pragma unroll
@@ -642,12 +739,12 @@ __device__ __forceinline__ void gemm_stream(const GemmPlan& P) {
 
   // compute cursor: tile tc (job jc), k-tile kc; zero tiles are written as met
   Job jc;
-  for (; tc < hi; tc += nbx) {
+  for (; tc >= 0; tc = sc.at(++kcn)) {
     jc = make_job<C, DX>(P, tc);
     if (jc.nk > 0) break;
     if (jc.rows > 0) store_tile<C, DWB>(a, acc, true, jc.C, jc.rows, jc.cols);
   }
-  if (tc >= hi) return;
+  if (tc < 0) return;
 
   Stage<C, DX, GB> st;
   if constexpr (GB)
@@ -655,21 +752,23 @@ __device__ __forceinline__ void gemm_stream(const GemmPlan& P) {
   else
     st.init(a.d_out, a.d_in);
   // load cursor: tile tl (job jl), k-tile kl, two k-tiles ahead of the compute
+  TileSeq sl = sc;
+  int kln = kcn;
   int tl = tc, kl = 0;
   Job jl = jc;
   if constexpr (GB) st.prefetch(jl.s0, 0);  // the row map of the first load
 #define LRM_ISSUE_LOAD()                                                        \
-  if (tl < hi) {                                                                \
+  if (tl >= 0) {                                                                \
     const bool first = kl < jl.nk0;                                             \
     st.load(pick_seg(jl.s0, jl.s1, first), (first ? kl : kl - jl.nk0) * BK);   \
     if (++kl == jl.nk) {                                                        \
       kl = 0;                                                                   \
-      for (tl += nbx; tl < hi; tl += nbx) {                                     \
+      for (tl = sl.at(++kln); tl >= 0; tl = sl.at(++kln)) {                     \
         jl = make_job<C, DX>(P, tl);                                            \
         if (jl.nk > 0) break;                                                   \
       }                                                                         \
     }                                                                           \
-    if (GB && tl < hi) {                                                        \
+    if (GB && tl >= 0) {                                                        \
       const bool f2 = kl < jl.nk0;                                              \
       st.prefetch(pick_seg(jl.s0, jl.s1, f2), (f2 ? kl : kl - jl.nk0) * BK);   \
     }                                                                           \
@@ -713,12 +812,12 @@ __device__ __forceinline__ void gemm_stream(const GemmPlan& P) {
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
       kc = 0;
-      for (tc += nbx; tc < hi; tc += nbx) {
+      for (tc = sc.at(++kcn); tc >= 0; tc = sc.at(++kcn)) {
         jc = make_job<C, DX>(P, tc);
         if (jc.nk > 0) break;
         if (jc.rows > 0) store_tile<C, DWB>(a, acc, true, jc.C, jc.rows, jc.cols);
       }
-      if (tc >= hi) break;
+      if (tc < 0) break;
     }
     __syncthreads();
   }
@@ -982,16 +1081,9 @@ __device__ __forceinline__ void gemm_dma(const GemmPlan& P) {
   constexpr int SA = C::BM * C::BK, SS = (C::BM + C::BN) * C::BK;  // elements
   __shared__ __attribute__((aligned(1024))) uint16_t L[S * SS];
   const GemmArgs& a = P.a;
-  const int x = blockIdx.x & 7, nbx = gridDim.x >> 3;
-  int lo, hi;
-  if constexpr (DX) {
-    const int n = ld_table(a.mt_off, a.E) * P.ntn_x;
-    lo = (int)((int64_t)n * x / 8);
-    hi = (int)((int64_t)n * (x + 1) / 8);
-  } else {
-    dw_share(P, x, &lo, &hi);
-  }
-  int tc = lo + (blockIdx.x >> 3);
+  TileSeq sc = tile_seq<DX>(P);
+  int kcn = 0;
+  int tc = sc.at(0);
 
   f32x4 acc[C::FM][C::FN];
 #pragma unroll
@@ -1003,12 +1095,12 @@ __device__ __forceinline__ void gemm_dma(const GemmPlan& P) {
   // which is zero wherever they are met (stored as constants, the zeros of
   // the fp32 stores end up spilled as scalar registers).
   Job jc;
-  for (; tc < hi; tc += nbx) {
+  for (; tc >= 0; tc = sc.at(++kcn)) {
     jc = make_job<C, DX>(P, tc);
     if (jc.nk > 0) break;
     if (jc.rows > 0) store_tile<C, DWB>(a, acc, false, jc.C, jc.rows, jc.cols);
   }
-  if (tc >= hi) return;
+  if (tc < 0) return;
 
   DmaStage<C, DX> st;
   st.init(a.d_out, a.d_in);
@@ -1018,18 +1110,20 @@ __device__ __forceinline__ void gemm_dma(const GemmPlan& P) {
   // (every wave issues the same ones); mk[s]: vm just after the loads of the
   // s-th oldest k-tile in flight
   int vm = 0, mk[S];
+  TileSeq sl = sc;
+  int kln = kcn;
   int tl = tc, kl = 0, nxt = 0;
   Job jl = jc;
   // the next k-tile of the stream (if any) into stage nxt, its mark in mk[slot]
   auto issue = [&](int slot) {
-    if (tl < hi) {
+    if (tl >= 0) {
       const bool first = kl < jl.nk0;
       uint16_t* dst = L + nxt * SS;
       st.load(pick_seg(jl.s0, jl.s1, first), (first ? kl : kl - jl.nk0) * C::BK, dst, dst + SA);
       vm += 2 * C::NQ;
       if (++kl == jl.nk) {
         kl = 0;
-        for (tl += nbx; tl < hi; tl += nbx) {
+        for (tl = sl.at(++kln); tl >= 0; tl = sl.at(++kln)) {
           jl = make_job<C, DX>(P, tl);
           if (jl.nk > 0) break;
         }
@@ -1063,8 +1157,8 @@ __device__ __forceinline__ void gemm_dma(const GemmPlan& P) {
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
           for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        tc += nbx;
-        if (tc >= hi) {
+        tc = sc.at(++kcn);
+        if (tc < 0) {
           done = true;
           break;
         }
@@ -1344,11 +1438,20 @@ static hipError_t launch_product(const GemmPlan& P, int ntiles_max, hipStream_t 
   return launch_stream<C, DX>(P, ntiles_max, s, per_tile);
 }
 
+int64_t gemm_workspace_ints(int E) {
+  return (int64_t)E + 1 + kPlanHead + 3 * (int64_t)plan_runs(E);
+}
+
 template <class CW, class CX>
 static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
   GemmPlan P{};
   hipError_t err = plan_tiles(a, CW::BM, CW::BN, CX::BM, CX::BN, &P, s);
   if (err != hipSuccess) return err;
+  if (P.nW > 0) {
+    P.a.dw_plan = a.mt_off + a.E + 1;
+    LRM_LAUNCH(1, kPlanThreads, 0, s, k_dw_plan)(P);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   // With many rows per expert (256x256 tiles for both products, MFMA-bound)
   // the k-tile counts of dW tiles follow the expert sizes, which are skewed.
   // Each XCD still takes its share of equal cost, but with one block per tile
@@ -1390,7 +1493,8 @@ int gemm_dx_tile_rows(const GemmArgs& a) {
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s) {
-  if (!a.offsets || (a.dXp && (!a.W || !a.mt_off || !a.Gp)) || (a.dW && !a.Gp) ||
+  if (!a.offsets || !a.mt_off || a.E < 1 || a.E > kPlanMaxE || (a.dXp && (!a.W || !a.Gp)) ||
+      (a.dW && !a.Gp) ||
       (a.dW && a.max_rows > 0 && !a.Xp && !a.xrow) ||
       (a.Gp2 && (!a.W2 || a.d_out2 != a.d_out)))
     return hipErrorInvalidValue;

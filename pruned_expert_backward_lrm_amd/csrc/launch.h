@@ -149,7 +149,7 @@ struct GemmArgs {
   const void* Gp2; const void* W2; int64_t w2_stride; int d_out2;  // optional
   float* dW;   // [E][d_out][d_in] or nullptr
   float* dXp;  // [max_rows][d_in] or nullptr
-  int32_t* mt_off;  // workspace [E+1]
+  int32_t* mt_off;  // workspace [gemm_workspace_ints(E)]: the dX row-tile prefix [E+1], then the dW schedule
   int mt_ready;     // mt_off already holds the prefix for gemm_dx_tile_rows(*this)
   int dw_bf16;      // dW is stored as bf16 (round to nearest even), bf16 kernels only
   hipEvent_t mid_event;  // recorded after the dW launch, before the dX launch (or null)
@@ -159,7 +159,10 @@ struct GemmArgs {
   // xsrc has xsrc_rows rows of leading dimension ldxs, under 2 GiB.
   const void* xsrc; int64_t ldxs; int64_t xsrc_rows;
   const int32_t* xrow; const float* xw;
+  int32_t* dw_plan;  // set by launch_grouped_gemm (inside the mt_off workspace)
 };
+// int32 entries of the grouped GEMM's workspace for E experts
+int64_t gemm_workspace_ints(int E);
 int gemm_tile_choice(const GemmArgs& a);
 // Rows of a dX tile of the bf16 kernels (the prefix mt_off is built for it).
 int gemm_dx_tile_rows(const GemmArgs& a);

@@ -407,7 +407,7 @@ lrm_status lrm_compact_rows(const lrm_pairs* pairs, const int32_t* kept, const i
 size_t lrm_grouped_bwd_workspace_size(int32_t E) {
   if (E < 1 || E > kMaxE) return 0;
   Carve c(nullptr);
-  c.take<int32_t>(E + 1);
+  c.take<int32_t>(gemm_workspace_ints(E));
   return c.size();
 }
 
@@ -435,7 +435,7 @@ lrm_status lrm_grouped_bwd(int32_t E, const int32_t* offsets, int32_t max_rows, 
   g.offsets = offsets; g.Gp = Gp; g.Xp = Xp; g.W = W; g.w_stride = w_stride;
   g.dW = dW; g.dXp = dXp;
   Carve r(ws);
-  g.mt_off = r.take<int32_t>(E + 1);
+  g.mt_off = r.take<int32_t>(gemm_workspace_ints(E));
   LRM_TRY_HIP(launch_grouped_gemm(g, as_stream(stream)));
   return LRM_OK;
 }
@@ -563,7 +563,7 @@ LinearPlan carve_linear(Carve& c, const lrm_problem* pb, const lrm_outputs* out,
   L.offsets = c.take<int32_t>(p.E + 1);
   L.kept = c.take<int32_t>(p.N);
   L.tok_off = c.take<int32_t>((int64_t)p.T + 1);
-  L.mt_off = c.take<int32_t>(p.E + 1);
+  L.mt_off = c.take<int32_t>(gemm_workspace_ints(p.E));
   L.Gp = c.take<char>(Mcap * pb->d_out * es);
   if (gather_loads(pb)) {
     L.xrow = c.take<int32_t>(Mcap);
@@ -630,7 +630,7 @@ GluPlan carve_glu(Carve& c, const lrm_problem* pb, const lrm_outputs* out, int64
   L.offsets = c.take<int32_t>(p.E + 1);
   L.kept = c.take<int32_t>(p.N);
   L.tok_off = c.take<int32_t>((int64_t)p.T + 1);
-  L.mt_off = c.take<int32_t>(p.E + 1);
+  L.mt_off = c.take<int32_t>(gemm_workspace_ints(p.E));
   L.Gd = c.take<char>(Md * H * es);
   L.Hd = c.take<char>(Md * I * es);
   L.U = c.take<float>(Md * I);
