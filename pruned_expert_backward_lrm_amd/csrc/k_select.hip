@@ -17,13 +17,17 @@
 //                     candidate order that keeps keys above the threshold and
 //                     the first (lowest-index) ties, and writes packed rows.
 // Scores are >= 0, so their fp32 bit patterns order like the values.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
 namespace lrm {
 
 constexpr int kSelThreads = 1024;
-constexpr int kSelRegKeys = 4;  // keys per thread held in registers by k_select
+constexpr int kSelRegKeys = 8;  // keys per thread held in registers by k_select
+constexpr int kSelRunKeys = 8;  // keys per thread and round of k_select's keep pass (larger experts)
+static_assert(kSelRunKeys * kSelThreads < (1 << 16), "packed round counts of k_select");
 constexpr int kScanTile = 8192;  // block counts staged in LDS per round by k_bucket_scan
 constexpr int kScatBatch = 8;   // 64-pair groups per wave loaded ahead by k_bucket_scatter
 
@@ -284,6 +288,19 @@ __global__ __launch_bounds__(64) void k_bucket_scatter(int N, int T, int E, int 
 // Candidates and packed slots are clipped to [0, limit), the extent of keys,
 // cand, pos and kept (offsets beyond it arise only when a captured call is
 // replayed with other host quotas, flagged by the offsets kernels).
+//
+// The threshold is the m-th largest key, found in three radix passes (bits
+// 20-31, 10-19, 0-9).  The 4096 bins of the first digit spread keys that share
+// an exponent; with 256 bins a few hot bins serialized the LDS atomics.
+// Experts of up to kSelRegKeys * kSelThreads candidates hold their keys in
+// registers, thread t the run of K = ceil(n / kSelThreads) consecutive
+// candidates from tK; larger ones are read from global memory, strided
+// (coalesced) by the passes.  Then, in candidate order, rounds of runs of
+// consecutive candidates per thread: each thread counts its keys above the
+// threshold and equal to it, one block scan of each count gives it its
+// first slot, and it keeps the keys above the threshold and the first r
+// equal ones of the expert.  The round's slots are staged in LDS and
+// written out by consecutive lanes on consecutive candidates.
 __global__ __launch_bounds__(kSelThreads) void k_select(const int32_t* __restrict__ cand_off,
                                                         const int32_t* __restrict__ offsets,
                                                         const uint32_t* __restrict__ keys,
@@ -296,9 +313,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const int32_t* __restric
   const int o = min(offsets[e], limit);
   const int m = min(offsets[e + 1], limit) - o;
   const int tid = threadIdx.x;
-  // two histograms and two result slots, alternating between radix passes,
-  // so that a pass needs two barriers (after the counts, after the search)
-  __shared__ int hist[2][256];
+  // the passes' histograms (4096 + 1024 bins), then a round's slots
+  constexpr int kHist = kSelRunKeys * kSelThreads > 4096 + 1024 ? kSelRunKeys * kSelThreads
+                                                                 : 4096 + 1024;
+  __shared__ int hist[kHist];
   __shared__ int lds[kSelThreads / kWave + 1];
   __shared__ uint32_t sh_prefix[2];
   __shared__ int sh_rank[2];
@@ -316,104 +334,150 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const int32_t* __restric
     for (int i = tid; i < n; i += kSelThreads) pos[id_of(c0 + i)] = -1;
     return;
   }
-  // radix search for the m-th largest key (rank r counted from the top); the
-  // keys of experts with up to kSelRegKeys * kSelThreads candidates are read
-  // once into registers
-  const bool in_regs = n <= kSelRegKeys * kSelThreads;
+  const int K = (n + kSelThreads - 1) / kSelThreads;  // run length (uniform)
+  const int i0 = tid * K;
+  const int cnt = max(0, min(K, n - i0));  // keys of this thread's run
+  const bool in_regs = K <= kSelRegKeys;
   uint32_t kr[kSelRegKeys];
-  int idr[kSelRegKeys];  // their ids, requested with the keys
 #pragma unroll
   for (int j = 0; j < kSelRegKeys; ++j) {
-    const int i = tid + j * kSelThreads;
-    const bool ld = in_regs && i < n;
-    kr[j] = ld ? keys[c0 + i] : 0u;
-    idr[j] = ld ? id_of(c0 + i) : 0;
+    kr[j] = 0u;
+    if (in_regs && j < K) {
+      const uint32_t v = keys[c0 + min(i0 + j, n - 1)];
+      kr[j] = j < cnt ? v : 0u;
+    }
   }
+  int* h0 = hist;         // 4096 bins: pass 1, then the first 1024 for pass 3
+  int* h1 = hist + 4096;  // 1024 bins: pass 2
+  for (int i = tid; i < 4096 + 1024; i += kSelThreads) hist[i] = 0;
+  __syncthreads();
   uint32_t prefix = 0, pmask = 0;
   int r = m;
-  if (tid < 256) hist[0][tid] = 0;
-  __syncthreads();
-  for (int shift = 24, buf = 0; shift >= 0; shift -= 8, buf ^= 1) {
-    int* h = hist[buf];
-    // the other histogram was last read before the previous pass's second
-    // barrier: clear it for the next pass
-    if (tid < 256) hist[buf ^ 1][tid] = 0;
+  // One pass: count the keys under the current prefix by digit (shift; nb
+  // bins in h), then find the digit of the r-th largest.
+  auto pass = [&](int* h, int shift, int nb, int buf) {
+    const uint32_t dm = (uint32_t)(nb - 1);
     if (in_regs) {
 #pragma unroll
-      for (int j = 0; j < kSelRegKeys; ++j) {
-        const uint32_t k = kr[j];
-        if (tid + j * kSelThreads < n && (k & pmask) == prefix)
-          atomicAdd(&h[(k >> shift) & 255u], 1);
-      }
+      for (int j = 0; j < kSelRegKeys; ++j)
+        if (j < cnt && (kr[j] & pmask) == prefix) atomicAdd(&h[(kr[j] >> shift) & dm], 1);
     } else {
-      for (int i = tid; i < n; i += kSelThreads) {
+      int i = tid;
+      for (; i + 3 * kSelThreads < n; i += 4 * kSelThreads) {
+        uint32_t k4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) k4[u] = keys[c0 + i + u * kSelThreads];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if ((k4[u] & pmask) == prefix) atomicAdd(&h[(k4[u] >> shift) & dm], 1);
+      }
+      for (; i < n; i += kSelThreads) {
         const uint32_t k = keys[c0 + i];
-        if ((k & pmask) == prefix) atomicAdd(&h[(k >> shift) & 255u], 1);
+        if ((k & pmask) == prefix) atomicAdd(&h[(k >> shift) & dm], 1);
       }
     }
     __syncthreads();
-    if (tid < kWave) {
-      // lane l owns bins 255-4l .. 252-4l (descending)
-      int c[4];
-      int local = 0;
+    // thread t holds the bins nb-1-q*t-i (q = nb / kSelThreads, descending)
+    const int q = nb / kSelThreads;
+    int c[4];
+    int local = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c[j] = h[255 - 4 * tid - j];
-        local += c[j];
-      }
-      int before = wave_incl_scan(local) - local;
+    for (int i = 0; i < 4; ++i) {
+      c[i] = i < q ? h[nb - 1 - q * tid - i] : 0;
+      local += c[i];
+    }
+    int tot;
+    int before = block_excl_scan<kSelThreads>(local, lds, &tot);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (before < r && before + c[j] >= r) {
-          sh_prefix[buf] = prefix | ((uint32_t)(255 - 4 * tid - j) << shift);
-          sh_rank[buf] = r - before;
-        }
-        before += c[j];
+    for (int i = 0; i < 4; ++i) {
+      if (i < q && before < r && before + c[i] >= r) {
+        sh_prefix[buf] = prefix | ((uint32_t)(nb - 1 - q * tid - i) << shift);
+        sh_rank[buf] = r - before;
       }
+      before += c[i];
     }
     __syncthreads();
     prefix = sh_prefix[buf];
     r = sh_rank[buf];
-    pmask |= 0xffu << shift;
-  }
-  // keep keys above the threshold, and the first r keys equal to it: one
-  // block scan of the packed counts (greater << 16 | equal, each < 2^16 per
-  // round); a kept key's slot is (greater before) + min(equal before, r)
-  const uint32_t K = prefix;
-  int eq_carry = 0, gt_carry = 0;
-  for (int base = 0; base < n; base += kSelThreads) {
-    const int i = base + tid;
-    const bool valid = i < n;
-    uint32_t k = 0u;
-    int id = 0;
-    if (in_regs) {
+    pmask |= dm << shift;
+  };
+  pass(h0, 20, 4096, 0);
+  // h0 is free again (its last reads were before pass 1's final barrier)
+  for (int i = tid; i < 1024; i += kSelThreads) h0[i] = 0;
+  pass(h1, 10, 1024, 1);
+  pass(h0, 0, 1024, 0);
+  const uint32_t T = prefix;
+  // keep the keys above T and the first r keys equal to it, in candidate
+  // order; a kept key's slot is (greater before) + min(equal before, r).
+  // Rounds of RUN * kSelThreads candidates, thread t the run of RUN from
+  // RUN t (its keys loaded together: a wave's runs share a few cache lines),
+  // one block scan of each count per round.
+  // One round: thread t the run of len_run candidates from base + len_run t
+  // (at most RUN, a compile-time bound; the run's keys in k, rl of them real).
+  int* slot_of = hist;  // the round's slots (-1: dropped), candidate order
+  int gt_carry = 0, eq_carry = 0;
+  auto round = [&](auto run_c, int len_run, int base, int rl, const uint32_t* k) {
+    constexpr int RUN = decltype(run_c)::value;
+    // the ids of the round's write-out, requested before the scan
+    const int len = min(len_run * kSelThreads, n - base);
+    int ids[RUN];
 #pragma unroll
-      for (int j = 0; j < kSelRegKeys; ++j)
-        if (base == j * kSelThreads) {
-          k = kr[j];
-          id = idr[j];
-        }
-    } else if (valid) {
-      k = keys[c0 + i];
-      id = id_of(c0 + i);
+    for (int u = 0; u < RUN; ++u) ids[u] = id_of(c0 + base + min(tid + u * kSelThreads, len - 1));
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < RUN; ++j) {
+      gt += (j < rl && k[j] > T) ? 1 : 0;
+      eq += (j < rl && k[j] == T) ? 1 : 0;
     }
-    const int eq = (valid && k == K) ? 1 : 0;
-    const int gt = (valid && k > K) ? 1 : 0;
+    // one scan of both counts, packed (a round's totals stay below 2^16);
+    // its barriers also order this round's slot stores after the previous
+    // round's reads
     int tot;
     const int ex = block_excl_scan<kSelThreads>((gt << 16) | eq, lds, &tot);
-    const int eq_before = eq_carry + (ex & 0xffff);
-    const int gt_before = gt_carry + (ex >> 16);
-    eq_carry += tot & 0xffff;
+    int gt_before = gt_carry + (ex >> 16);
+    int eq_before = eq_carry + (ex & 0xffff);
     gt_carry += tot >> 16;
-    const bool keep = gt || (eq && eq_before < r);
-    if (valid) {
-      if (keep) {
-        const int slot = gt_before + min(eq_before, r);
-        kept[o + slot] = id;
-        pos[id] = o + slot;
-      } else {
-        pos[id] = -1;
+    eq_carry += tot & 0xffff;
+#pragma unroll
+    for (int j = 0; j < RUN; ++j) {
+      if (j < rl) {
+        const bool g = k[j] > T, q = k[j] == T;
+        slot_of[len_run * tid + j] =
+            (g || (q && eq_before < r)) ? o + gt_before + min(eq_before, r) : -1;
+        gt_before += g ? 1 : 0;
+        eq_before += q ? 1 : 0;
       }
+    }
+    __syncthreads();
+    // write out with consecutive lanes on consecutive candidates (a wave's
+    // stores then cover few cache lines)
+#pragma unroll
+    for (int u = 0; u < RUN; ++u) {
+      const int i = tid + u * kSelThreads;
+      if (i < len) {
+        const int slot = slot_of[i];
+        pos[ids[u]] = slot;
+        if (slot >= 0) kept[slot] = ids[u];
+      }
+    }
+  };
+  if (in_regs) {
+    round(std::integral_constant<int, kSelRegKeys>{}, K, 0, cnt, kr);
+  } else {
+    constexpr int RUN = kSelRunKeys;
+    // the next round's keys are requested before this round's scan
+    uint32_t k[RUN], kn[RUN];
+#pragma unroll
+    for (int j = 0; j < RUN; ++j) kn[j] = keys[c0 + min(RUN * tid + j, n - 1)];
+    for (int base = 0; base < n; base += RUN * kSelThreads) {
+      const int rs = base + RUN * tid;
+      const int rl = max(0, min(RUN, n - rs));
+#pragma unroll
+      for (int j = 0; j < RUN; ++j) {
+        k[j] = kn[j];
+        kn[j] = keys[c0 + min(rs + RUN * kSelThreads + j, n - 1)];
+      }
+      round(std::integral_constant<int, RUN>{}, RUN, base, rl, k);
     }
   }
 }

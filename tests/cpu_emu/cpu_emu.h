@@ -246,6 +246,10 @@ inline void buffer_store8(u32x2_emu v, BufRsrc r, int voff, int soff) {
   const long long off = (long long)voff + soff;
   if (off >= 0 && off + 8 <= r.n) std::memcpy(const_cast<char*>(r.base) + off, &v, 8);
 }
+inline void buffer_store4(int v, BufRsrc r, int voff, int soff) {
+  const long long off = (long long)voff + soff;
+  if (off >= 0 && off + 4 <= r.n) std::memcpy(const_cast<char*>(r.base) + off, &v, 4);
+}
 // v_perm_b32: result byte i = byte sel_i of the 8-byte value {s0 (bytes 4..7), s1 (bytes 0..3)}
 inline unsigned perm(unsigned s0, unsigned s1, unsigned sel) {
   const unsigned long long v = ((unsigned long long)s0 << 32) | s1;
@@ -267,6 +271,8 @@ typedef ::emu::BufRsrc __amdgpu_buffer_rsrc_t;
   ::emu::buffer_store16((v), (r), (voff), (soff))
 #define __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, aux) \
   ::emu::buffer_store8((v), (r), (voff), (soff))
+#define __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, soff, aux) \
+  ::emu::buffer_store4((v), (r), (voff), (soff))
 #define __builtin_amdgcn_perm(s0, s1, sel) ::emu::perm((s0), (s1), (sel))
 
 namespace emu {

@@ -137,6 +137,42 @@ def test_select_large_expert(L):
     check_packing(pos, offsets, r.expert, E)
 
 
+@pytest.mark.parametrize("ties", [False, True])
+def test_select_run_boundaries(L, ties):
+    """Experts at the per-expert selection's size boundaries: 8192 candidates
+    (the last size held in registers, 8 per thread), 8193 (keys read from
+    memory, a second round of one candidate), 16385 and 1; quotas of one
+    candidate, half, and all but one.  With ties: a handful of integer scores,
+    zeros among them, so the threshold falls in runs of equal keys that cross
+    thread and round boundaries."""
+    say("select boundaries", ties)
+    sizes = [8192, 8193, 16385, 1, 3]
+    E = len(sizes) * 3
+    rng = np.random.default_rng(11 + ties)
+    expert = np.concatenate([np.full(n, e, np.int32)
+                             for e, n in enumerate(sizes * 3)])
+    order = rng.permutation(expert.size)
+    expert = expert[order]
+    N = expert.size
+    r = synth.Routing(N, E, 1, expert, np.arange(N, dtype=np.int32),
+                      rng.random(N).astype(np.float32), np.bincount(expert, minlength=E), {})
+    if ties:
+        s = rng.integers(0, 5, N).astype(np.float32)
+    else:
+        s = (rng.standard_normal(N) ** 2 * 1e-3).astype(np.float32)
+    c = r.counts
+    q = np.concatenate([np.ones(len(sizes)), c[len(sizes):2 * len(sizes)] // 2,
+                        np.maximum(c[2 * len(sizes):] - 1, 0)]).astype(np.int64)
+    pos, offsets, kept, _ = _select(L, r, s, q)
+    ora = O.select_top_quota(r.expert, s.astype(np.float64), q, E)
+    gk = kept_from_pos(pos, r.expert, E)
+    for e in range(E):
+        assert np.array_equal(gk[e], ora[e]), f"expert {e} ({c[e]} candidates, quota {q[e]})"
+    check_packing(pos, offsets, r.expert, E)
+    M = offsets[-1]
+    assert np.array_equal(kept[:M], np.concatenate(ora))
+
+
 def test_select_keep_all_and_index_errors(L):
     say("select keep_all / index errors")
     p = synth.make_linear(128, 5, 2, 16, 16, dtype="f32", seed=6)
