@@ -56,13 +56,33 @@ __global__ __launch_bounds__(256) void k_row_sumsq(const char* __restrict__ M, i
   if (lane_id() == 0) out[r] = s;
 }
 
+// silu(a) = a / (1 + e^-a) in fp32, within a few ulp, in about half the
+// instructions of expf and an IEEE divide (the GLU score pass is bound by
+// this arithmetic, not by its loads):
+//   e^-a = 2^t 2^c with t = -a log2(e) rounded to fp32 and c its rounding
+//   error (an fma, plus the low part of log2(e)), 2^c ~ 1 + c ln 2 (|c| <
+//   2^-17); 2^t by the hardware exp2 (v_exp_f32);
+//   1 / (1 + e^-a) by the hardware reciprocal and one Newton step, e^-a
+//   capped at 2^126 so that its reciprocal stays a normal number (below
+//   a = -87, where the cap applies, |silu(a)| < 2^-120: a negligible term of
+//   a sum of squares).
+__device__ __forceinline__ float silu_f32(float a) {
+  const float kL = 1.44269502f, kLlo = 1.92596299e-8f, kLn2 = 0.693147181f;
+  const float t = -a * kL;
+  const float c = fmaf(-a, kL, -t) - a * kLlo;
+  const float e = fminf(__builtin_amdgcn_exp2f(t) * fmaf(c, kLn2, 1.0f), 8.50705917e37f);
+  const float d = 1.0f + e;
+  float r = __builtin_amdgcn_rcpf(d);
+  r = fmaf(r, fmaf(-d, r, 1.0f), r);
+  return a * r;
+}
+
 // h = silu(a) * b for one 16-byte chunk of a and b; returns sum of h^2.
 __device__ __forceinline__ double glu_chunk_sumsq_bf16(u32x4 a, u32x4 b, double acc) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float a0 = bf16_lo(a[i]), a1 = bf16_hi(a[i]);
-    float h0 = a0 / (1.0f + expf(-a0)) * bf16_lo(b[i]);
-    float h1 = a1 / (1.0f + expf(-a1)) * bf16_hi(b[i]);
+    float h0 = silu_f32(bf16_lo(a[i])) * bf16_lo(b[i]);
+    float h1 = silu_f32(bf16_hi(a[i])) * bf16_hi(b[i]);
     acc = fma((double)h0, (double)h0, acc);
     acc = fma((double)h1, (double)h1, acc);
   }
@@ -71,8 +91,7 @@ __device__ __forceinline__ double glu_chunk_sumsq_bf16(u32x4 a, u32x4 b, double 
 __device__ __forceinline__ double glu_chunk_sumsq_f32(u32x4 a, u32x4 b, double acc) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float av = __uint_as_float(a[i]);
-    float h = av / (1.0f + expf(-av)) * __uint_as_float(b[i]);
+    float h = silu_f32(__uint_as_float(a[i])) * __uint_as_float(b[i]);
     acc = fma((double)h, (double)h, acc);
   }
   return acc;
