@@ -330,6 +330,9 @@ inline V4 ds_read_tr16(const V4* p) {
 }
 }  // namespace emu
 #define __builtin_amdgcn_ds_read_tr16_b64_v4i16(p) ::emu::ds_read_tr16(p)
+// the hardware exp2 and reciprocal, modelled correctly rounded
+#define __builtin_amdgcn_exp2f(x) ::exp2f(x)
+#define __builtin_amdgcn_rcpf(x) (1.0f / (x))
 // memory operations complete at once here: waits have nothing to wait for
 #define __builtin_amdgcn_s_waitcnt(imm) ((void)(imm))
 #define __builtin_amdgcn_s_barrier() ::emu::syncthreads()
