@@ -574,8 +574,8 @@ __device__ __forceinline__ void mma_k32(f32x4 (&acc)[C::FM][C::FN], const uint16
 // 1.093 -> 1.062 (persistent, 65536 tokens) and 1.46 -> 1.13 (one block per
 // tile, GLM-4.5 shape).  Tiles inside a run keep their raster order.
 //
-// One block (k_dw_plan) writes the schedule of a launch into the GEMM
-// workspace after mt_off:
+// One block (k_dw_plan; 256 threads up to 1024 experts, else 1024) writes
+// the schedule of a launch into the GEMM workspace after mt_off:
 //   [0..8]   share starts in the tile list (share x = [lo_x, lo_{x+1}))
 //   [9..17]  first run of each share (runs of share x: [base_x, base_{x+1}))
 //   then three arrays of kPlanRuns(E) entries, in run order: the run's first
@@ -590,18 +590,18 @@ __device__ __forceinline__ int dw_cost(const GemmArgs& a, int e) {
   return (Me + BK - 1) / BK + kStoreCost;
 }
 
-constexpr int kPlanThreads = 1024;
-
-__global__ __launch_bounds__(kPlanThreads) void k_dw_plan(GemmPlan P) {
+// NT threads (E <= 4 NT: one block scan of the expert costs)
+template <int NT>
+__global__ __launch_bounds__(NT) void k_dw_plan(GemmPlan P) {
   const GemmArgs& a = P.a;
   const int E = a.E, per = P.ntm_w * P.ntn, R = plan_runs(E);
   int32_t* plan = a.dw_plan;
   __shared__ int cum[kPlanMaxE + 1];  // exclusive prefix of the expert costs
-  __shared__ int lds[kPlanThreads / kWave + 1];
+  __shared__ int lds[NT / kWave + 1];
   __shared__ int lo[9], base[9];
   __shared__ int re[plan_runs(kPlanMaxE)], rf[plan_runs(kPlanMaxE)];
   __shared__ int rn[plan_runs(kPlanMaxE)], rc[plan_runs(kPlanMaxE)];
-  block_scan_array<kPlanThreads>(E, [&](int e) { return dw_cost(a, e); }, cum, lds);
+  block_scan_array<NT>(E, [&](int e) { return dw_cost(a, e); }, cum, lds);
   __syncthreads();
   const int t = threadIdx.x;
   if (t <= 8) {
@@ -636,7 +636,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_dw_plan(GemmPlan P) {
   __syncthreads();
   const int nr = base[8];
   // the runs in expert order: share x, expert e, tiles [a0, a1) of the list
-  for (int r = t; r < nr; r += kPlanThreads) {
+  for (int r = t; r < nr; r += NT) {
     int x = 0;
     while (base[x + 1] <= r) ++x;
     const int e = lo[x] / per + (r - base[x]);
@@ -649,7 +649,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_dw_plan(GemmPlan P) {
   __syncthreads();
   // rank of each run inside its share (cost descending, then expert order)
   // and its first position: the tiles of the runs ranked before it
-  for (int r = t; r < nr; r += kPlanThreads) {
+  for (int r = t; r < nr; r += NT) {
     int x = 0;
     while (base[x + 1] <= r) ++x;
     int rank = 0, pos = 0;
@@ -1449,8 +1449,13 @@ static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
   if (err != hipSuccess) return err;
   if (P.nW > 0) {
     P.a.dw_plan = a.mt_off + a.E + 1;
-    LRM_LAUNCH(1, kPlanThreads, 0, s, k_dw_plan)(P);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (!a.dw_plan_ready) {
+      if (a.E <= 4 * 256)
+        LRM_LAUNCH(1, 256, 0, s, k_dw_plan<256>)(P);
+      else
+        LRM_LAUNCH(1, 1024, 0, s, k_dw_plan<1024>)(P);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
   }
   // With many rows per expert (256x256 tiles for both products, MFMA-bound)
   // the k-tile counts of dW tiles follow the expert sizes, which are skewed.
@@ -1480,6 +1485,17 @@ int gemm_tile_choice(const GemmArgs& a) {
   if (env && env[0] == 'X') return 3;
   const int64_t per_expert = a.E > 0 ? (int64_t)a.max_rows / a.E : 0;
   return per_expert >= 192 ? 2 : 3;
+}
+
+int gemm_dw_tiles_per_expert(const GemmArgs& a) {
+  if (!a.bf16 || !a.dW) return 0;
+  auto per = [&](int bm, int bn) { return ((a.d_out + bm - 1) / bm) * ((a.d_in + bn - 1) / bn); };
+  switch (gemm_tile_choice(a)) {
+    case 3:
+    case 2: return per(CfgL::BM, CfgL::BN);
+    case 1: return per(CfgM::BM, CfgM::BN);
+    default: return per(CfgS::BM, CfgS::BN);
+  }
 }
 
 int gemm_dx_tile_rows(const GemmArgs& a) {

@@ -160,9 +160,15 @@ struct GemmArgs {
   const void* xsrc; int64_t ldxs; int64_t xsrc_rows;
   const int32_t* xrow; const float* xw;
   int32_t* dw_plan;  // set by launch_grouped_gemm (inside the mt_off workspace)
+  // the workspace already holds the dW schedule of a launch with the same
+  // offsets, max_rows and gemm_dw_tiles_per_expert (the schedule depends on
+  // nothing else)
+  int dw_plan_ready;
 };
 // int32 entries of the grouped GEMM's workspace for E experts
 int64_t gemm_workspace_ints(int E);
+// dW tiles per expert of the bf16 kernels (0: no scheduled dW launch)
+int gemm_dw_tiles_per_expert(const GemmArgs& a);
 int gemm_tile_choice(const GemmArgs& a);
 // Rows of a dX tile of the bf16 kernels (the prefix mt_off is built for it).
 int gemm_dx_tile_rows(const GemmArgs& a);

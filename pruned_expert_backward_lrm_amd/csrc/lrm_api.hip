@@ -984,6 +984,11 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
       gg.xsrc_rows = xsrc_rows;
     }
     gg.mid_event = mark.at(9);
+    // the down projection's dW launch left the schedule of these offsets and
+    // max_rows in the workspace: the gate and up launches reuse it when their
+    // tiles per expert agree (the schedule depends on nothing else)
+    const int plan_per = gemm_dw_tiles_per_expert(gd);
+    gg.dw_plan_ready = plan_per > 0 && gemm_dw_tiles_per_expert(gg) == plan_per;
     LRM_TRY_HIP(launch_grouped_gemm(gg, s));
     LRM_TRY_HIP(mark(10));
     GemmArgs gu{};
@@ -991,6 +996,7 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
     gu.offsets = L.offsets; gu.Gp = L.GB; gu.Xp = L.Xgu;
     gu.dW = out->dW_up; gu.dXp = nullptr; gu.mt_off = L.mt_off;
     gu.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
+    gu.dw_plan_ready = plan_per > 0 && gemm_dw_tiles_per_expert(gu) == plan_per;
     if (L.xrow_u) {
       gu.xrow = L.xrow_u; gu.xw = L.xw_u; gu.xsrc = pb->X.ptr; gu.ldxs = pb->X.ld;
       gu.xsrc_rows = xsrc_rows;
