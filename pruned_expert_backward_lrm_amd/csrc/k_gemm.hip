@@ -85,10 +85,11 @@ __device__ __forceinline__ bool is_dx_tile(int L, int nW, int nX, int* idx) {
   return false;
 }
 
-// Grouped raster over an nr x nc tile grid: tiles are taken kRasterH rows at a
-// time, column by column, so the tiles resident on one XCD at any moment (a
-// window of consecutive positions) share a few row panels and a few column
-// panels in its L2 instead of one row panel and every column panel.
+// Grouped raster over an nr x nc tile grid (the dW tiles of one expert):
+// tiles are taken kRasterH rows at a time, column by column, so the tiles
+// resident on one XCD at any moment (a window of consecutive positions) share
+// a few row panels and a few column panels in its L2 instead of one row panel
+// and every column panel.
 constexpr int kRasterH = 4;
 __device__ __forceinline__ void raster(int t, int nr, int nc, int* r, int* c) {
   const int r0 = t / (kRasterH * nc) * kRasterH;
@@ -96,6 +97,27 @@ __device__ __forceinline__ void raster(int t, int nr, int nc, int* r, int* c) {
   const int rem = t - r0 * nc;
   *r = r0 + rem % gh;
   *c = rem / gh;
+}
+
+// dX tiles (row tiles of all experts, back to back, x nc column tiles): the
+// row tiles of one expert are taken kDxGroup at a time, in groups aligned to
+// the expert's first row tile, column by column.  The tiles of a group that
+// read one column panel of W_e then run side by side on one XCD and share it
+// in its L2; groups of a fixed height over the concatenated rows straddle
+// experts, and each straddled expert's panel comes from HBM once per group.
+// Returns the expert of the tile (row tile mt, column tile tn).
+constexpr int kDxGroup = 8;
+__device__ __forceinline__ int dx_raster(const int32_t* mt_off, int E, int t, int nc, int* mt,
+                                         int* tn) {
+  const int m = t / nc;  // a row tile of the group that holds position t
+  const int e = find_expert(mt_off, E, m);
+  const int e0 = ld_table(mt_off, e);
+  const int g0 = e0 + (m - e0) / kDxGroup * kDxGroup;
+  const int gh = min(kDxGroup, ld_table(mt_off, e + 1) - g0);
+  const int rem = t - g0 * nc;
+  *mt = g0 + rem % gh;
+  *tn = rem / gh;
+  return e;
 }
 
 // ------------------------------------------------------------------ bf16
@@ -430,8 +452,7 @@ __device__ __forceinline__ Job make_job(const GemmPlan& P, int t) {
     j.cols = min(C::BN, a.d_in - j0);
   } else {
     int mt, tn;
-    raster(t, ld_table(a.mt_off, a.E), P.ntn_x, &mt, &tn);
-    const int e = find_expert(a.mt_off, a.E, mt);
+    const int e = dx_raster(a.mt_off, a.E, t, P.ntn_x, &mt, &tn);
     const int m0 = ld_table(a.offsets, e) + (mt - ld_table(a.mt_off, e)) * C::BM;
     const int rows = min(C::BM, min(ld_table(a.offsets, e + 1), a.max_rows) - m0);
     const int j0 = tn * C::BN;
