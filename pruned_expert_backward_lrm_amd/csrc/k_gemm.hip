@@ -591,20 +591,39 @@ __device__ __forceinline__ void mma_k32(f32x4 (&acc)[C::FM][C::FN], const uint16
 // one block per tile then is the hardware's greedy dispatch in that order (a
 // longest-first schedule), and persistent blocks deal the sorted tiles in
 // snake order (block b takes positions b, 2nbx - 1 - b, 2nbx + b, ...).
-// Host model on the skewed workloads, longest block over the ideal share:
-// 1.093 -> 1.062 (persistent, 65536 tokens) and 1.46 -> 1.13 (one block per
-// tile, GLM-4.5 shape).  Tiles inside a run keep their raster order.
+// Tiles inside a run keep their raster order.
+//
+// Heavy experts are striped: when one tile of expert e costs at least a
+// quarter of a CU's ideal load (c_e * 1024 >= per * sum of c) and an expert
+// has at least 8 tiles, its tiles are not part of the cut but dealt to the 8
+// XCDs in 8 contiguous stripes (the i-th heavy expert's stripe s goes to XCD
+// (s - i) mod 8, which spreads the longer stripes of a ragged split), and
+// the other experts' tiles are cut as above.  A contiguous cut would hand
+// whole shares to a heavy expert's long tiles (on the GLM-4.5 local-32
+// share, 42 tiles of 141 k-tiles for 32 CUs: 1.46x the ideal in any order).
+// Host model, longest CU over the ideal: 1.46 -> 1.03 (GLM-4.5 local-32
+// share), 1.13 -> 1.01 (Qwen3 SwiGLU); no expert is heavy on the 65536-token
+// SwiGLU and Qwen3 linear shapes (1.062 and 1.072, from longest first alone).
+// Stripes cost extra operand reads: each XCD reads the panels its stripe
+// needs.  With at least 8 tiles per expert, a heavy expert's cost exceeds
+// 8 / 1024 of the total, so at most 128 experts are heavy.
 //
 // One block (k_dw_plan; 256 threads up to 1024 experts, else 1024) writes
 // the schedule of a launch into the GEMM workspace after mt_off:
-//   [0..8]   share starts in the tile list (share x = [lo_x, lo_{x+1}))
+//   [0..8]   prefix of the share lengths in tiles
 //   [9..17]  first run of each share (runs of share x: [base_x, base_{x+1}))
-//   then three arrays of kPlanRuns(E) entries, in run order: the run's first
+//   then three arrays of plan_runs(E) entries, in run order: the run's first
 //   position inside its share, its expert, its first tile within the expert.
 constexpr int kStoreCost = 2;
 constexpr int kPlanHead = 18;
 constexpr int kPlanMaxE = 4096;
-__host__ __device__ constexpr int plan_runs(int E) { return E + 8; }
+constexpr int kHeavyDiv = 1024;  // heavy: c_e * kHeavyDiv >= per * sum of c
+constexpr int kPlanMaxHeavy = kHeavyDiv / 8;
+// runs: (share, expert) pairs of the cut (at most E + 7) plus 8 stripes per
+// heavy expert
+__host__ __device__ constexpr int plan_runs(int E) {
+  return E + 8 + 8 * (E < kPlanMaxHeavy ? E : kPlanMaxHeavy);
+}
 
 __device__ __forceinline__ int dw_cost(const GemmArgs& a, int e) {
   const int Me = max(0, min(a.offsets[e + 1], a.max_rows) - a.offsets[e]);
@@ -619,25 +638,47 @@ __global__ __launch_bounds__(NT) void k_dw_plan(GemmPlan P) {
   int32_t* plan = a.dw_plan;
   __shared__ int cum[kPlanMaxE + 1];  // exclusive prefix of the expert costs
   __shared__ int lds[NT / kWave + 1];
-  __shared__ int lo[9], base[9];
+  __shared__ int lo[9], base[9], ncut[8], len[8];
+  __shared__ int heavy[kPlanMaxHeavy];
   __shared__ int re[plan_runs(kPlanMaxE)], rf[plan_runs(kPlanMaxE)];
   __shared__ int rn[plan_runs(kPlanMaxE)], rc[plan_runs(kPlanMaxE)];
+  const int t = threadIdx.x;
+  // the total cost, then the heavy experts (in expert order), then the
+  // prefix of the costs with the heavy experts' left out
   block_scan_array<NT>(E, [&](int e) { return dw_cost(a, e); }, cum, lds);
   __syncthreads();
-  const int t = threadIdx.x;
+  const int64_t lim = (int64_t)per * cum[E];
+  __syncthreads();
+  auto is_heavy = [&](int e) {
+    return per >= 8 && (int64_t)dw_cost(a, e) * kHeavyDiv >= lim;
+  };
+  block_scan_array<NT>(E, [&](int e) { return is_heavy(e) ? 1 : 0; }, cum, lds);
+  __syncthreads();
+  const int nh = cum[E];
+  for (int e = t; e < E; e += NT)
+    if (cum[e + 1] > cum[e]) heavy[cum[e]] = e;
+  if (t < 8) len[t] = 0;
+  __syncthreads();
+  block_scan_array<NT>(E, [&](int e) { return is_heavy(e) ? 0 : dw_cost(a, e); }, cum, lds);
+  __syncthreads();
   if (t <= 8) {
-    // share start: the first tile whose start cost is >= total * t / 8
+    // cut start: the first tile whose start cost is >= total * t / 8 (a
+    // heavy expert's tiles cost nothing here and are skipped as runs)
     int v = t == 0 ? 0 : E * per;
     if (t > 0 && t < 8) {
-      const int64_t target = (int64_t)per * cum[E] * t / 8;
-      int l = 0, h = E;  // largest e < E with per * cum[e] <= target
-      while (h - l > 1) {
-        const int m = (l + h) >> 1;
-        if ((int64_t)per * cum[m] <= target) l = m; else h = m;
+      if (cum[E] == 0) {
+        v = 0;
+      } else {
+        const int64_t target = (int64_t)per * cum[E] * t / 8;
+        int l = 0, h = E;  // largest e < E with per * cum[e] <= target
+        while (h - l > 1) {
+          const int m = (l + h) >> 1;
+          if ((int64_t)per * cum[m] <= target) l = m; else h = m;
+        }
+        const int c = cum[l + 1] - cum[l];  // > 0: per * cum[l + 1] > target
+        const int64_t j = (target - (int64_t)per * cum[l] + c - 1) / c;
+        v = l * per + (int)min<int64_t>(j, per);
       }
-      const int c = cum[l + 1] - cum[l];
-      const int64_t j = (target - (int64_t)per * cum[l] + c - 1) / c;
-      v = l * per + (int)min<int64_t>(j, per);
     }
     lo[t] = v;
   }
@@ -646,30 +687,52 @@ __global__ __launch_bounds__(NT) void k_dw_plan(GemmPlan P) {
     int n = 0;
     for (int x = 0; x < 8; ++x) {
       base[x] = n;
-      if (lo[x + 1] > lo[x]) n += (lo[x + 1] - 1) / per - lo[x] / per + 1;
+      ncut[x] = lo[x + 1] > lo[x] ? (lo[x + 1] - 1) / per - lo[x] / per + 1 : 0;
+      n += ncut[x] + nh;
     }
     base[8] = n;
-    for (int x = 0; x <= 8; ++x) {
-      plan[x] = lo[x];
-      plan[9 + x] = base[x];
-    }
   }
   __syncthreads();
   const int nr = base[8];
-  // the runs in expert order: share x, expert e, tiles [a0, a1) of the list
+  // each share's runs: those of the cut in expert order (a heavy expert's
+  // with no tiles), then one stripe of every heavy expert
   for (int r = t; r < nr; r += NT) {
     int x = 0;
     while (base[x + 1] <= r) ++x;
-    const int e = lo[x] / per + (r - base[x]);
-    const int a0 = max(lo[x], e * per), a1 = min(lo[x + 1], (e + 1) * per);
-    re[r] = e;
-    rf[r] = a0 - e * per;
-    rn[r] = a1 - a0;
-    rc[r] = cum[e + 1] - cum[e];
+    const int i = r - base[x];
+    if (i < ncut[x]) {
+      const int e = lo[x] / per + i;
+      const int a0 = max(lo[x], e * per), a1 = min(lo[x + 1], (e + 1) * per);
+      const int c = cum[e + 1] - cum[e];  // 0: a heavy expert
+      re[r] = e;
+      rf[r] = a0 - e * per;
+      rn[r] = c > 0 ? a1 - a0 : 0;
+      rc[r] = c;
+    } else {
+      const int k = i - ncut[x];
+      const int e = heavy[k];
+      const int sx = (x + k) & 7;
+      const int f0 = per * sx / 8, f1 = per * (sx + 1) / 8;
+      re[r] = e;
+      rf[r] = f0;
+      rn[r] = f1 - f0;
+      rc[r] = dw_cost(a, e);
+    }
+    atomicAdd(&len[x], rn[r]);
   }
   __syncthreads();
-  // rank of each run inside its share (cost descending, then expert order)
-  // and its first position: the tiles of the runs ranked before it
+  if (t == 0) {
+    int n = 0;
+    for (int x = 0; x < 8; ++x) {
+      plan[x] = n;
+      n += len[x];
+      plan[9 + x] = base[x];
+    }
+    plan[8] = n;
+    plan[17] = base[8];
+  }
+  // rank of each run inside its share (cost descending, then run order) and
+  // its first position: the tiles of the runs ranked before it
   for (int r = t; r < nr; r += NT) {
     int x = 0;
     while (base[x + 1] <= r) ++x;

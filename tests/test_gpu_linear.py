@@ -361,6 +361,44 @@ def test_gemm_lds_dma_bit_exact(L, d_out, monkeypatch):
         assert rel_fro(dXp[a:b].numpy(), G64[a:b] @ O.f64(W[e].cpu())) < 1e-5
 
 
+@pytest.mark.parametrize("tile", ["L", "X"])
+@pytest.mark.parametrize("d_out", [512, 768])
+def test_dw_heavy_expert_stripes(L, d_out, tile, monkeypatch):
+    """dW tiles of heavy experts (one tile at least a quarter of a CU's ideal
+    load) are dealt to the 8 XCDs in stripes, the other experts' tiles in
+    equal-cost contiguous shares.  Four heavy experts among 100, 8 tiles per
+    expert (d_out 512: one tile per stripe) or 12 (d_out 768: stripes of 1 and
+    2 tiles), one block per tile (L) and persistent blocks (X): every expert's
+    dW against the fp64 product, outputs prefilled with NaN so that a tile
+    left out shows."""
+    monkeypatch.setenv("LRM_GEMM_TILE", tile)
+    d_in = 1024
+    rng = np.random.default_rng(11)
+    sizes = rng.integers(20, 41, 100)
+    sizes[[7, 50]] = 2500
+    sizes[[20, 81]] = 300
+    sizes[33] = 0
+    E = len(sizes)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M = int(offsets[-1])
+    say("dw heavy stripes", d_out, tile, M)
+    W = synth.normal((E, d_out, d_in), 0.02, torch.bfloat16, DEV, "stripe", 1)
+    Gp = synth.normal((M, d_out), 1.0, torch.bfloat16, DEV, "stripe", 2)
+    Xp = synth.normal((M, d_in), 1.0, torch.bfloat16, DEV, "stripe", 3)
+    off = torch.as_tensor(offsets, device=DEV)
+    dW = torch.full((E, d_out, d_in), float("nan"), device=DEV)
+    L.lrm_grouped_bwd(E, off, M, Gp, Xp, W, d_in, d_out, dW, None)
+    torch.cuda.synchronize()
+    dW = dW.cpu().numpy()
+    G64, X64 = Gp.double().cpu().numpy(), Xp.double().cpu().numpy()
+    for e in range(E):
+        a, b = offsets[e], offsets[e + 1]
+        if a == b:
+            assert not dW[e].any(), e
+            continue
+        assert rel_fro(dW[e], G64[a:b].T @ X64[a:b]) < 1e-5, e
+
+
 # ------------------------------------------------------------ fused call
 
 @pytest.mark.parametrize("x_rows,g_rows", [("token", "pair"), ("pair", "token")])
