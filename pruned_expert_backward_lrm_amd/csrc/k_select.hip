@@ -17,6 +17,7 @@
 //                     candidate order that keeps keys above the threshold and
 //                     the first (lowest-index) ties, and writes packed rows.
 // Scores are >= 0, so their fp32 bit patterns order like the values.
+#include <cstdlib>
 #include <type_traits>
 
 #include "common.h"
@@ -301,17 +302,13 @@ __global__ __launch_bounds__(64) void k_bucket_scatter(int N, int T, int E, int 
 // first slot, and it keeps the keys above the threshold and the first r
 // equal ones of the expert.  The round's slots are staged in LDS and
 // written out by consecutive lanes on consecutive candidates.
-__global__ __launch_bounds__(kSelThreads) void k_select(const int32_t* __restrict__ cand_off,
-                                                        const int32_t* __restrict__ offsets,
-                                                        const uint32_t* __restrict__ keys,
-                                                        const int32_t* __restrict__ cand,
-                                                        int32_t* __restrict__ pos,
-                                                        int32_t* __restrict__ kept, int limit) {
-  const int e = blockIdx.x;
-  const int c0 = min(cand_off[e], limit);
-  const int n = min(cand_off[e + 1], limit) - c0;
-  const int o = min(offsets[e], limit);
-  const int m = min(offsets[e + 1], limit) - o;
+//
+// select_expert: the workgroup's expert has candidates c0 .. c0 + n - 1 and
+// keeps m of them at packed slots o .. o + m - 1 (all clipped already).  Its
+// pointers are plain (no restrict): the one-launch selection below writes
+// keys and cand earlier in the same kernel.
+__device__ __forceinline__ void select_expert(int c0, int n, int o, int m, const uint32_t* keys,
+                                              const int32_t* cand, int32_t* pos, int32_t* kept) {
   const int tid = threadIdx.x;
   // the passes' histograms (4096 + 1024 bins), then a round's slots
   constexpr int kHist = kSelRunKeys * kSelThreads > 4096 + 1024 ? kSelRunKeys * kSelThreads
@@ -482,6 +479,171 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const int32_t* __restric
   }
 }
 
+__global__ __launch_bounds__(kSelThreads) void k_select(const int32_t* __restrict__ cand_off,
+                                                        const int32_t* __restrict__ offsets,
+                                                        const uint32_t* __restrict__ keys,
+                                                        const int32_t* __restrict__ cand,
+                                                        int32_t* __restrict__ pos,
+                                                        int32_t* __restrict__ kept, int limit) {
+  const int e = blockIdx.x;
+  const int c0 = min(cand_off[e], limit);
+  const int n = min(cand_off[e + 1], limit) - c0;
+  const int o = min(offsets[e], limit);
+  const int m = min(offsets[e + 1], limit) - o;
+  select_expert(c0, n, o, m, keys, cand, pos, kept);
+}
+
+// Selection of a small call in one launch, in place of the bucketing kernels
+// and k_select.  One workgroup per expert reads every pair's expert and token
+// (N <= kSmallSelN; E * N <= kSmallSelWork bounds the redundant reads, served
+// by L2), so each builds the whole expert histogram and the candidate and
+// kept offsets itself, with no wait on another workgroup.  It then writes its
+// own candidates in pair order with their keys and selects as k_select does.
+// Workgroup 0 also writes the offsets, the error word, the row-tile prefix,
+// the token offsets and pos = -1 for pairs with an index out of range.
+// Thread t reads pairs r * kSelThreads + t (rounds r, coalesced); a round's
+// candidates of the expert are ranked by one ballot per wave, and one block
+// scan over the ballots' counts, in (round, wave) order, gives each its slot.
+// Outputs are those of the bucketing path bit for bit.
+// Measured per call (Zipf routings): 18.7 against 25.7 us at 512 pairs, 23.0
+// against 29.2 at 8192 pairs over 128 experts, even at 16384, slower at 32768
+// (47 against 40: every workgroup reads every pair), hence the bound.
+constexpr int kSmallSelN = 8192;
+constexpr int64_t kSmallSelWork = 1 << 21;
+constexpr int kSmallSelE = 1024;
+constexpr int kSmallRounds = kSmallSelN / kSelThreads;  // <= 64: one bit each
+static_assert(kSmallRounds <= 64, "one bit per round in a 64-bit mask");
+
+bool select_one_launch_ok(int N, int E) {
+  const char* env = getenv("LRM_SELECT_ONE_LAUNCH");
+  if (env && env[0] == '0') return false;
+  return N <= kSmallSelN && E <= kSmallSelE && (int64_t)E * N <= kSmallSelWork;
+}
+
+struct SmallSelArgs {
+  int N, T, E;
+  const int32_t* token;
+  const int32_t* expert;
+  const int32_t* quota;  // device [E], or nullptr: qp when use_qp
+  const float* score;
+  int32_t* cand_off;
+  int32_t* offsets;
+  int32_t* cand;
+  uint32_t* keys;
+  int32_t* pos;
+  int32_t* kept;
+  uint32_t* err;
+  int32_t* tok_off;  // or nullptr
+  int32_t* mt_off;   // or nullptr
+  int mt_bm;
+  int64_t max_kept;
+  int limit;
+  int use_qp;
+  QuotaPack qp;
+};
+
+__global__ __launch_bounds__(kSelThreads) void k_select_small(SmallSelArgs a) {
+  constexpr int NW = kSelThreads / kWave;
+  __shared__ int cnt[kSmallSelE];     // candidates per expert
+  __shared__ int mcount[kSmallSelE];  // kept per expert (capped by the scan)
+  __shared__ int coff[kSmallSelE + 1], koff[kSmallSelE + 1];
+  __shared__ uint64_t bal[kSmallRounds * NW];
+  __shared__ int bal_off[kSmallRounds * NW + 1];
+  __shared__ int lds[NW + 1];
+  __shared__ uint32_t eor;
+  const int e = blockIdx.x, tid = threadIdx.x, w = tid >> 6, l = lane_id();
+  const int N = a.N, T = a.T, E = a.E;
+  for (int i = tid; i < E; i += kSelThreads) cnt[i] = 0;
+  if (tid == 0) eor = 0u;
+  __syncthreads();
+  const int R = (N + kSelThreads - 1) / kSelThreads;
+  const uint64_t lt = (l == 0) ? 0ull : (~0ull >> (64 - l));  // lanes below this one
+  uint64_t mine = 0;  // bit r: pair r * kSelThreads + tid is a candidate of e
+  uint32_t bad = 0;
+  // rounds in batches of kSmallBatch, every load of a batch issued before
+  // the first is used (a round's loads alone would wait one L2 latency each);
+  // the token order is checked by workgroup 0 only, the one that writes the
+  // error word
+  constexpr int kSmallBatch = 8;
+  for (int r0 = 0; r0 < R; r0 += kSmallBatch) {
+    int exv[kSmallBatch], tkv[kSmallBatch], tpv[kSmallBatch];
+#pragma unroll
+    for (int u = 0; u < kSmallBatch; ++u) {
+      const int p = (r0 + u) * kSelThreads + tid;
+      const bool in = r0 + u < R && p < N;
+      exv[u] = in ? a.expert[p] : -1;
+      tkv[u] = in ? a.token[p] : 0;
+      tpv[u] = (e == 0 && in && p > 0) ? a.token[p - 1] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kSmallBatch; ++u) {
+      const int r = r0 + u;
+      if (r >= R) break;  // uniform
+      const int p = r * kSelThreads + tid;
+      const bool in = p < N;
+      const int ex = exv[u], tk = tkv[u];
+      bool valid = false;
+      if (in) {
+        if (ex < 0 || ex >= E) bad |= kErrExpertRange;
+        if (tk < 0 || tk >= T) bad |= kErrTokenRange;
+        if (e == 0 && p > 0 && tpv[u] > tk) bad |= kErrTokenOrder;
+        valid = ex >= 0 && ex < E && tk >= 0 && tk < T;
+        if (valid) atomicAdd(&cnt[ex], 1);
+        if (e == 0) {
+          if (!valid) a.pos[p] = -1;
+          if (a.tok_off) token_offsets_at(p, N, T, a.token, a.tok_off);
+        }
+      }
+      const bool hit = valid && ex == e;
+      const uint64_t b = __ballot(hit);
+      if (l == 0) bal[r * NW + w] = b;
+      mine |= (uint64_t)(hit ? 1 : 0) << r;
+    }
+  }
+  if (e == 0 && tid == 0 && a.tok_off) token_offsets_at(N, N, T, a.token, a.tok_off);
+  if (bad) atomicOr(&eor, bad);
+  __syncthreads();
+  // quotas: device array, or by value, or keep all
+  for (int i = tid; i < E; i += kSelThreads) {
+    const int q = a.quota ? max(a.quota[i], 0) : (a.use_qp ? max(a.qp.q[i], 0) : 0x7fffffff);
+    mcount[i] = min(q, cnt[i]);
+  }
+  block_scan_array<kSelThreads>(E, [&](int i) { return cnt[i]; }, coff, lds);
+  __syncthreads();
+  const bool over = scan_kept_capped(E, mcount, koff, a.max_kept, lds);
+  if (e == 0 && a.mt_off) {
+    block_scan_array<kSelThreads>(
+        E, [&](int i) { return (mcount[i] + a.mt_bm - 1) / a.mt_bm; }, a.mt_off, lds);
+  }
+  // slots of the expert's candidates: ballot counts in (round, wave) order
+  block_scan_array<kSelThreads>(R * NW, [&](int i) { return __popcll(bal[i]); }, bal_off, lds);
+  __syncthreads();
+  const int limit = a.limit;
+  const int c0 = min(coff[e], limit);
+  const int n = min(coff[e + 1], limit) - c0;
+  const int o = min(koff[e], limit);
+  const int m = min(koff[e + 1], limit) - o;
+  for (uint64_t mm = mine; mm; mm &= mm - 1) {
+    const int r = __builtin_ctzll(mm);
+    const int p = r * kSelThreads + tid;
+    const int idx = bal_off[r * NW + w] + __popcll(bal[r * NW + w] & lt);
+    if (idx < n) {
+      a.cand[c0 + idx] = p;
+      a.keys[c0 + idx] = __float_as_uint(a.score[p]);
+    }
+  }
+  if (e == 0) {
+    for (int i = tid; i <= E; i += kSelThreads) {
+      a.cand_off[i] = coff[i];
+      a.offsets[i] = koff[i];
+    }
+    if (tid == 0) a.err[0] = eor | (over ? kErrCapacity : 0u);
+  }
+  // the candidates written above are read back by other threads of the block
+  __syncthreads();
+  select_expert(c0, n, o, m, a.keys, a.cand, a.pos, a.kept);
+}
+
 // tok_off[t] = first pair index whose token is >= t, for t in [0, T].
 __global__ __launch_bounds__(256) void k_token_offsets(int N, int T,
                                                        const int32_t* __restrict__ token,
@@ -552,6 +714,24 @@ hipError_t launch_select(int E, const int32_t* cand_off, const int32_t* offsets,
                          int limit, hipStream_t s) {
   LRM_LAUNCH(E, kSelThreads, 0, s, k_select)(cand_off, offsets, keys, cand, pos, kept,
                                              limit < 0 ? 0 : limit);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_one(const BucketArgs& b, int32_t* kept, int limit, hipStream_t s) {
+  if (!select_one_launch_ok(b.N, b.E) || b.keep_all || !b.score || !b.keys) return hipErrorInvalidValue;
+  if (b.mt_off && b.mt_bm < 1) return hipErrorInvalidValue;
+  const bool use_qp = !b.quota && b.qpack;
+  if (use_qp && b.E > kQuotaPackMax) return hipErrorInvalidValue;
+  SmallSelArgs a{};
+  a.N = b.N; a.T = b.T; a.E = b.E; a.token = b.token; a.expert = b.expert;
+  a.quota = b.quota; a.score = b.score;
+  a.cand_off = b.cand_off; a.offsets = b.offsets; a.cand = b.cand; a.keys = b.keys;
+  a.pos = b.pos; a.kept = kept; a.err = b.err; a.tok_off = b.tok_off;
+  a.mt_off = b.mt_off; a.mt_bm = b.mt_bm; a.max_kept = b.max_kept;
+  a.limit = limit < 0 ? 0 : limit;
+  a.use_qp = use_qp ? 1 : 0;
+  if (use_qp) a.qp = *b.qpack;
+  LRM_LAUNCH(b.E, kSelThreads, 0, s, k_select_small)(a);
   return hipGetLastError();
 }
 

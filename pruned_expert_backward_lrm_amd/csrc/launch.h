@@ -83,6 +83,12 @@ hipError_t launch_select(int E, const int32_t* cand_off, const int32_t* offsets,
 // quota: device [E]; or qpack (host, by value, E <= kQuotaPackMax) when quota
 // is nullptr; both nullptr: keep all.  More than cap kept rows (cap >= 0) set
 // kErrCapacity in err[0].
+// The selection of a small call in one launch (the bucketing kernels and
+// launch_select together), keep_all == 0 and keys gathered: same outputs.
+// select_one_launch_ok(N, E) says whether it applies (LRM_SELECT_ONE_LAUNCH=0
+// turns it off).
+bool select_one_launch_ok(int N, int E);
+hipError_t launch_select_one(const BucketArgs& b, int32_t* kept, int limit, hipStream_t s);
 hipError_t launch_kept_offsets(int E, const int32_t* cand_off, const int32_t* quota,
                                const QuotaPack* qpack, int32_t* offsets, uint32_t* err,
                                int64_t cap, hipStream_t s);

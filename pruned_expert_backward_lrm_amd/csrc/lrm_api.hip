@@ -216,6 +216,10 @@ lrm_status run_select(const lrm_pairs* p, const float* score, const int32_t* quo
   b.keys = keep_all ? nullptr : w.keys;
   b.pos = pos; b.keep_all = keep_all; b.err = w.err; b.blkerr = w.blkerr; b.tok_off = tok_off;
   b.mt_off = mt_off; b.mt_bm = mt_bm; b.max_kept = max_kept;
+  if (!keep_all && select_one_launch_ok(p->N, p->E)) {
+    LRM_TRY_HIP(launch_select_one(b, kept, p->N, s));
+    return LRM_OK;
+  }
   LRM_TRY_HIP(launch_bucket(b, s));
   if (!keep_all)
     LRM_TRY_HIP(launch_select(p->E, w.cand_off, offsets, w.keys, w.cand, pos, kept, p->N, s));

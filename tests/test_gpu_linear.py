@@ -137,6 +137,61 @@ def test_select_large_expert(L):
     check_packing(pos, offsets, r.expert, E)
 
 
+@pytest.mark.parametrize("case", ["tiny_fp32", "ties_8192", "wide_1024", "device_quota",
+                                  "bad_indices"])
+def test_select_one_launch_matches_bucketing(L, case, monkeypatch):
+    """The one-launch selection of small calls (one workgroup per expert that
+    histograms every pair itself) against the bucketing kernels followed by
+    the per-expert select (LRM_SELECT_ONE_LAUNCH=0): pos, kept offsets, the
+    kept list and the error word bit for bit.  Cases: the tiny fp32 workload's
+    routing and quotas; 8192 pairs (the largest one-launch call) with scores
+    from five integers (runs of ties); 1024 experts (host quotas copied, not
+    passed by value) with quotas of 0, all and more than all; quotas on the
+    device; expert ids out of range and tokens out of order (flagged, pos -1)."""
+    rng = np.random.default_rng(21)
+    flags = 0
+    if case == "tiny_fp32":
+        spec = synth.CONFIGS[1]
+        r = synth.make_routing(spec["T"], spec["E"], spec["k"], spec["zipf"], "cfg", 1)
+        s = (rng.standard_normal(r.N) ** 2).astype(np.float32)
+        q = np.asarray(synth._quotas(1, r, None)["quota"], np.int64)
+    else:
+        N, E = {"ties_8192": (8192, 64), "wide_1024": (2048, 1024),
+                "device_quota": (4096, 256), "bad_indices": (4096, 16)}[case]
+        expert = np.minimum(rng.zipf(1.3, N) - 1, E - 1).astype(np.int32)
+        token = np.sort(rng.integers(0, N // 4, N)).astype(np.int32)
+        if case == "bad_indices":
+            expert[rng.integers(0, N, 40)] = E
+            expert[rng.integers(0, N, 40)] = -1
+            token[100], token[101] = token[101] + 1, token[100]
+        r = synth.Routing(N // 4, E, 1, expert, token, rng.random(N).astype(np.float32),
+                          np.bincount(expert[(expert >= 0) & (expert < E)], minlength=E), {})
+        if case == "ties_8192":
+            s = rng.integers(0, 5, N).astype(np.float32)
+        else:
+            s = (rng.standard_normal(N) ** 2).astype(np.float32)
+        c = r.counts
+        q = (c // 3 + (np.arange(E) % 3)).astype(np.int64)
+        if case == "wide_1024":
+            q[::7] = 0
+            q[1::7] = c[1::7]
+            q[2::7] = c[2::7] + 9
+    quota = q
+    if case == "device_quota":
+        flags = L.LRM_QUOTA_ON_DEVICE
+        quota = torch.as_tensor(q.astype(np.int32), device=DEV)
+    res = {}
+    for one in ("1", "0"):
+        monkeypatch.setenv("LRM_SELECT_ONE_LAUNCH", one)
+        say("select one launch", case, one, r.N, r.E)
+        pos, offsets, kept, ws = _select(L, r, s, quota, flags)
+        err = int(ws[:4].cpu().numpy().view(np.uint32)[0])
+        res[one] = (pos, offsets, kept[: max(int(offsets[-1]), 0)], err)
+    for a, b, name in zip(res["1"], res["0"], ("pos", "offsets", "kept", "err")):
+        assert np.array_equal(np.asarray(a), np.asarray(b)), name
+    assert (res["1"][3] != 0) == (case == "bad_indices")
+
+
 @pytest.mark.parametrize("ties", [False, True])
 def test_select_run_boundaries(L, ties):
     """Experts at the per-expert selection's size boundaries: 8192 candidates
