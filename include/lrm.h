@@ -49,6 +49,13 @@
  *     (no floating-point atomics; all reductions in a fixed order).
  *   - No exception crosses this interface.  Functions are re-entrant when
  *     concurrent calls use distinct workspaces and outputs.
+ *   - Environment variables read at each call, for benchmarking and testing
+ *     (the defaults are the tuned paths): LRM_GEMM_TILE=S|M|L|X forces one
+ *     bf16 tile configuration of the grouped GEMM; LRM_GEMM_DMA=2|4 runs the
+ *     256x256 tiles with operands loaded straight into LDS (bit-identical
+ *     results, slower on the measured shapes); LRM_SELECT_ONE_LAUNCH=0 keeps
+ *     calls of up to 8192 pairs on the bucketing kernels (bit-identical
+ *     results).  Workspace sizes do not depend on them.
  */
 #ifndef LRM_H_
 #define LRM_H_
