@@ -168,9 +168,12 @@ __device__ __forceinline__ rsrc_t make_rsrc(const char* base, int64_t nbytes) {
   const int n = nbytes <= 0 ? 0 : (nbytes > 0x7ffffff0ll ? 0x7ffffff0 : (int)nbytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, n, kRsrcWord3);
 }
+// AUX: cache policy of the load (0 default, kStreamAux non-temporal)
+template <int AUX = 0>
 __device__ __forceinline__ u32x4 bload(rsrc_t r, int off) {
-  return (u32x4)__builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return (u32x4)__builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
 }
+constexpr int kStreamAux = 2;  // the nt bit
 
 // Row panel, k contiguous (dX: Gp rows of one expert): row r at
 // base + r*ld, k-tile [k0, k0+64).  Bytes valid: rows_valid rows.
@@ -215,7 +218,8 @@ __device__ __forceinline__ uint32_t pick_half(uint32_t x, uint32_t y, int hi) {
 // (k, n) at base + k*ld + n, columns [n0, n0+R), rows k < kend valid.  The
 // tile is cut into 4(k) x 8(n) blocks, each read with four 16-byte loads and
 // transposed in registers into eight 8-byte LDS stores (rows n, 4 k each).
-template <int R, int NT>
+// AUX: cache policy of the loads.
+template <int R, int NT, int AUX = 0>
 struct TransTile {
   static constexpr int NB = 16 * (R / 8);  // blocks per tile
   static constexpr int Q = (NB + NT - 1) / NT;
@@ -246,7 +250,7 @@ struct TransTile {
 #pragma unroll
     for (int q = 0; q < Q; ++q)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[q][r] = bload(rs, off[q] + r * row);
+      for (int r = 0; r < 4; ++r) v[q][r] = bload<AUX>(rs, off[q] + r * row);
   }
   __device__ __forceinline__ void store(uint16_t* lds) const {
 #pragma unroll
@@ -371,12 +375,18 @@ __device__ __forceinline__ TileSrc pick_seg(const TileSrc& x, const TileSrc& y, 
 }
 
 // GB: the B panel gathered (GatherTile) instead of read from packed rows.
+// dX tiles of 64 rows serve experts that keep few rows: each W_e column panel
+// is then read by about one row tile, so its loads stream past the caches
+// (measured on the Qwen3 linear shape: dX 140 -> 118 us; on 256-row tiles,
+// whose W panels the expert's other row tiles read again, the same bit costs
+// 12-24%).
 template <class C, bool A_DIRECT, bool GB = false>
 struct Stage {
+  static constexpr int BAUX = (A_DIRECT && C::BM <= 64) ? kStreamAux : 0;
   using ATile = typename std::conditional<A_DIRECT, DirectTile<C::BM, C::NT>,
                                           TransTile<C::BM, C::NT>>::type;
   using BTile = typename std::conditional<GB, GatherTile<C::BN, C::NT>,
-                                          TransTile<C::BN, C::NT>>::type;
+                                          TransTile<C::BN, C::NT, BAUX>>::type;
   ATile A;
   BTile B;
   int64_t lda, ldb, b_rows;
