@@ -243,14 +243,23 @@ struct TransTile {
       off[q] = b < NB ? (int)((kg * 4 * ld + ng * 8) * 2) : 0x7ffffff0;
     }
   }
-  __device__ __forceinline__ void load(const char* base, int64_t ld, int k0, int kend, int n0) {
+  // stream: the loads take the AUX policy (otherwise the default one)
+  __device__ __forceinline__ void load(const char* base, int64_t ld, int k0, int kend, int n0,
+                                       bool stream = false) {
     const rsrc_t rs = make_rsrc(base + ((int64_t)k0 * ld + n0) * 2,
                                 (int64_t)(kend - k0) * ld * 2 - (int64_t)n0 * 2);
     const int row = (int)(ld * 2);
+    if (AUX != 0 && stream) {
 #pragma unroll
-    for (int q = 0; q < Q; ++q)
+      for (int q = 0; q < Q; ++q)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[q][r] = bload<AUX>(rs, off[q] + r * row);
+        for (int r = 0; r < 4; ++r) v[q][r] = bload<AUX>(rs, off[q] + r * row);
+    } else {
+#pragma unroll
+      for (int q = 0; q < Q; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[q][r] = bload<0>(rs, off[q] + r * row);
+    }
   }
   __device__ __forceinline__ void store(uint16_t* lds) const {
 #pragma unroll
@@ -359,6 +368,7 @@ struct TileSrc {
   int a_n0, b_n0;    // transposed panels: first column of the tile
   int K;             // k extent (direct: columns of A; transposed: valid rows)
   const int32_t* brow; const float* bw;  // gathered B: row map of the expert's rows
+  int stream;  // dX: the expert has one row tile, its W panel is read once
 };
 
 __device__ __forceinline__ TileSrc pick_seg(const TileSrc& x, const TileSrc& y, bool first) {
@@ -371,15 +381,17 @@ __device__ __forceinline__ TileSrc pick_seg(const TileSrc& x, const TileSrc& y, 
   r.K = first ? x.K : y.K;
   r.brow = first ? x.brow : y.brow;
   r.bw = first ? x.bw : y.bw;
+  r.stream = first ? x.stream : y.stream;
   return r;
 }
 
 // GB: the B panel gathered (GatherTile) instead of read from packed rows.
-// dX tiles of 64 rows serve experts that keep few rows: each W_e column panel
-// is then read by about one row tile, so its loads stream past the caches
-// (measured on the Qwen3 linear shape: dX 140 -> 118 us; on 256-row tiles,
-// whose W panels the expert's other row tiles read again, the same bit costs
-// 12-24%).
+// dX tiles of 64 rows serve experts that keep few rows: when an expert has a
+// single row tile, each W_e column panel is read once, so its loads stream
+// past the caches (measured on the Qwen3 linear shape: dX 140 -> 120 us).
+// W panels that other row tiles of the expert read again keep the default
+// policy: streamed, they cost 12% at half the rows kept, and 12-24% on
+// 256-row tiles.
 template <class C, bool A_DIRECT, bool GB = false>
 struct Stage {
   static constexpr int BAUX = (A_DIRECT && C::BM <= 64) ? kStreamAux : 0;
@@ -405,7 +417,7 @@ struct Stage {
     if constexpr (GB)
       B.load(s.b, ldb, b_rows, s.b_n0);
     else
-      B.load(s.b, ldb, k0, s.K, s.b_n0);
+      B.load(s.b, ldb, k0, s.K, s.b_n0, s.stream);
   }
   // gathered B: the row map of the load after this one
   __device__ __forceinline__ void prefetch(const TileSrc& s, int k0) {
@@ -455,6 +467,7 @@ __device__ __forceinline__ Job make_job(const GemmPlan& P, int t) {
     }
     j.s0.a_rows_valid = 0; j.s0.a_n0 = i0; j.s0.b_n0 = j0;
     j.s0.K = Me;
+    j.s0.stream = 0;
     j.s1 = j.s0;
     j.nk0 = j.nk = (Me + C::BK - 1) / C::BK;
     j.C = a.dW + (int64_t)e * a.d_out * a.d_in + (int64_t)i0 * a.d_in + j0;
@@ -470,6 +483,7 @@ __device__ __forceinline__ Job make_job(const GemmPlan& P, int t) {
     j.s0.b = (const char*)a.W + (int64_t)e * a.w_stride * 2;
     j.s0.a_rows_valid = rows; j.s0.a_n0 = 0; j.s0.b_n0 = j0;
     j.s0.K = a.d_out;
+    j.s0.stream = ld_table(a.mt_off, e + 1) - ld_table(a.mt_off, e) <= 1;
     j.s0.brow = nullptr;
     j.s0.bw = nullptr;
     j.s1 = j.s0;
