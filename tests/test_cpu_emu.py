@@ -6,10 +6,11 @@ access of a kernel or of the host code aborts the run; the outputs must pass
 the same oracle checks as the GPU parity tests.  Runs without a GPU.
 
 Every lane is an OS thread and every wave collective two 64-thread barriers,
-so a case takes 30-130 s.  The default run keeps three: the tiny fp32
+so a case takes 30-130 s.  The default run keeps four: the tiny fp32
 workload (every step, the fp32 GEMM), the bf16 grouped GEMM in its 256x256
-tiles, and the same tiles on the LDS-DMA kernels; LRM_EMU_FULL=1 runs all of
-them (about 25 minutes on 8 cores).
+tiles, the same tiles on the LDS-DMA kernels, and the dW schedule with its
+tiles striped over the XCDs; LRM_EMU_FULL=1 runs all of them (about 28
+minutes on 8 cores).
 """
 
 from __future__ import annotations
@@ -206,6 +207,19 @@ def test_emu_gemm_lds_dma(driver, tmp_path, dma):
         ref = run_emu(driver, tmp_path, p, env_extra={"LRM_GEMM_TILE": "L", "LRM_GEMM_DMA": "0"})
         for k in ("dW", "dX"):
             assert torch.equal(ref[k], got[k]), k
+
+
+@pytest.mark.parametrize("tile", ["L", pytest.param("X", marks=extended)])
+def test_emu_dw_heavy_stripes(driver, tmp_path, tile):
+    """The dW schedule with heavy experts striped over the XCDs: 8 tiles per
+    expert (512 x 1024 outputs of 256 x 256).  The total work is small, so
+    every expert (an empty one included) counts as heavy and all tiles go
+    out in stripes, past runs of the equal-cost cut that hold no tiles; one
+    block per tile (L) and persistent blocks (X), under AddressSanitizer and
+    judged against the oracle.  (A mix of heavy and light experts needs more
+    work than the emulation affords; the GPU tests cover it.)"""
+    p = synth.make_linear(240, 6, 1, 1024, 512, dtype="bf16", seed=12, zipf=1.8)
+    judge_linear(p, run_emu(driver, tmp_path, p, env_extra={"LRM_GEMM_TILE": tile}))
 
 
 @extended
