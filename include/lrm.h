@@ -420,8 +420,14 @@ typedef struct lrm_outputs {
   float* dH;
 } lrm_outputs;
 
-/* The whole pruned expert backward of one layer call, all steps enqueued on
- * one stream with no device->host synchronisation:
+/* The whole pruned expert backward of one layer call (the page "LRMoE
+ * урезает обратный проход MoE ...", section "Что делает LRMoE: полный прямой
+ * проход, обрезанный обратный": quotas fixed before the backward, bullet
+ * "Квоты до вычислений"; scoring and selection, bullet "Отбор по метрике
+ * LRM"; packing, variable-size GEMMs and the return to the original layout,
+ * bullet "Физическое уплотнение"; the SwiGLU order down -> gate/up is the
+ * reading stated at the top of this header), all steps enqueued on one
+ * stream with no device->host synchronisation:
  *   LINEAR: score -> select -> compact -> grouped GEMM (dW, dXp) -> unpermute.
  *   SWIGLU: down score -> select -> compact (g, w*h) -> grouped GEMM
  *           (dW_down, u = W_down^T g) -> SwiGLU backward ga = u*b*silu'(a),
