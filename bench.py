@@ -794,8 +794,8 @@ def main():
         record_counters(a.record_counters, a.config, a.variant)
         return
     if a.gpus != 1:
-        log("bench.py: this build runs on exactly one GPU (one GPU's share of the experts); "
-            "--gpus must be 1")
+        log("bench.py: the library runs one GPU's share of the experts on one GPU "
+            "(the collectives across GPUs are not part of it); --gpus must be 1")
         sys.exit(2)
     from pruned_expert_backward_lrm_amd import lrm as L
     from pruned_expert_backward_lrm_amd import synth
