@@ -138,10 +138,12 @@ def workload_name(spec, T, E, k, shape, variant=None):
     return f"{spec['name']}{'-' + variant if variant else ''}: {shape} E={E} top-{k} zipf={spec['zipf']}"
 
 
-def gemm_roles(kind, pass_through):
+def gemm_roles(kind, pass_through, fused=False):
     """The grouped-GEMM launches of one fused call, in launch order."""
     if kind == "linear":
         return ["gemm_dW", "gemm_dX"]
+    if fused:
+        return ["gemm_down_dW", "gemm_down_dX", "gemm_gateup_dW", "gemm_gateup_dX"]
     if pass_through:
         return ["gemm_down_dW", "gemm_down_dX", "gemm_gate_dW", "gemm_gate_dX", "gemm_up_dW"]
     return ["gemm_down_dW", "gemm_down_dX", "gemm_gate_dW", "gemm_gate_dX", "gemm_up_dW",
@@ -152,6 +154,14 @@ def glu_pass_through(p):
     """The gate/up selections keep every down-kept row (one shared dX launch)."""
     return bool(np.all(np.asarray(p["quota_gate"]) >= np.asarray(p["quota_down"]))
                 and np.all(np.asarray(p["quota_up"]) >= np.asarray(p["quota_down"])))
+
+
+def glu_gate_up_fused(dtype, I, pass_through, gather=False):
+    """One launch computes both gate/up weight gradients: pass-through, bf16
+    inputs, I a multiple of 64, packed w x (no gathering loaders), unless
+    LRM_FUSE_GATE_UP=0."""
+    return (pass_through and dtype == "bf16" and I % 64 == 0 and not gather
+            and not os.environ.get("LRM_FUSE_GATE_UP", "1").startswith("0"))
 
 
 def workload_of(cfg, variant=None):
@@ -167,19 +177,21 @@ def workload_of(cfg, variant=None):
         shape = f"T={r.T} d_in={spec['d_in']} d_out={spec['d_out']}"
         Me = np.minimum(q["quota"], r.counts).astype(np.int64)
         work = gemm_launch_work("linear", r.E, b, 4, Me, d_in=spec["d_in"], d_out=spec["d_out"])
-        return workload_name(spec, r.T, r.E, r.k, shape, variant), work, True
+        return workload_name(spec, r.T, r.E, r.k, shape, variant), work, gemm_roles("linear", True)
     shape = f"T={r.T} H={spec['H']} I={spec['I']}"
     Md = np.minimum(q["quota_down"], r.counts).astype(np.int64)
     Mg = np.minimum(q["quota_gate"], Md)
     Mu = np.minimum(q["quota_up"], Md)
     pt = glu_pass_through(q)
+    fused = glu_gate_up_fused(spec["dtype"], spec["I"], pt)
     work = gemm_launch_work("swiglu", r.E, b, 4, Md, Mg, Mu, H=spec["H"], I=spec["I"],
-                            pass_through=pt)
-    return workload_name(spec, r.T, r.E, r.k, shape, variant), work, pt
+                            pass_through=pt, fused=fused)
+    return (workload_name(spec, r.T, r.E, r.k, shape, variant), work,
+            gemm_roles("swiglu", pt, fused))
 
 
 def gemm_launch_work(kind, E, b, wb, Md, Mg=None, Mu=None, d_in=0, d_out=0, H=0, I=0,
-                     pass_through=True):
+                     pass_through=True, fused=False):
     """Algorithmic bytes and flops of each grouped-GEMM launch of one call.
     A dW launch writes every expert's dW (wb bytes an element) and reads its
     packed operands once; a dX launch reads W of the experts that kept rows
@@ -196,8 +208,12 @@ def gemm_launch_work(kind, E, b, wb, Md, Mg=None, Mu=None, d_in=0, d_out=0, H=0,
 
     if kind == "linear":
         return {"gemm_dW": dw(Md, d_out, d_in), "gemm_dX": dx(Md, d_out, d_in)}
-    w = {"gemm_down_dW": dw(Md, H, I), "gemm_down_dX": dx(Md, H, I),
-         "gemm_gate_dW": dw(Mg, I, H), "gemm_up_dW": dw(Mu, I, H)}
+    w = {"gemm_down_dW": dw(Md, H, I), "gemm_down_dX": dx(Md, H, I)}
+    if fused:  # both weight gradients in one launch (2I rows), then both dX terms
+        w["gemm_gateup_dW"] = dw(Md, 2 * I, H)
+        w["gemm_gateup_dX"] = dx(Md, I, H, nseg=2)
+        return w
+    w.update({"gemm_gate_dW": dw(Mg, I, H), "gemm_up_dW": dw(Mu, I, H)})
     if pass_through:
         w["gemm_gate_dX"] = dx(Md, I, H, nseg=2)   # gate and up in one launch, K = 2I
     else:
@@ -232,9 +248,7 @@ def summarize_counters(dirs, cfg, variant=None):
     import csv
     import glob
 
-    from pruned_expert_backward_lrm_amd import synth
-    workload, work, pt = workload_of(cfg, variant)
-    roles = gemm_roles(synth.CONFIGS[cfg]["kind"], pt)
+    workload, work, roles = workload_of(cfg, variant)
     mean = {role: {} for role in roles}
     names = {}
     for d in dirs:
@@ -307,9 +321,7 @@ def record_counters(dirs, cfg, variant=None):
     import csv
     import glob
 
-    workload, work, pt = workload_of(cfg, variant)
-    from pruned_expert_backward_lrm_amd import synth
-    roles = gemm_roles(synth.CONFIGS[cfg]["kind"], pt)
+    workload, work, roles = workload_of(cfg, variant)
     counters = ["FETCH_SIZE", "WRITE_SIZE", "MfmaUtil"][:len(dirs)]
     per = {role: {} for role in roles}
     names, scale = {}, {}
@@ -390,9 +402,7 @@ def summarize_trace(d, cfg, steps, warmup, variant=None):
     import csv
     import glob
 
-    from pruned_expert_backward_lrm_amd import synth
-    workload, work, pt = workload_of(cfg, variant)
-    roles = gemm_roles(synth.CONFIGS[cfg]["kind"], pt)
+    workload, work, roles = workload_of(cfg, variant)
     trace = sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True))
     stats = sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True))
     if not trace:
@@ -508,11 +518,17 @@ class Workload:
                             offsets_gate=torch.empty(r.E + 1, **i32),
                             offsets_up=torch.empty(r.E + 1, **i32))
             self.pass_through = glu_pass_through(p)
+            self.fused = glu_gate_up_fused(p["dtype"], I, self.pass_through, gather)
+            # one span per pair of consecutive boundaries; None: boundaries that
+            # coincide (the fused gate/up launches leave two such spans)
+            gu = (["gemm_gateup_dW", "gemm_gateup_dX", None, None] if self.fused else
+                  ["gemm_gate_dW", "gemm_gate_dX", "gemm_up_dW", "gemm_up_dX"])
             self.stages = ["score_down", "select_down", "compact_down", "gemm_down_dW",
                            "gemm_down_dX", "glu_bwd", "select_gate_up", "compact_gate_up",
-                           "gemm_gate_dW", "gemm_gate_dX", "gemm_up_dW", "gemm_up_dX",
-                           "unpermute"]
-        self.gemm_roles = gemm_roles(self.kind, self.pass_through)
+                           *gu, "unpermute"]
+        if self.kind == "linear":
+            self.fused = False
+        self.gemm_roles = gemm_roles(self.kind, self.pass_through, self.fused)
         self.out["offsets"] = torch.empty(r.E + 1, **i32)
         u8 = dict(dtype=torch.uint8, device=dev)
         self.ws = torch.empty(L.lrm_workspace_size(self.pb), **u8)
@@ -579,7 +595,7 @@ class Workload:
             "unpermute": dict(bytes=M * H * 4 * (1 if self.pass_through else 2) + T * H * 4),
         }
         w.update(gemm_launch_work("swiglu", E, b, wb, Md, Mg, Mu, H=H, I=I,
-                                  pass_through=self.pass_through))
+                                  pass_through=self.pass_through, fused=self.fused))
         return w
 
 
@@ -602,7 +618,7 @@ def time_fused(W, steps, warmup):
     torch.cuda.synchronize()
     wall_ev = (time.perf_counter() - t0) / steps
     per = {name: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)]))
-           for i, name in enumerate(W.stages)}
+           for i, name in enumerate(W.stages) if name is not None}
     return wall, per, wall_ev
 
 
@@ -837,7 +853,7 @@ def main():
     roles = W.gemm_roles
     flops = sum(work[s]["flops"] for s in roles)
     gbytes = sum(work[s]["bytes"] for s in roles)
-    gemm_stages = [s for s in W.stages if s.startswith("gemm_")]
+    gemm_stages = [s for s in per if s.startswith("gemm_")]
     t_g = sum(per[s] for s in gemm_stages) * 1e-3
     ai = flops / gbytes
     peak_tf = PEAK_TFLOPS[p["dtype"]]
@@ -878,10 +894,10 @@ def main():
     roof["algorithmic_flops"] = kd["flops"]
     roof["algorithmic_bytes"] = kd["bytes"]
     roof["launch_ms"] = round(per[dom], 4)
-    mem_stages = [s for s in W.stages if not s.startswith("gemm_") and s in work]
+    mem_stages = [s for s in per if not s.startswith("gemm_") and s in work]
     log("bench: measuring device-copy bandwidth")
     cgbs = copy_gbs(dev)
-    sc = [s for s in W.stages if s.startswith("score") or s.startswith("compact")]
+    sc = [s for s in per if s.startswith("score") or s.startswith("compact")]
     gbs_of = lambda s: work[s]["bytes"] / (per[s] * 1e-3) / 1e9  # noqa: E731
     line = {
         "metric": METRIC,

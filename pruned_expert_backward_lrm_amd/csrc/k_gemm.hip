@@ -440,10 +440,16 @@ struct Job {
   TileSrc s0, s1;
   int nk0, nk;   // k-tiles of segment 0, of both segments
   float* C;
+  // split dW: tile rows from split on go to C2 (row r of the tile at C2 +
+  // r * d_in); split >= the tile height: one output
+  float* C2;
+  int split;
   int rows, cols;  // valid output rows and columns (rows <= 0: no output)
 };
 
-template <class C, bool DX>
+// SPLIT: the dW launch writes two outputs (GemmArgs::dw_split); a template
+// parameter, so that the other kernels carry none of its state.
+template <class C, bool DX, bool SPLIT = false>
 __device__ __forceinline__ Job make_job(const GemmPlan& P, int t) {
   const GemmArgs& a = P.a;
   Job j;
@@ -470,7 +476,18 @@ __device__ __forceinline__ Job make_job(const GemmPlan& P, int t) {
     j.s0.stream = 0;
     j.s1 = j.s0;
     j.nk0 = j.nk = (Me + C::BK - 1) / C::BK;
-    j.C = a.dW + (int64_t)e * a.d_out * a.d_in + (int64_t)i0 * a.d_in + j0;
+    if constexpr (SPLIT) {
+      // rows [0, sp) of the expert's dW in dW, rows [sp, d_out) in dW2; the
+      // pointer of a part this tile does not reach is never written through
+      const int sp = a.dw_split;
+      j.C = a.dW + (int64_t)e * sp * a.d_in + (int64_t)i0 * a.d_in + j0;
+      j.C2 = a.dW2 + (int64_t)e * (a.d_out - sp) * a.d_in + (int64_t)(i0 - sp) * a.d_in + j0;
+      j.split = sp - i0;
+    } else {
+      j.C = a.dW + (int64_t)e * a.d_out * a.d_in + (int64_t)i0 * a.d_in + j0;
+      j.C2 = j.C;
+      j.split = C::BM;
+    }
     j.rows = min(C::BM, a.d_out - i0);
     j.cols = min(C::BN, a.d_in - j0);
   } else {
@@ -479,7 +496,8 @@ __device__ __forceinline__ Job make_job(const GemmPlan& P, int t) {
     const int m0 = ld_table(a.offsets, e) + (mt - ld_table(a.mt_off, e)) * C::BM;
     const int rows = min(C::BM, min(ld_table(a.offsets, e + 1), a.max_rows) - m0);
     const int j0 = tn * C::BN;
-    j.s0.a = (const char*)a.Gp + (int64_t)m0 * a.d_out * 2;
+    const int64_t lda = a.lda > 0 ? a.lda : a.d_out;
+    j.s0.a = (const char*)a.Gp + m0 * lda * 2;
     j.s0.b = (const char*)a.W + (int64_t)e * a.w_stride * 2;
     j.s0.a_rows_valid = rows; j.s0.a_n0 = 0; j.s0.b_n0 = j0;
     j.s0.K = a.d_out;
@@ -489,12 +507,14 @@ __device__ __forceinline__ Job make_job(const GemmPlan& P, int t) {
     j.s1 = j.s0;
     j.nk0 = j.nk = (a.d_out + C::BK - 1) / C::BK;
     if (a.Gp2) {  // second segment of the same shape (host-checked: d_out2 == d_out)
-      j.s1.a = (const char*)a.Gp2 + (int64_t)m0 * a.d_out * 2;
+      j.s1.a = (const char*)a.Gp2 + m0 * lda * 2;
       j.s1.b = (const char*)a.W2 + (int64_t)e * a.w2_stride * 2;
       j.nk = 2 * j.nk0;
     }
     if (rows <= 0) j.nk = 0;
     j.C = a.dXp + (int64_t)m0 * a.d_in + j0;
+    j.C2 = j.C;
+    j.split = C::BM;
     j.rows = rows;
     j.cols = min(C::BN, a.d_in - j0);
   }
@@ -563,16 +583,27 @@ __device__ __forceinline__ void write_tile(const f32x4 (&acc)[C::FM][C::FN], boo
   }
 }
 
-// A finished (or zero) output tile at out (an element of dW or dXp): dW
-// tiles go out as bf16 when the call asks for it.
-template <class C, bool DWB>
+// A finished (or zero) output tile of job j (in dW, or dW and dW2 when split,
+// or dXp): dW tiles go out as bf16 when the call asks for it.  A split tile's
+// waves each lie on one side of the split (it is a multiple of the wave's
+// 64 rows), so each picks its output as a whole.
+template <class C, bool DWB, bool SPLIT = false>
 __device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x4 (&acc)[C::FM][C::FN],
-                                           bool zero, float* out, int rows, int cols) {
+                                           bool zero, const Job& j) {
+  float* out = j.C;
+  float* base = a.dW;
+  if constexpr (SPLIT) {
+    static_assert(C::TM == 64, "a wave's rows lie on one side of a split at a multiple of 64");
+    const int wm = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) / C::WGN;
+    const bool second = wm * C::TM >= j.split;
+    out = second ? j.C2 : j.C;
+    base = second ? a.dW2 : a.dW;
+  }
   if constexpr (DWB)
-    write_tile<C, true>(acc, zero, reinterpret_cast<uint16_t*>(a.dW) + (out - a.dW), a.d_in,
-                        rows, cols);
+    write_tile<C, true>(acc, zero, reinterpret_cast<uint16_t*>(base) + (out - base), a.d_in,
+                        j.rows, j.cols);
   else
-    write_tile<C, false>(acc, zero, out, a.d_in, rows, cols);
+    write_tile<C, false>(acc, zero, out, a.d_in, j.rows, j.cols);
 }
 
 // MFMAs of k-granules kk..kk+3 (lane group l >> 4 takes granule kk + (l >> 4))
@@ -829,7 +860,7 @@ __device__ __forceinline__ TileSeq tile_seq(const GemmPlan& P) {
 // ahead, one barrier per k-tile.  The loads of a tile's first k-tiles are thus
 // in flight while the previous tile's outputs are written.  A tile with no
 // k-tiles (an expert that kept no rows) writes zeros.
-template <class C, bool DX, bool DWB, bool GB = false>
+template <class C, bool DX, bool DWB, bool GB = false, bool SPLIT = false>
 __device__ __forceinline__ void gemm_stream(const GemmPlan& P) {
   __shared__ __attribute__((aligned(16))) uint16_t As[C::STAGES * C::BM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[C::STAGES * C::BN * BK];
@@ -848,17 +879,17 @@ __device__ __forceinline__ void gemm_stream(const GemmPlan& P) {
   // compute cursor: tile tc (job jc), k-tile kc; zero tiles are written as met
   Job jc;
   for (; tc >= 0; tc = sc.at(++kcn)) {
-    jc = make_job<C, DX>(P, tc);
+    jc = make_job<C, DX, SPLIT>(P, tc);
     if (jc.nk > 0) break;
-    if (jc.rows > 0) store_tile<C, DWB>(a, acc, true, jc.C, jc.rows, jc.cols);
+    if (jc.rows > 0) store_tile<C, DWB, SPLIT>(a, acc, true, jc);
   }
   if (tc < 0) return;
 
   Stage<C, DX, GB> st;
   if constexpr (GB)
-    st.init(a.d_out, a.ldxs, a.xsrc_rows);
+    st.init(a.lda > 0 ? a.lda : a.d_out, a.ldxs, a.xsrc_rows);
   else
-    st.init(a.d_out, a.d_in);
+    st.init(a.lda > 0 ? a.lda : a.d_out, a.d_in);
   // load cursor: tile tl (job jl), k-tile kl, two k-tiles ahead of the compute
   TileSeq sl = sc;
   int kln = kcn;
@@ -872,7 +903,7 @@ __device__ __forceinline__ void gemm_stream(const GemmPlan& P) {
     if (++kl == jl.nk) {                                                        \
       kl = 0;                                                                   \
       for (tl = sl.at(++kln); tl >= 0; tl = sl.at(++kln)) {                     \
-        jl = make_job<C, DX>(P, tl);                                            \
+        jl = make_job<C, DX, SPLIT>(P, tl);                                            \
         if (jl.nk > 0) break;                                                   \
       }                                                                         \
     }                                                                           \
@@ -914,16 +945,16 @@ __device__ __forceinline__ void gemm_stream(const GemmPlan& P) {
   for (;;) {
     LRM_KSTEP();
     if (++kc == jc.nk) {
-      store_tile<C, DWB>(a, acc, false, jc.C, jc.rows, jc.cols);
+      store_tile<C, DWB, SPLIT>(a, acc, false, jc);
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
       kc = 0;
       for (tc = sc.at(++kcn); tc >= 0; tc = sc.at(++kcn)) {
-        jc = make_job<C, DX>(P, tc);
+        jc = make_job<C, DX, SPLIT>(P, tc);
         if (jc.nk > 0) break;
-        if (jc.rows > 0) store_tile<C, DWB>(a, acc, true, jc.C, jc.rows, jc.cols);
+        if (jc.rows > 0) store_tile<C, DWB, SPLIT>(a, acc, true, jc);
       }
       if (tc < 0) break;
     }
@@ -943,6 +974,12 @@ __global__ __launch_bounds__(C::NT, C::WPE) void k_gemm_stream(GemmPlan P) {
 template <class C>
 __global__ __launch_bounds__(C::NT, C::WPE) void k_gemm_stream_dwbf16(GemmPlan P) {
   gemm_stream<C, false, true>(P);
+}
+
+// dW products split over two outputs (GemmArgs::dw_split), fp32 or bf16 dW
+template <class C, bool DWB>
+__global__ __launch_bounds__(C::NT, C::WPE) void k_gemm_stream_split(GemmPlan P) {
+  gemm_stream<C, false, DWB, false, true>(P);
 }
 
 // dW products with the B panel gathered from its source rows (fp32 or bf16 dW)
@@ -1206,12 +1243,12 @@ __device__ __forceinline__ void gemm_dma(const GemmPlan& P) {
   for (; tc >= 0; tc = sc.at(++kcn)) {
     jc = make_job<C, DX>(P, tc);
     if (jc.nk > 0) break;
-    if (jc.rows > 0) store_tile<C, DWB>(a, acc, false, jc.C, jc.rows, jc.cols);
+    if (jc.rows > 0) store_tile<C, DWB>(a, acc, false, jc);
   }
   if (tc < 0) return;
 
   DmaStage<C, DX> st;
-  st.init(a.d_out, a.d_in);
+  st.init(a.lda > 0 ? a.lda : a.d_out, a.d_in);
   DmaFrag<C, DX> fr;
   fr.init();
   // vm: vector memory instructions this wave has issued since the first load
@@ -1258,7 +1295,7 @@ __device__ __forceinline__ void gemm_dma(const GemmPlan& P) {
       bool done = false;
       for (;;) {
         if (jc.rows > 0) {
-          store_tile<C, DWB>(a, acc, false, jc.C, jc.rows, jc.cols);
+          store_tile<C, DWB>(a, acc, false, jc);
           vm += C::NSTORE;
         }
 #pragma unroll
@@ -1460,6 +1497,17 @@ static hipError_t launch_stream(const GemmPlan& P, int ntiles_max, hipStream_t s
   if (ntiles_max <= 0) return hipSuccess;
   const int64_t want = ((int64_t)ntiles_max + 7) & ~7ll;
   if constexpr (!DX) {
+    if (P.a.dw_split > 0) {
+      // the split dW kernels (their residency is that of the plain ones)
+      const int G = per_tile ? (int)want
+                             : (int)std::min<int64_t>(
+                                   want, std::max(8, stream_grid_cap<C, false>() & ~7));
+      if (P.a.dw_bf16)
+        LRM_LAUNCH(G, C::NT, 0, s, k_gemm_stream_split<C, true>)(P);
+      else
+        LRM_LAUNCH(G, C::NT, 0, s, k_gemm_stream_split<C, false>)(P);
+      return hipGetLastError();
+    }
     if (P.a.xrow) {
       // the gathering dW kernels (their residency is that of the plain ones)
       const int G = per_tile ? (int)want
@@ -1508,7 +1556,7 @@ static int dma_choice() {
 template <class C>
 static bool dma_ok(const GemmArgs& a, bool dx) {
   auto al = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
-  if (a.d_in % 8 || a.d_out % 8 || !al(a.Gp)) return false;
+  if (a.d_in % 8 || a.d_out % 8 || a.lda % 8 || !al(a.Gp)) return false;
   if (!dx) return !a.xrow && al(a.Xp);
   if (a.d_out % C::BK || !al(a.W) || a.w_stride % 8) return false;
   return !a.Gp2 || (al(a.Gp2) && al(a.W2) && a.w2_stride % 8 == 0);
@@ -1538,7 +1586,7 @@ template <class C, bool DX>
 static hipError_t launch_product(const GemmPlan& P, int ntiles_max, hipStream_t s,
                                  bool per_tile) {
   if constexpr (std::is_same<C, CfgL>::value) {
-    const int d = dma_choice();
+    const int d = P.a.dw_split > 0 ? 0 : dma_choice();  // the DMA kernels write one dW
     if (d == 2 && dma_ok<CfgD>(P.a, DX)) return launch_dma<CfgD, DX>(P, ntiles_max, s, per_tile);
     if (d == 4 && dma_ok<CfgD4>(P.a, DX))
       return launch_dma<CfgD4, DX>(P, ntiles_max, s, per_tile);
@@ -1624,6 +1672,12 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   if (a.xrow && (!a.bf16 || !a.xsrc || !a.xw || a.xsrc_rows * a.ldxs * 2 >= (1ll << 31) ||
                  a.ldxs < a.d_in))
+    return hipErrorInvalidValue;
+  // the row stride of Gp (Gp2) and the split dW: bf16 kernels only; a split
+  // on a multiple of the waves' 64 rows
+  if (a.lda != 0 && (!a.bf16 || a.lda < a.d_out || a.lda % 8)) return hipErrorInvalidValue;
+  if (a.dw_split != 0 && (!a.bf16 || !a.dW || !a.dW2 || a.xrow || a.dw_split < 0 ||
+                          a.dw_split >= a.d_out || a.dw_split % 64))
     return hipErrorInvalidValue;
   if (a.bf16) {
     // 32-bit store offsets inside a tile (the public entry points check this)

@@ -35,8 +35,9 @@ __global__ __launch_bounds__(256) void k_glu_bwd(GluBwdArgs g) {
   if constexpr (BF16) {
     const u32x4* ar = reinterpret_cast<const u32x4*>((const uint16_t*)g.A + (int64_t)p * g.lda);
     const u32x4* br = reinterpret_cast<const u32x4*>((const uint16_t*)g.B + (int64_t)p * g.ldb);
-    u32x4* gar = reinterpret_cast<u32x4*>((uint16_t*)g.GA + (int64_t)m * g.I);
-    u32x4* gbr = reinterpret_cast<u32x4*>((uint16_t*)g.GB + (int64_t)m * g.I);
+    const int64_t ldg = g.ldg > 0 ? g.ldg : g.I;
+    u32x4* gar = reinterpret_cast<u32x4*>((uint16_t*)g.GA + (int64_t)m * ldg);
+    u32x4* gbr = reinterpret_cast<u32x4*>((uint16_t*)g.GB + (int64_t)m * ldg);
     for (int c = lane_id(); c < g.I / 8; c += kWave) {
       const u32x4 va = ar[c], vb = br[c];
       const f32x4 u0 = *reinterpret_cast<const f32x4*>(urow + c * 8);
@@ -61,8 +62,9 @@ __global__ __launch_bounds__(256) void k_glu_bwd(GluBwdArgs g) {
   } else {
     const float* ar = (const float*)g.A + (int64_t)p * g.lda;
     const float* br = (const float*)g.B + (int64_t)p * g.ldb;
-    float* gar = (float*)g.GA + (int64_t)m * g.I;
-    float* gbr = (float*)g.GB + (int64_t)m * g.I;
+    const int64_t ldg = g.ldg > 0 ? g.ldg : g.I;
+    float* gar = (float*)g.GA + (int64_t)m * ldg;
+    float* gbr = (float*)g.GB + (int64_t)m * ldg;
     for (int c = lane_id() * 4; c < g.I; c += kWave * 4) {
       const f32x4 va = *reinterpret_cast<const f32x4*>(ar + c);
       const f32x4 vb = *reinterpret_cast<const f32x4*>(br + c);
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(256) void k_glu_bwd(GluBwdArgs g) {
 hipError_t launch_glu_bwd(const GluBwdArgs& g, hipStream_t s) {
   if (g.max_rows <= 0) return hipSuccess;
   if (!g.offsets_down || !g.kept_down || !g.U || !g.A || !g.B || !g.GA || !g.GB ||
-      ((g.s_gate || g.s_up) && !g.x2))
+      ((g.s_gate || g.s_up) && !g.x2) || (g.ldg != 0 && g.ldg < g.I))
     return hipErrorInvalidValue;
   const int blocks = (g.max_rows + 3) / 4;
   if (g.bf16)

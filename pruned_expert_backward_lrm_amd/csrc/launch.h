@@ -149,10 +149,17 @@ hipError_t launch_row_map(const CompactArgs& a, int32_t* xrow, float* xw, hipStr
 struct GemmArgs {
   int E, bf16, max_rows, d_in, d_out;
   const int32_t* offsets;
-  const void* Gp;  // [rows][d_out]
+  const void* Gp;  // [rows][d_out], rows lda apart (bf16 kernels; lda 0: d_out)
+  int lda;
   const void* Xp;  // [rows][d_in]
   const void* W; int64_t w_stride;  // [E][d_out][d_in]
   const void* Gp2; const void* W2; int64_t w2_stride; int d_out2;  // optional
+  // dW split in two outputs (bf16 kernels; dw_split 0: one output): rows
+  // [0, dw_split) of each expert's dW go to dW ([E][dw_split][d_in]) and rows
+  // [dw_split, d_out) to dW2 ([E][d_out - dw_split][d_in]); dw_split is a
+  // multiple of 64, so every wave of a tile writes to one of them
+  float* dW2;
+  int dw_split;
   float* dW;   // [E][d_out][d_in] or nullptr
   float* dXp;  // [max_rows][d_in] or nullptr
   int32_t* mt_off;  // workspace [gemm_workspace_ints(E)]: the dX row-tile prefix [E+1], then the dW schedule
@@ -214,7 +221,8 @@ struct GluBwdArgs {
   const void* A; int64_t lda;
   const void* B; int64_t ldb;
   const double* x2; int x_pair;
-  void* GA; void* GB;  // [rows][I]
+  void* GA; void* GB;  // [rows][I], rows ldg apart (0: I)
+  int ldg;
   float* s_gate; float* s_up;
 };
 hipError_t launch_glu_bwd(const GluBwdArgs& a, hipStream_t s);

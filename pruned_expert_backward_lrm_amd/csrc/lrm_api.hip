@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/lrm.h: argument validation,
 // workspace planning and the stream-ordered launch sequences.  Nothing here
 // allocates device memory; scratch comes from the caller's workspace.
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -638,6 +639,8 @@ GluPlan carve_glu(Carve& c, const lrm_problem* pb, const lrm_outputs* out, int64
   L.Gd = c.take<char>(Md * H * es);
   L.Hd = c.take<char>(Md * I * es);
   L.U = c.take<float>(Md * I);
+  // GA then GB, back to back: the fused gate/up path writes rows of [GA | GB]
+  // (2I wide) into the span of both
   L.GA = c.take<char>(Md * I * es);
   L.GB = c.take<char>(Md * I * es);
   L.s_gate = c.take<float>(Md);
@@ -883,6 +886,17 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   GluPlan L = carve_glu(c, pb, out, z.Md, z.Mg, z.Mu, z.pass_through);
   const int bf16 = pb->dtype == LRM_BF16;
   const int H = pb->H, I = pb->I, E = p->E;
+  // Gate and up keep the same rows (one packing): their weight gradients are
+  // one product Gp^T X with Gp = [GA | GB] ([rows][2I], the SwiGLU backward
+  // writes GA and GB side by side into the span of both) split over dW_gate
+  // and dW_up, which tiles 2I where I alone leaves a part-filled last tile.
+  // bf16 kernels, I a multiple of 64 (the split falls between waves), packed
+  // w x (the gathering loaders write one output).
+  // (LRM_FUSE_GATE_UP=0 keeps two launches, for comparison.)
+  const char* fenv = getenv("LRM_FUSE_GATE_UP");
+  const bool fuse_gu = z.pass_through && bf16 && I % 64 == 0 && !L.xrow_g &&
+                       !(fenv && fenv[0] == '0');
+  void* const GBw = fuse_gu ? static_cast<void*>(static_cast<char*>(L.GA) + (int64_t)I * 2) : L.GB;
   GemmArgs gd{};
   gd.E = E; gd.bf16 = bf16; gd.max_rows = (int)z.Md;
   const int dx_rows = gemm_dx_tile_rows(gd);
@@ -923,7 +937,7 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   gb.T = p->T; gb.bf16 = bf16; gb.max_rows = (int)z.Md; gb.E = E; gb.I = I;
   gb.offsets_down = L.offsets; gb.kept_down = L.kept; gb.token = p->token; gb.weight = p->weight;
   gb.U = L.U; gb.A = pb->A.ptr; gb.lda = pb->A.ld; gb.B = pb->B.ptr; gb.ldb = pb->B.ld;
-  gb.x2 = L.x2; gb.x_pair = x_pair; gb.GA = L.GA; gb.GB = L.GB;
+  gb.x2 = L.x2; gb.x_pair = x_pair; gb.GA = L.GA; gb.GB = GBw; gb.ldg = fuse_gu ? 2 * I : 0;
   gb.s_gate = keep_all ? nullptr : L.s_gate;
   gb.s_up = keep_all ? nullptr : L.s_up;
   LRM_TRY_HIP(launch_glu_bwd(gb, s));
@@ -975,40 +989,63 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
     else
       LRM_TRY_HIP(launch_compact(cx, s));
     LRM_TRY_HIP(mark(8));
-    GemmArgs gg{};
-    gg.E = E; gg.bf16 = bf16; gg.max_rows = (int)z.Md; gg.d_in = H; gg.d_out = I;
-    gg.offsets = L.offsets; gg.Gp = L.GA; gg.Xp = L.Xgu;
-    gg.W = pb->W_gate; gg.w_stride = (int64_t)I * H;
-    gg.Gp2 = L.GB; gg.W2 = pb->W_up; gg.w2_stride = (int64_t)I * H; gg.d_out2 = I;
-    gg.dW = out->dW_gate; gg.dXp = L.dXp; gg.mt_off = L.mt_off;
-    gg.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
-    const int64_t xsrc_rows = x_pair ? p->N : p->T;
-    if (L.xrow_g) {
-      gg.xrow = L.xrow_g; gg.xw = L.xw_g; gg.xsrc = pb->X.ptr; gg.ldxs = pb->X.ld;
-      gg.xsrc_rows = xsrc_rows;
+    if (fuse_gu) {
+      GemmArgs gw{};
+      gw.E = E; gw.bf16 = bf16; gw.max_rows = (int)z.Md; gw.d_in = H; gw.d_out = 2 * I;
+      gw.offsets = L.offsets; gw.Gp = L.GA; gw.Xp = L.Xgu;
+      gw.dW = out->dW_gate; gw.dW2 = out->dW_up; gw.dw_split = I;
+      gw.mt_off = L.mt_off;
+      gw.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
+      LRM_TRY_HIP(launch_grouped_gemm(gw, s));
+      LRM_TRY_HIP(mark(9));
+      // both input-gradient products, K = 2I in two segments of [GA | GB]
+      GemmArgs gx{};
+      gx.E = E; gx.bf16 = bf16; gx.max_rows = (int)z.Md; gx.d_in = H; gx.d_out = I;
+      gx.lda = 2 * I;
+      gx.offsets = L.offsets; gx.Gp = L.GA; gx.W = pb->W_gate; gx.w_stride = (int64_t)I * H;
+      gx.Gp2 = GBw; gx.W2 = pb->W_up; gx.w2_stride = (int64_t)I * H; gx.d_out2 = I;
+      gx.dXp = L.dXp; gx.mt_off = L.mt_off;
+      LRM_TRY_HIP(launch_grouped_gemm(gx, s));
+      LRM_TRY_HIP(mark(10));
+      LRM_TRY_HIP(mark(11));
+      LRM_TRY_HIP(mark(12));
+      sa.pos[0] = L.pos; sa.src[0] = L.dXp; sa.src_rows[0] = (int)z.Md;
+    } else {
+      GemmArgs gg{};
+      gg.E = E; gg.bf16 = bf16; gg.max_rows = (int)z.Md; gg.d_in = H; gg.d_out = I;
+      gg.offsets = L.offsets; gg.Gp = L.GA; gg.Xp = L.Xgu;
+      gg.W = pb->W_gate; gg.w_stride = (int64_t)I * H;
+      gg.Gp2 = L.GB; gg.W2 = pb->W_up; gg.w2_stride = (int64_t)I * H; gg.d_out2 = I;
+      gg.dW = out->dW_gate; gg.dXp = L.dXp; gg.mt_off = L.mt_off;
+      gg.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
+      const int64_t xsrc_rows = x_pair ? p->N : p->T;
+      if (L.xrow_g) {
+        gg.xrow = L.xrow_g; gg.xw = L.xw_g; gg.xsrc = pb->X.ptr; gg.ldxs = pb->X.ld;
+        gg.xsrc_rows = xsrc_rows;
+      }
+      gg.mid_event = mark.at(9);
+      // the down projection's dW launch left the schedule of these offsets and
+      // max_rows in the workspace: the gate and up launches reuse it when their
+      // tiles per expert agree (the schedule depends on nothing else)
+      const int plan_per = gemm_dw_tiles_per_expert(gd);
+      gg.dw_plan_ready = plan_per > 0 && gemm_dw_tiles_per_expert(gg) == plan_per;
+      LRM_TRY_HIP(launch_grouped_gemm(gg, s));
+      LRM_TRY_HIP(mark(10));
+      GemmArgs gu{};
+      gu.E = E; gu.bf16 = bf16; gu.max_rows = (int)z.Md; gu.d_in = H; gu.d_out = I;
+      gu.offsets = L.offsets; gu.Gp = L.GB; gu.Xp = L.Xgu;
+      gu.dW = out->dW_up; gu.dXp = nullptr; gu.mt_off = L.mt_off;
+      gu.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
+      gu.dw_plan_ready = plan_per > 0 && gemm_dw_tiles_per_expert(gu) == plan_per;
+      if (L.xrow_u) {
+        gu.xrow = L.xrow_u; gu.xw = L.xw_u; gu.xsrc = pb->X.ptr; gu.ldxs = pb->X.ld;
+        gu.xsrc_rows = xsrc_rows;
+      }
+      LRM_TRY_HIP(launch_grouped_gemm(gu, s));
+      LRM_TRY_HIP(mark(11));
+      LRM_TRY_HIP(mark(12));
+      sa.pos[0] = L.pos; sa.src[0] = L.dXp; sa.src_rows[0] = (int)z.Md;
     }
-    gg.mid_event = mark.at(9);
-    // the down projection's dW launch left the schedule of these offsets and
-    // max_rows in the workspace: the gate and up launches reuse it when their
-    // tiles per expert agree (the schedule depends on nothing else)
-    const int plan_per = gemm_dw_tiles_per_expert(gd);
-    gg.dw_plan_ready = plan_per > 0 && gemm_dw_tiles_per_expert(gg) == plan_per;
-    LRM_TRY_HIP(launch_grouped_gemm(gg, s));
-    LRM_TRY_HIP(mark(10));
-    GemmArgs gu{};
-    gu.E = E; gu.bf16 = bf16; gu.max_rows = (int)z.Md; gu.d_in = H; gu.d_out = I;
-    gu.offsets = L.offsets; gu.Gp = L.GB; gu.Xp = L.Xgu;
-    gu.dW = out->dW_up; gu.dXp = nullptr; gu.mt_off = L.mt_off;
-    gu.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
-    gu.dw_plan_ready = plan_per > 0 && gemm_dw_tiles_per_expert(gu) == plan_per;
-    if (L.xrow_u) {
-      gu.xrow = L.xrow_u; gu.xw = L.xw_u; gu.xsrc = pb->X.ptr; gu.ldxs = pb->X.ld;
-      gu.xsrc_rows = xsrc_rows;
-    }
-    LRM_TRY_HIP(launch_grouped_gemm(gu, s));
-    LRM_TRY_HIP(mark(11));
-    LRM_TRY_HIP(mark(12));
-    sa.pos[0] = L.pos; sa.src[0] = L.dXp; sa.src_rows[0] = (int)z.Md;
   } else {
     const void* GAsrc[2] = {L.GA, L.GB};
     int32_t* keptv[2] = {L.kept_g, L.kept_u};

@@ -6,11 +6,12 @@ access of a kernel or of the host code aborts the run; the outputs must pass
 the same oracle checks as the GPU parity tests.  Runs without a GPU.
 
 Every lane is an OS thread and every wave collective two 64-thread barriers,
-so a case takes 30-130 s.  The default run keeps four: the tiny fp32
+so a case takes 30-130 s.  The default run keeps five: the tiny fp32
 workload (every step, the fp32 GEMM), the bf16 grouped GEMM in its 256x256
-tiles, the same tiles on the LDS-DMA kernels, and the dW schedule with its
-tiles striped over the XCDs; LRM_EMU_FULL=1 runs all of them (about 28
-minutes on 8 cores).
+tiles, the same tiles on the LDS-DMA kernels, the dW schedule with its
+tiles striped over the XCDs, and the SwiGLU gate/up weight gradients in one
+launch over two outputs; LRM_EMU_FULL=1 runs all of them (about 30 minutes
+on 8 cores).
 """
 
 from __future__ import annotations
@@ -239,6 +240,22 @@ def test_emu_swiglu(driver, tmp_path, dtype, variant):
     p = synth.make_swiglu(160, 6, 2, 136, 72, dtype=dtype, seed=5, zipf=1.2, quotas=quotas,
                           g_std=1e-2)
     judge_swiglu(p, run_emu(driver, tmp_path, p))
+
+
+@pytest.mark.parametrize("tile", [pytest.param("S", marks=extended), "L",
+                                  pytest.param("X", marks=extended)])
+def test_emu_swiglu_fused_gate_up(driver, tmp_path, tile):
+    """Gate and up keep the down stage's rows (same quotas), bf16, I = 192: one
+    dW launch over [GA | GB] (2I = 384 rows per expert) writes rows below I to
+    dW_gate and the rest to dW_up, a tile straddling the split (256-row tiles:
+    rows 0..255 hold all of the gate rows and 64 up rows; 128-row tiles: the
+    second one's waves write to either side), and the dX launch reads GA and
+    GB as two K segments of the 2I-wide rows.  Under AddressSanitizer and
+    judged against the oracle."""
+    p = synth.make_swiglu(160, 6, 2, 72, 192, dtype="bf16", seed=5, zipf=1.2,
+                          quotas=(lambda c: c // 2, lambda c: c // 2, lambda c: c // 2),
+                          g_std=1e-2)
+    judge_swiglu(p, run_emu(driver, tmp_path, p, env_extra={"LRM_GEMM_TILE": tile}))
 
 
 def _no_pairs(kind, dtype, T=48, E=4):

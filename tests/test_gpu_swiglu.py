@@ -151,6 +151,33 @@ def test_fused_swiglu_lds_dma_bit_exact(L, flags, monkeypatch):
         judge_swiglu(p, res["2"])
 
 
+@pytest.mark.parametrize("tile", ["S", "M", "L", "X"])
+@pytest.mark.parametrize("shape", [(200, 64), (200, 192), (776, 320)])
+@pytest.mark.parametrize("flags", [0, 2])
+def test_fused_gate_up_dw_bit_exact(L, tile, shape, flags, monkeypatch):
+    """Same quotas, bf16, I a multiple of 64: one launch computes dW_gate and
+    dW_up over [GA | GB] (2I rows per expert split at I, tiles straddling the
+    split), and the dX launch reads GA and GB as two K segments of the
+    2I-wide rows.  Every output equals the two-launch path's
+    (LRM_FUSE_GATE_UP=0) bit for bit, fp32 and bf16 (LRM_DW_BF16 = 2) weight
+    gradients; at H = 776, I = 320 the 256x256 tiles number 12 per expert,
+    so the heavy experts' tiles go out in XCD stripes.  Judged against the
+    oracle with fp32 weight gradients."""
+    H, I = shape
+    monkeypatch.setenv("LRM_GEMM_TILE", tile)
+    say("fused gate/up dW", tile, shape, flags)
+    p = synth.make_swiglu(1200, 8, 2, H, I, dtype="bf16", seed=31, zipf=1.3,
+                          quotas=QUOTAS["same"], g_std=1e-2)
+    got = run_swiglu(L, p, DEV, flags=flags)
+    monkeypatch.setenv("LRM_FUSE_GATE_UP", "0")
+    ref = run_swiglu(L, p, DEV, flags=flags)
+    for k in ("dW_gate", "dW_up", "dW_down", "dX", "dH", "score", "pos", "score_gate",
+              "pos_gate", "pos_up"):
+        assert torch.equal(got[k], ref[k]), k
+    if flags == 0:
+        judge_swiglu(p, got)
+
+
 def test_fused_swiglu_deterministic(L):
     p = synth.make_swiglu(500, 8, 2, 256, 128, dtype="bf16", seed=8, zipf=1.1,
                           quotas=QUOTAS["second"])
