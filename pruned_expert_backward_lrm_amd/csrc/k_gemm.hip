@@ -692,20 +692,23 @@ __global__ __launch_bounds__(NT) void k_dw_plan(GemmPlan P) {
   const int E = a.E, per = P.ntm_w * P.ntn, R = plan_runs(E);
   int32_t* plan = a.dw_plan;
   __shared__ int cum[kPlanMaxE + 1];  // exclusive prefix of the expert costs
+  __shared__ int cst[kPlanMaxE];      // the expert costs (one read of the offsets)
   __shared__ int lds[NT / kWave + 1];
   __shared__ int lo[9], base[9], ncut[8], len[8];
   __shared__ int heavy[kPlanMaxHeavy];
   __shared__ int re[plan_runs(kPlanMaxE)], rf[plan_runs(kPlanMaxE)];
   __shared__ int rn[plan_runs(kPlanMaxE)], rc[plan_runs(kPlanMaxE)];
   const int t = threadIdx.x;
+  for (int e = t; e < E; e += NT) cst[e] = dw_cost(a, e);
+  __syncthreads();
   // the total cost, then the heavy experts (in expert order), then the
   // prefix of the costs with the heavy experts' left out
-  block_scan_array<NT>(E, [&](int e) { return dw_cost(a, e); }, cum, lds);
+  block_scan_array<NT>(E, [&](int e) { return cst[e]; }, cum, lds);
   __syncthreads();
   const int64_t lim = (int64_t)per * cum[E];
   __syncthreads();
   auto is_heavy = [&](int e) {
-    return per >= 8 && (int64_t)dw_cost(a, e) * kHeavyDiv >= lim;
+    return per >= 8 && (int64_t)cst[e] * kHeavyDiv >= lim;
   };
   block_scan_array<NT>(E, [&](int e) { return is_heavy(e) ? 1 : 0; }, cum, lds);
   __syncthreads();
@@ -714,7 +717,7 @@ __global__ __launch_bounds__(NT) void k_dw_plan(GemmPlan P) {
     if (cum[e + 1] > cum[e]) heavy[cum[e]] = e;
   if (t < 8) len[t] = 0;
   __syncthreads();
-  block_scan_array<NT>(E, [&](int e) { return is_heavy(e) ? 0 : dw_cost(a, e); }, cum, lds);
+  block_scan_array<NT>(E, [&](int e) { return is_heavy(e) ? 0 : cst[e]; }, cum, lds);
   __syncthreads();
   if (t <= 8) {
     // cut start: the first tile whose start cost is >= total * t / 8 (a
@@ -771,7 +774,7 @@ __global__ __launch_bounds__(NT) void k_dw_plan(GemmPlan P) {
       re[r] = e;
       rf[r] = f0;
       rn[r] = f1 - f0;
-      rc[r] = dw_cost(a, e);
+      rc[r] = cst[e];
     }
     atomicAdd(&len[x], rn[r]);
   }
