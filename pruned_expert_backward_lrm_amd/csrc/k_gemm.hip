@@ -529,11 +529,13 @@ __device__ __forceinline__ Job make_job(const GemmPlan& P, int t) {
 // instead of 256).
 constexpr int kOobOff = 0x7fff0000;  // past every tile's bound (tiles span < 1 GiB)
 
+template <int AUX = 0>
 __device__ __forceinline__ void bstore16(rsrc_t r, int off, u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, AUX);
 }
+template <int AUX = 0>
 __device__ __forceinline__ void bstore8(rsrc_t r, int off, u32x2 v) {
-  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, AUX);
 }
 
 // A wave-uniform value the compiler cannot see through: offsets built from it
@@ -548,11 +550,87 @@ __device__ __forceinline__ int opaque_uniform(int x) {
 }
 #endif
 
+// Value of v in lane (l - N) mod 16 of l's 16-lane row (DPP row rotation).
+template <int N>
+__device__ __forceinline__ float row_rot(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + N, 0xf, 0xf, false));
+}
+
+// The accumulators of a wave's 16-row block i over NF = 4 fragments
+// 4J..4J+3 (16 rows x 64 columns) rearranged for row-contiguous stores:
+// afterwards lane l holds row 4q + (l >> 4), columns 4 (l & 15) .. + 3 of the
+// block in out[q], so each 16-lane quarter of a store covers 256 contiguous
+// bytes of one row.  In the MFMA layout (lane l: row l & 15, columns
+// 4 (l >> 4) .. + 3 of a fragment) a quarter stores 16 bytes into each of 16
+// rows; one CU sustains about 35 GB/s of those stores against about 150 GB/s
+// of 256-byte row pieces (measured on gfx950), and a tile's stores hold up
+// the next tile's loads.
+// Indexing (fragment f, lane bits g = l >> 4, r = l & 15 with r = 4q + a):
+// swapping the fragment bits with lane bits 3..2 (DPP row rotations by 8,
+// then 4 and 12) puts q in the register index and f in lane bits 3..2; a
+// lane permutation exchanging lane bits 5..4 with 1..0 (ds_bpermute) then
+// leaves lane (a, f, g) holding row 4q + a, columns 16 f + 4 g.
+// With NF = 2 fragments 2J, 2J+1 (16 rows x 32 columns) only fragment bit 0
+// and lane bit 2 are swapped: lane l then holds row 8 ((l >> 3) & 1) + 4q +
+// (l >> 4), columns 4 (l & 7) .. + 3 in out[q], q < 2 (a quarter: two rows
+// of 128 bytes).
+template <class C, int NF>
+__device__ __forceinline__ void row_major_group(const f32x4 (&acc)[C::FM][C::FN], int i, int J,
+                                                f32x4 (&out)[NF]) {
+  static_assert(NF == 2 || NF == 4, "fragments per group");
+  const int l = lane_id();
+  const bool b3 = (l >> 3) & 1, b2 = (l >> 2) & 1;
+  float v[NF][4];
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[f][k] = acc[i][NF * J + f][k];
+  if constexpr (NF == 4) {
+    // fragment bit 1 <-> lane bit 3 (lanes l and l ^ 8)
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float x = v[f][k], y = v[f + 2][k];
+        const float xr = row_rot<8>(x), yr = row_rot<8>(y);
+        v[f][k] = b3 ? yr : x;
+        v[f + 2][k] = b3 ? y : xr;
+      }
+  }
+  // fragment bit 0 <-> lane bit 2 (lanes l and l ^ 4: l - 4 where bit 2 is
+  // set, l + 4 where it is clear)
+#pragma unroll
+  for (int f = 0; f < NF; f += 2)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float x = v[f][k], y = v[f + 1][k];
+      const float y4 = row_rot<4>(y), x12 = row_rot<12>(x);
+      v[f][k] = b2 ? y4 : x;
+      v[f + 1][k] = b2 ? y : x12;
+    }
+  // lane bits 5..4 <-> 1..0
+  const int src = (((l & 3) << 4) | (l & 12) | (l >> 4)) << 2;
+#pragma unroll
+  for (int q = 0; q < NF; ++q)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      out[q][k] = __builtin_bit_cast(
+          float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, v[q][k])));
+}
+
 // Writes a tile's accumulators (or zeros) within its valid rows and columns
 // (rows <= 0: nothing is written, but every store is still issued).  Elements
 // of ES bytes; lane l holds C[row = .. + (l & 15)][col = .. + (l >> 4) * 4 + 0..3].
-// ldc < 2^20 (checked by the launcher), so a tile spans less than 1 GiB.
-template <class C, bool BF16>
+// ROWS: the stores go out row-contiguous (row_major_group, groups of four
+// fragments, or of two where a wave row holds two), non-temporal (the nt
+// bit: the output is not read again by this launch, and whole lines leave
+// the caches early instead of evicting operand panels); otherwise in the
+// MFMA layout with the default policy (the gathering kernels, whose
+// registers the rearrangement would spill; non-temporal stores of partial
+// lines measured slower).  ldc < 2^20 (checked by the launcher), so a tile
+// spans less than 1 GiB.
+template <class C, bool BF16, bool ROWS = true>
 __device__ __forceinline__ void write_tile(const f32x4 (&acc)[C::FM][C::FN], bool zero,
                                            void* out, int64_t ldc, int rows, int cols) {
   constexpr int ES = BF16 ? 2 : 4;
@@ -561,6 +639,37 @@ __device__ __forceinline__ void write_tile(const f32x4 (&acc)[C::FM][C::FN], boo
   const int64_t extent = (rows > 0 && cols > 0) ? ((int64_t)(rows - 1) * ldc + cols) * ES : 0;
   const rsrc_t rs = make_rsrc((const char*)out, extent);
   const int ld = opaque_uniform((int)ldc);
+  if constexpr (ROWS && C::FN % 2 == 0) {
+    constexpr int NF = C::FN % 4 == 0 ? 4 : 2;
+    const int rl = wm * C::TM + (l >> 4) + (NF == 2 ? 8 * ((l >> 3) & 1) : 0);
+    const int cl = wn * C::TN + (NF == 4 ? (l & 15) : (l & 7)) * 4;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int J = 0; J < C::FN / NF; ++J) {
+        f32x4 o[NF];
+        if (zero) {
+#pragma unroll
+          for (int q = 0; q < NF; ++q) o[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        } else {
+          row_major_group<C, NF>(acc, i, J, o);
+        }
+#pragma unroll
+        for (int q = 0; q < NF; ++q) {
+          const int row = rl + i * 16 + q * 4, col = cl + J * 16 * NF;
+          const int off = row < rows && col < cols ? (row * ld + col) * ES : kOobOff;
+          if constexpr (BF16) {
+            u32x2 v;
+            v[0] = pack_bf16x2(o[q][0], o[q][1]);
+            v[1] = pack_bf16x2(o[q][2], o[q][3]);
+            bstore8<kStreamAux>(rs, off, v);
+          } else {
+            bstore16<kStreamAux>(rs, off, __builtin_bit_cast(u32x4, o[q]));
+          }
+        }
+      }
+    return;
+  }
   const int row0 = wm * C::TM + (l & 15), col0 = wn * C::TN + (l >> 4) * 4;
   const int base = (row0 * ld + col0) * ES;
   const int rr = rows - row0, cc = cols - col0;
@@ -587,7 +696,7 @@ __device__ __forceinline__ void write_tile(const f32x4 (&acc)[C::FM][C::FN], boo
 // or dXp): dW tiles go out as bf16 when the call asks for it.  A split tile's
 // waves each lie on one side of the split (it is a multiple of the wave's
 // 64 rows), so each picks its output as a whole.
-template <class C, bool DWB, bool SPLIT = false>
+template <class C, bool DWB, bool SPLIT = false, bool ROWS = true>
 __device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x4 (&acc)[C::FM][C::FN],
                                            bool zero, const Job& j) {
   float* out = j.C;
@@ -600,10 +709,10 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x4 (&acc)
     base = second ? a.dW2 : a.dW;
   }
   if constexpr (DWB)
-    write_tile<C, true>(acc, zero, reinterpret_cast<uint16_t*>(base) + (out - base), a.d_in,
-                        j.rows, j.cols);
+    write_tile<C, true, ROWS>(acc, zero, reinterpret_cast<uint16_t*>(base) + (out - base),
+                              a.d_in, j.rows, j.cols);
   else
-    write_tile<C, false>(acc, zero, out, a.d_in, j.rows, j.cols);
+    write_tile<C, false, ROWS>(acc, zero, out, a.d_in, j.rows, j.cols);
 }
 
 // MFMAs of k-granules kk..kk+3 (lane group l >> 4 takes granule kk + (l >> 4))
@@ -884,7 +993,7 @@ __device__ __forceinline__ void gemm_stream(const GemmPlan& P) {
   for (; tc >= 0; tc = sc.at(++kcn)) {
     jc = make_job<C, DX, SPLIT>(P, tc);
     if (jc.nk > 0) break;
-    if (jc.rows > 0) store_tile<C, DWB, SPLIT>(a, acc, true, jc);
+    if (jc.rows > 0) store_tile<C, DWB, SPLIT, !GB>(a, acc, true, jc);
   }
   if (tc < 0) return;
 
@@ -948,7 +1057,7 @@ __device__ __forceinline__ void gemm_stream(const GemmPlan& P) {
   for (;;) {
     LRM_KSTEP();
     if (++kc == jc.nk) {
-      store_tile<C, DWB, SPLIT>(a, acc, false, jc);
+      store_tile<C, DWB, SPLIT, !GB>(a, acc, false, jc);
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -957,7 +1066,7 @@ __device__ __forceinline__ void gemm_stream(const GemmPlan& P) {
       for (tc = sc.at(++kcn); tc >= 0; tc = sc.at(++kcn)) {
         jc = make_job<C, DX, SPLIT>(P, tc);
         if (jc.nk > 0) break;
-        if (jc.rows > 0) store_tile<C, DWB, SPLIT>(a, acc, true, jc);
+        if (jc.rows > 0) store_tile<C, DWB, SPLIT, !GB>(a, acc, true, jc);
       }
       if (tc < 0) break;
     }

@@ -277,14 +277,18 @@ typedef ::emu::BufRsrc __amdgpu_buffer_rsrc_t;
 
 namespace emu {
 // DPP model for the controls the kernels use: row_shr:n (0x110 + n),
-// row_bcast:15 (0x142), row_bcast:31 (0x143); bound_ctrl off (lanes without a
-// valid source, or in rows outside row_mask, get old).
+// row_ror:n (0x120 + n), row_bcast:15 (0x142), row_bcast:31 (0x143);
+// bound_ctrl off (lanes without a valid source, or in rows outside row_mask,
+// get old).
 inline int update_dpp(int old, int src, int ctrl, int row_mask) {
   const int lane = ctx.lane, row = lane >> 4, i = lane & 15;
   int from = -1;
   if (ctrl > 0x110 && ctrl < 0x120) {
     const int n = ctrl - 0x110;
     if (i >= n) from = lane - n;
+  } else if (ctrl > 0x120 && ctrl < 0x130) {
+    const int n = ctrl - 0x120;
+    from = 16 * row + ((i - n) & 15);
   } else if (ctrl == 0x142) {
     if (row >= 1) from = 16 * row - 1;
   } else if (ctrl == 0x143) {
@@ -298,6 +302,8 @@ inline int update_dpp(int old, int src, int ctrl, int row_mask) {
 }  // namespace emu
 #define __builtin_amdgcn_update_dpp(old, src, ctrl, rmask, bmask, bc) \
   ::emu::update_dpp((old), (src), (ctrl), (rmask))
+// ds_bpermute: each lane reads v from lane (addr / 4) mod 64
+#define __builtin_amdgcn_ds_bpermute(addr, v) ::emu::exchange((int)(v), ((addr) >> 2) & 63)
 
 #define threadIdx (::emu::ctx.tid)
 #define blockIdx (::emu::ctx.bid)
