@@ -6,12 +6,12 @@ access of a kernel or of the host code aborts the run; the outputs must pass
 the same oracle checks as the GPU parity tests.  Runs without a GPU.
 
 Every lane is an OS thread and every wave collective two 64-thread barriers,
-so a case takes 30-130 s.  The default run keeps five: the tiny fp32
+so a case takes 30-150 s.  The default run keeps four: the tiny fp32
 workload (every step, the fp32 GEMM), the bf16 grouped GEMM in its 256x256
-tiles, the same tiles on the LDS-DMA kernels, the dW schedule with its
-tiles striped over the XCDs, and the SwiGLU gate/up weight gradients in one
-launch over two outputs; LRM_EMU_FULL=1 runs all of them (about 30 minutes
-on 8 cores).
+tiles, the dW schedule with its tiles striped over the XCDs, and the SwiGLU
+gate/up weight gradients in one launch over two outputs; LRM_EMU_FULL=1
+runs all of them, the opt-in LDS-DMA kernels included (about 30 minutes on
+8 cores, or 10 with pytest -n 3).
 """
 
 from __future__ import annotations
@@ -191,7 +191,7 @@ def test_emu_linear_tile_configs(driver, tmp_path, tile):
     judge_linear(p, run_emu(driver, tmp_path, p, env_extra={"LRM_GEMM_TILE": tile}))
 
 
-@pytest.mark.parametrize("dma", ["2", pytest.param("4", marks=extended)])
+@pytest.mark.parametrize("dma", [pytest.param("2", marks=extended), pytest.param("4", marks=extended)])
 def test_emu_gemm_lds_dma(driver, tmp_path, dma):
     """The 256x256 kernels whose operand tiles go straight into LDS and whose
     k-strided operands are read with transposing LDS reads (LRM_GEMM_DMA=2:
