@@ -108,10 +108,50 @@ __global__ __launch_bounds__(256) void k_bucket_count(int N, int T, int E, int c
   for (int e = threadIdx.x; e < E; e += 256) blkcnt[(int64_t)e * gridDim.x + blockIdx.x] = hist[e];
 }
 
+// Large histograms (E * nblk of at least kRowsMinWork counts, nblk at most
+// kRowsMaxBlk): the rows of blkcnt are scanned by many workgroups, one wave
+// per expert, before k_bucket_scan (one workgroup) makes the offsets:
+// blkcnt[e][b] -> exclusive within-expert offset of block b, and
+// cand_off[e] = n_e for k_bucket_scan to take (rows_done).  Each lane loads
+// all its counts of the row before the wave scans them.  (On the 65536-token
+// workload, E = 128 rows of 1024 blocks, one workgroup took 47 us over the
+// rows.)  The CPU-emulation build lowers the bound so its small problems run
+// this path.
+#ifndef LRM_BUCKET_ROWS_MIN
+#define LRM_BUCKET_ROWS_MIN 32768
+#endif
+constexpr int64_t kRowsMinWork = LRM_BUCKET_ROWS_MIN;
+constexpr int kRowsMaxBlk = 1024;
+constexpr int kRowsPer = kRowsMaxBlk / kWave;  // counts per lane
+__global__ __launch_bounds__(kSelThreads) void k_bucket_rows(int nblk, int E,
+                                                             int32_t* __restrict__ blkcnt,
+                                                             int32_t* __restrict__ cand_off) {
+  const int e = blockIdx.x * (kSelThreads / kWave) + (int)(threadIdx.x >> 6);
+  if (e >= E) return;  // whole waves (no barrier in this kernel)
+  const int l = lane_id();
+  int32_t* row = blkcnt + (int64_t)e * nblk;
+  int v[kRowsPer];
+#pragma unroll
+  for (int u = 0; u < kRowsPer; ++u) {
+    const int b = u * kWave + l;
+    v[u] = b < nblk ? row[b] : 0;
+  }
+  int run = 0;
+#pragma unroll
+  for (int u = 0; u < kRowsPer; ++u) {
+    const int b = u * kWave + l;
+    const int incl = wave_incl_scan(v[u]);
+    if (b < nblk) row[b] = run + incl - v[u];
+    run += __shfl(incl, kWave - 1, kWave);
+  }
+  if (l == 0) cand_off[e] = run;
+}
+
 // blkcnt[e][b] -> exclusive within-expert offset of block b (one wave scans
 // one expert's block counts, 64 at a time); cand_off = prefix of the
 // per-expert counts; offsets = prefix of M_e = min(quota_e, n_e)
-// (quota == nullptr: keep all).
+// (quota == nullptr: keep all).  rows_done: k_bucket_rows has scanned the
+// rows and left n_e in cand_off[e].
 // Also: err[0] = OR of the blocks' error bits; mt_off (optional) = prefix of
 // ceil(M_e / mt_bm), the dX row tiles of the grouped GEMM.
 __global__ __launch_bounds__(kSelThreads) void k_bucket_scan(int nblk, int E,
@@ -123,7 +163,8 @@ __global__ __launch_bounds__(kSelThreads) void k_bucket_scan(int nblk, int E,
                                                              uint32_t* __restrict__ err,
                                                              int32_t* __restrict__ mt_off,
                                                              int mt_bm, QuotaPack qp,
-                                                             int use_qp, int64_t max_kept) {
+                                                             int use_qp, int64_t max_kept,
+                                                             int rows_done) {
   LRM_DYN_SHARED(int, counts);  // [2E]: counts, then kept counts min(quota, count)
   __shared__ int lds[kSelThreads / kWave + 1];
   __shared__ uint32_t eor;
@@ -157,12 +198,19 @@ __global__ __launch_bounds__(kSelThreads) void k_bucket_scan(int nblk, int E,
       v[u] = idx < cnt ? src[idx] : 0;
     }
   };
-  if (E > 0) load_round(0);
+  if (E > 0 && !rows_done) load_round(0);
   if (threadIdx.x < E) mcount[threadIdx.x] = q0;
   for (int e = threadIdx.x + kSelThreads; e < E; e += kSelThreads) mcount[e] = quota_of(e);
   __syncthreads();  // eor and mcount initialised
   if (bad) atomicOr(&eor, bad);
-  for (int e0 = 0; e0 < E; e0 += R) {
+  if (rows_done) {
+    for (int e = threadIdx.x; e < E; e += kSelThreads) {
+      const int n = cand_off[e];
+      counts[e] = n;
+      mcount[e] = min(mcount[e], n);
+    }
+  }
+  for (int e0 = 0; e0 < E && !rows_done; e0 += R) {
     const int rows = min(R, E - e0);
 #pragma unroll
     for (int u = 0; u < PER; ++u) stage[threadIdx.x + u * kSelThreads] = v[u];
@@ -698,9 +746,15 @@ hipError_t launch_bucket(const BucketArgs& a, hipStream_t s) {
   if (a.mt_off && a.mt_bm < 1) return hipErrorInvalidValue;
   const bool use_qp = !a.quota && a.qpack;
   if (use_qp && a.E > kQuotaPackMax) return hipErrorInvalidValue;
+  const bool rows = a.N > 0 && nblk <= kRowsMaxBlk && (int64_t)a.E * nblk >= kRowsMinWork;
+  if (rows) {
+    constexpr int per = kSelThreads / kWave;
+    LRM_LAUNCH((a.E + per - 1) / per, kSelThreads, 0, s, k_bucket_rows)(nblk, a.E, a.blkcnt,
+                                                                          a.cand_off);
+  }
   LRM_LAUNCH(1, kSelThreads, 2 * a.E * sizeof(int), s, k_bucket_scan)(
       nblk, a.E, a.blkcnt, a.quota, a.cand_off, a.offsets, a.blkerr, a.err, a.mt_off, a.mt_bm,
-      use_qp ? *a.qpack : QuotaPack{}, use_qp ? 1 : 0, a.max_kept);
+      use_qp ? *a.qpack : QuotaPack{}, use_qp ? 1 : 0, a.max_kept, rows ? 1 : 0);
   if (a.N > 0) {
     LRM_LAUNCH(nblk, 64, a.E * sizeof(int), s, k_bucket_scatter)(a.N, a.T, a.E, chunk, a.token,
                                                          a.expert, a.blkcnt, a.cand_off, a.score,

@@ -35,8 +35,11 @@ CLANG = "/opt/rocm/llvm/bin/clang++"
 # host quotas of more than QUOTA_PACK_MAX experts take the library's stream-copy
 # path (512 in the product build; lowered here so that path runs on small E)
 QUOTA_PACK_MAX = 8
+# the bucketing's many-workgroup row scan runs from this many histogram
+# counts (32768 in the product build; 1 here so every emulated call takes it)
+BUCKET_ROWS_MIN = 1
 FLAGS = ["-std=c++20", "-O1", "-g", "-fsanitize=address", "-fno-omit-frame-pointer",
-         f"-DLRM_QUOTA_PACK_MAX={QUOTA_PACK_MAX}"]
+         f"-DLRM_QUOTA_PACK_MAX={QUOTA_PACK_MAX}", f"-DLRM_BUCKET_ROWS_MIN={BUCKET_ROWS_MIN}"]
 
 LINEAR, SWIGLU = 0, 1
 F32, BF16 = 0, 1
