@@ -6,12 +6,13 @@ access of a kernel or of the host code aborts the run; the outputs must pass
 the same oracle checks as the GPU parity tests.  Runs without a GPU.
 
 Every lane is an OS thread and every wave collective two 64-thread barriers,
-so a case takes 30-150 s.  The default run keeps four: the tiny fp32
-workload (every step, the fp32 GEMM), the bf16 grouped GEMM in its 256x256
-tiles, the dW schedule with its tiles striped over the XCDs, and the SwiGLU
-gate/up weight gradients in one launch over two outputs; LRM_EMU_FULL=1
-runs all of them, the opt-in LDS-DMA kernels included (about 30 minutes on
-8 cores, or 10 with pytest -n 3).
+so a case takes 30-150 s.  The default run keeps the tiny fp32 workload
+(every step, the fp32 GEMM), the bf16 grouped GEMM in its 256x256 tiles,
+the dW schedule with its tiles striped over the XCDs, the SwiGLU gate/up
+weight gradients in one launch over two outputs, and the selection's error
+and capacity cases; LRM_EMU_FULL=1 runs all of them, the opt-in LDS-DMA and
+gathering kernels included (about 30 minutes on 8 cores, or 10 with
+pytest -n 3).
 """
 
 from __future__ import annotations
@@ -334,6 +335,7 @@ def test_emu_selection_past_packed_capacity(driver, tmp_path, kind):
             assert out[k].numpy()[-1] <= cap
 
 
+@extended
 def test_emu_gather_loads(driver, tmp_path):
     """LRM_GATHER_LOADS (16) under AddressSanitizer: the dW loader that
     gathers and scales the x rows itself stays in bounds (a ragged k tail,
