@@ -137,6 +137,30 @@ def test_select_large_expert(L):
     check_packing(pos, offsets, r.expert, E)
 
 
+def test_select_bucket_rows_ragged(L):
+    """A histogram of 100 experts x 391 blocks (100000 pairs): at least 32768
+    counts, so its rows are scanned by many workgroups (one wave per expert,
+    a partial last workgroup, rows not a multiple of 64 blocks) before the
+    offsets are formed.  Kept sets against the oracle, ties included, and
+    one expert with no pair at all."""
+    say("select, many-workgroup histogram rows")
+    T, E, k = 50000, 100, 2
+    rng = np.random.default_rng(17)
+    token = np.repeat(np.arange(T, dtype=np.int32), k)
+    expert = rng.integers(0, E - 1, T * k).astype(np.int32)  # expert E - 1 gets none
+    r = synth.Routing(T, E, k, expert, token, rng.random(T * k).astype(np.float32),
+                      np.bincount(expert, minlength=E), {})
+    s = (rng.standard_normal(r.N) ** 2 * 1e-3).astype(np.float32)
+    s[::53] = s[7]
+    q = (r.counts * 5) // 9 + (np.arange(E) % 3 == 0)
+    pos, offsets, kept, _ = _select(L, r, s, q)
+    ora = O.select_top_quota(r.expert, s.astype(np.float64), q, E)
+    gk = kept_from_pos(pos, r.expert, E)
+    for e in range(E):
+        assert np.array_equal(gk[e], ora[e]), f"expert {e}"
+    check_packing(pos, offsets, r.expert, E)
+
+
 @pytest.mark.parametrize("case", ["tiny_fp32", "ties_8192", "wide_1024", "device_quota",
                                   "bad_indices"])
 def test_select_one_launch_matches_bucketing(L, case, monkeypatch):
