@@ -796,7 +796,10 @@ __device__ __forceinline__ int dw_cost(const GemmArgs& a, int e) {
 
 // NT threads (E <= 4 NT: one block scan of the expert costs)
 template <int NT>
-__global__ __launch_bounds__(NT) void k_dw_plan(GemmPlan P) {
+// Workgroup 0 plans P0, workgroup 1 (when launched) P1: a call plans two dW
+// launches at once (GemmArgs::dw_plan_next).
+__global__ __launch_bounds__(NT) void k_dw_plan(GemmPlan P0, GemmPlan P1) {
+  const GemmPlan& P = blockIdx.x == 0 ? P0 : P1;
   const GemmArgs& a = P.a;
   const int E = a.E, per = P.ntm_w * P.ntn, R = plan_runs(E);
   int32_t* plan = a.dw_plan;
@@ -1710,6 +1713,26 @@ int64_t gemm_workspace_ints(int E) {
   return (int64_t)E + 1 + kPlanHead + 3 * (int64_t)plan_runs(E);
 }
 
+// The fields of a GemmPlan that k_dw_plan reads, for the dW launch of b (bf16
+// kernels, its tile configuration): false if b has no scheduled dW launch.
+static bool dw_plan_of(const GemmArgs& b, GemmPlan* Q) {
+  if (gemm_dw_tiles_per_expert(b) <= 0) return false;
+  int bm = CfgS::BM, bn = CfgS::BN;
+  switch (gemm_tile_choice(b)) {
+    case 3:
+    case 2: bm = CfgL::BM; bn = CfgL::BN; break;
+    case 1: bm = CfgM::BM; bn = CfgM::BN; break;
+    default: break;
+  }
+  *Q = GemmPlan{};
+  Q->a = b;
+  Q->ntm_w = (b.d_out + bm - 1) / bm;
+  Q->ntn = (b.d_in + bn - 1) / bn;
+  Q->nW = b.E * Q->ntm_w * Q->ntn;
+  Q->a.dw_plan = b.mt_off + b.E + 1;
+  return true;
+}
+
 template <class CW, class CX>
 static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
   GemmPlan P{};
@@ -1718,10 +1741,14 @@ static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
   if (P.nW > 0) {
     P.a.dw_plan = a.mt_off + a.E + 1;
     if (!a.dw_plan_ready) {
+      // the next launch's schedule in the same launch, by a second workgroup
+      GemmPlan P2 = P;
+      const GemmArgs* nx = a.dw_plan_next;
+      const int nb = nx && nx->E == a.E && nx->mt_off && dw_plan_of(*nx, &P2) ? 2 : 1;
       if (a.E <= 4 * 256)
-        LRM_LAUNCH(1, 256, 0, s, k_dw_plan<256>)(P);
+        LRM_LAUNCH(nb, 256, 0, s, k_dw_plan<256>)(P, P2);
       else
-        LRM_LAUNCH(1, 1024, 0, s, k_dw_plan<1024>)(P);
+        LRM_LAUNCH(nb, 1024, 0, s, k_dw_plan<1024>)(P, P2);
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
   }

@@ -177,6 +177,11 @@ struct GemmArgs {
   // offsets, max_rows and gemm_dw_tiles_per_expert (the schedule depends on
   // nothing else)
   int dw_plan_ready;
+  // host pointer, or null: when this launch plans its dW schedule, the same
+  // plan launch also writes the schedule of *dw_plan_next (a later bf16 dW
+  // launch with the same E, offsets and max_rows, into its own mt_off
+  // workspace), which then runs with dw_plan_ready
+  const GemmArgs* dw_plan_next;
 };
 // int32 entries of the grouped GEMM's workspace for E experts
 int64_t gemm_workspace_ints(int E);

@@ -599,6 +599,7 @@ struct GluPlan {
   int32_t* kept;
   int32_t* tok_off;
   int32_t* mt_off;
+  int32_t* mt_off2;  // the one gate/up dW launch's schedule (planned with the down one)
   void* Gd;      // [Md][H] g rows
   void* Hd;      // [Md][I] w * h rows
   float* U;      // [Md][I]
@@ -636,6 +637,7 @@ GluPlan carve_glu(Carve& c, const lrm_problem* pb, const lrm_outputs* out, int64
   L.kept = c.take<int32_t>(p.N);
   L.tok_off = c.take<int32_t>((int64_t)p.T + 1);
   L.mt_off = c.take<int32_t>(gemm_workspace_ints(p.E));
+  L.mt_off2 = c.take<int32_t>(gemm_workspace_ints(p.E));
   L.Gd = c.take<char>(Md * H * es);
   L.Hd = c.take<char>(Md * I * es);
   L.U = c.take<float>(Md * I);
@@ -897,6 +899,14 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   const bool fuse_gu = z.pass_through && bf16 && I % 64 == 0 && !L.xrow_g &&
                        !(fenv && fenv[0] == '0');
   void* const GBw = fuse_gu ? static_cast<void*>(static_cast<char*>(L.GA) + (int64_t)I * 2) : L.GB;
+  // the one gate/up weight-gradient launch: its schedule depends only on the
+  // down stage's offsets, so the down launch's plan launch writes it as well
+  GemmArgs gw{};
+  gw.E = E; gw.bf16 = bf16; gw.max_rows = (int)z.Md; gw.d_in = H; gw.d_out = 2 * I;
+  gw.offsets = L.offsets; gw.Gp = L.GA; gw.Xp = L.Xgu;
+  gw.dW = out->dW_gate; gw.dW2 = out->dW_up; gw.dw_split = I;
+  gw.mt_off = L.mt_off2; gw.dw_plan_ready = 1;
+  gw.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
   GemmArgs gd{};
   gd.E = E; gd.bf16 = bf16; gd.max_rows = (int)z.Md;
   const int dx_rows = gemm_dx_tile_rows(gd);
@@ -927,6 +937,7 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
   gd.dW = out->dW_down; gd.dXp = L.U; gd.mt_off = L.mt_off; gd.mt_ready = 1;
   gd.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
   gd.mid_event = mark.at(4);
+  gd.dw_plan_next = fuse_gu ? &gw : nullptr;
   LRM_TRY_HIP(launch_grouped_gemm(gd, s));
   LRM_TRY_HIP(mark(5));
   // ---- SwiGLU backward and the gate/up scores
@@ -990,12 +1001,6 @@ lrm_status run_swiglu(const lrm_problem* pb, const lrm_outputs* out, void* ws, h
       LRM_TRY_HIP(launch_compact(cx, s));
     LRM_TRY_HIP(mark(8));
     if (fuse_gu) {
-      GemmArgs gw{};
-      gw.E = E; gw.bf16 = bf16; gw.max_rows = (int)z.Md; gw.d_in = H; gw.d_out = 2 * I;
-      gw.offsets = L.offsets; gw.Gp = L.GA; gw.Xp = L.Xgu;
-      gw.dW = out->dW_gate; gw.dW2 = out->dW_up; gw.dw_split = I;
-      gw.mt_off = L.mt_off;
-      gw.dw_bf16 = (pb->flags & LRM_DW_BF16) != 0;
       LRM_TRY_HIP(launch_grouped_gemm(gw, s));
       LRM_TRY_HIP(mark(9));
       // both input-gradient products, K = 2I in two segments of [GA | GB]
