@@ -472,10 +472,11 @@ lrm_status lrm_expert_backward(const lrm_problem* prob, const lrm_outputs* out, 
  *           launch, 11 after the up dW launch, 12 after the up dX launch,
  *           13 after unpermute (end).  When the gate/up selections keep every
  *           down-kept row, one launch computes both input-gradient products
- *           (between 9 and 10) and 12 coincides with 11; with bf16 inputs and
- *           I a multiple of 64 one launch also computes both weight gradients
- *           (between 8 and 9), the input-gradient launch sits between 9 and
- *           10, and 11 and 12 coincide with 10.
+ *           (between 9 and 10) and 12 coincides with 11; with bf16 inputs,
+ *           I a multiple of 64 and no LRM_GATHER_LOADS, one launch also
+ *           computes both weight gradients (between 8 and 9), the
+ *           input-gradient launch sits between 9 and 10, and 11 and 12
+ *           coincide with 10.
  * The time between consecutive events is that stage's device time on the
  * stream (for profiling; the results are those of lrm_expert_backward). */
 lrm_status lrm_expert_backward_events(const lrm_problem* prob, const lrm_outputs* out, void* ws,
